@@ -1,0 +1,290 @@
+"""fp64 / float32-emulating CPU oracle for the batch-invariant token-logprob path.
+
+TEST INFRASTRUCTURE ONLY: used by the tests, the smoke check and the
+``cpu_baseline`` leg of ``bench.py``; never by the product path.  It shares no
+code with the HIP library or its Python binding.
+
+Sources (the three web pages this method is described on):
+
+* [IsoExec] "IsoExec: Unified Execution to Eliminate Trainer-Inference
+  Mismatch in SkyRL", section "Parallelism-invariant kernels" and its figure of
+  the fixed binary reduction tree: the contraction dimension K is cut into N
+  contiguous leaves, each leaf is a deterministic matrix-core product with FP32
+  accumulation, and the leaves are combined by a fixed binary schedule.  The
+  contract example in "Unified execution contract" pins ``leaves = 8`` and an
+  FP32 leaf dtype.
+* [Bit-consistent RL] "Termina el entrenamiento RL más rápido: Consistente a
+  nivel de bits, de alto rendimiento y dirigido por agentes", section 2 (diff is
+  the per-sampled-token logprob difference and must be exactly zero; batch
+  independence and phase consistency), section 4.4 (per-row expert GEMM result
+  independent of layout) and section 4.5 (expert outputs summed in FP32 in a
+  fixed order on the token's owner).
+
+Readings where the pages leave a step open (each is listed in the design doc):
+
+* R1 tree shape: a balanced tree of adjacent pairs, level by level, over a
+  power-of-two leaf count: for 8 leaves ``((P0+P1)+(P2+P3))+((P4+P5)+(P6+P7))``.
+* R5 the logits stay FP32 (the tree output) before the softmax.
+* R6 the log-softmax is max-shifted: ``lse = g + log(sum(exp(x - g)))``.
+* R8 a sampled id outside ``[0, V)`` yields NaN for that row only.
+* R12 the MoE combine runs in ascending expert id, ``acc = acc + g*y`` with a
+  float32 multiply then a float32 add, each rounded to nearest even.
+
+Parity status:
+
+* ``contraction_ref``, ``lse_ref``, ``log_softmax_ref``, ``logprob_ref``,
+  ``moe_ref``: plain definitions in fp64; pinned by brute force (exact rational
+  arithmetic), closed forms and invariants in ``tests/test_oracle_pins.py``.
+* ``leaf_tree_f32``, ``leaf_tree_gemm_f32``, ``moe_combine_f32``: float32
+  emulators of the fixed orders; pinned by hand-derived closed forms.  They are
+  exact models of the GPU only where every leaf sum (or every expert output) is
+  itself exact in float32; elsewhere the rounding inside one leaf, which the
+  matrix-core instruction performs, is not modelled ("parity unpinned" beyond
+  the tolerance).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f64",
+    "as_f64",
+    "leaf_bounds",
+    "contraction_ref",
+    "leaf_tree_f32",
+    "leaf_tree_gemm_f32",
+    "lse_ref",
+    "log_softmax_ref",
+    "logprob_ref",
+    "gumbel_max_ids",
+    "moe_ref",
+    "moe_combine_f32",
+    "k3_kl",
+]
+
+
+# ---------------------------------------------------------------------------
+# bf16 storage
+# ---------------------------------------------------------------------------
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Decode bf16 bit patterns (uint16) to float64.
+
+    bf16 is the upper half of an IEEE float32, so widening the 16 bits to the
+    top of a 32-bit word gives the float32 with the same value; float32 widens
+    to float64 exactly.
+    """
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def as_f64(x) -> np.ndarray:
+    """Accept bf16 bit patterns (uint16) or any real array; return float64."""
+    a = np.asarray(x)
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f64(a)
+    return a.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Leaf partition and the fixed tree   [IsoExec, Parallelism-invariant kernels]
+# ---------------------------------------------------------------------------
+
+def leaf_bounds(K: int, leaves: int) -> list[tuple[int, int]]:
+    """Leaf l covers columns ``[l*K/L, (l+1)*K/L)``: contiguous, equal, fixed.
+
+    The count is a power of two (reading R1) and must divide K (reading R2).
+    """
+    if leaves < 1 or (leaves & (leaves - 1)) != 0:
+        raise ValueError("leaves must be a power of two")
+    if K % leaves != 0:
+        raise ValueError("K must be a multiple of leaves")
+    ell = K // leaves
+    return [(l * ell, (l + 1) * ell) for l in range(leaves)]
+
+
+def leaf_tree_f32(partials) -> np.ndarray:
+    """Combine float32 leaf partials ``P[0..L-1]`` by the fixed binary tree.
+
+    Reading R1: adjacent leaves are paired level by level,
+    ``T(a, b) = T(a, mid) + T(mid, b)`` with ``mid = (a + b) / 2``, every add a
+    float32 add rounded to nearest even.  ``partials`` has shape ``[L, ...]``;
+    the result has the trailing shape.
+    """
+    level = [np.asarray(p, dtype=np.float32) for p in partials]
+    n = len(level)
+    if n < 1 or (n & (n - 1)) != 0:
+        raise ValueError("leaf count must be a power of two")
+    with np.errstate(over="ignore", invalid="ignore"):
+        while len(level) > 1:
+            level = [np.add(level[2 * i], level[2 * i + 1], dtype=np.float32)
+                     for i in range(len(level) // 2)]
+    return level[0]
+
+
+def contraction_ref(A, W, row_chunk: int = 256) -> np.ndarray:
+    """Exact contraction ``X[m, n] = sum_k A[m, k] * W[n, k]`` in float64.
+
+    This is the value every leaf schedule approximates [IsoExec,
+    Parallelism-invariant kernels].  ``A`` is ``[M, K]`` and ``W`` is ``[N, K]``
+    (row-major, K contiguous, the layout of a linear / LM-head weight).  Each
+    bf16 x bf16 product is exact in float64; rows are computed in chunks only to
+    bound memory (rows are independent, so chunking reorders nothing).
+    """
+    A64 = as_f64(A)
+    W64 = as_f64(W)
+    if A64.ndim != 2 or W64.ndim != 2 or A64.shape[1] != W64.shape[1]:
+        raise ValueError("A must be [M, K] and W must be [N, K]")
+    M = A64.shape[0]
+    out = np.empty((M, W64.shape[0]), dtype=np.float64)
+    WT = W64.T
+    for r0 in range(0, M, row_chunk):
+        r1 = min(M, r0 + row_chunk)
+        out[r0:r1] = A64[r0:r1] @ WT
+    return out
+
+
+def leaf_tree_gemm_f32(A, W, leaves: int) -> np.ndarray:
+    """Float32 model of the leaf-tree contraction.
+
+    Each leaf sum ``P_l[m, n] = sum_{k in leaf l} A[m, k] W[n, k]`` is formed in
+    float64 and rounded once to float32; the leaves are then combined by
+    ``leaf_tree_f32``.  This equals the GPU bit for bit exactly when every leaf
+    sum is representable in float32 and exact in float64 (for example one
+    nonzero product per leaf, or small integers); otherwise the rounding inside
+    a leaf is not modelled.
+    """
+    A64 = as_f64(A)
+    W64 = as_f64(W)
+    K = A64.shape[1]
+    parts = []
+    for k0, k1 in leaf_bounds(K, leaves):
+        parts.append((A64[:, k0:k1] @ W64[:, k0:k1].T).astype(np.float32))
+    return leaf_tree_f32(parts)
+
+
+# ---------------------------------------------------------------------------
+# Log-softmax and the sampled-token logprob   [Bit-consistent RL, section 2]
+# ---------------------------------------------------------------------------
+
+def lse_ref(X) -> np.ndarray:
+    """Row-wise ``log(sum_v exp(X[m, v]))`` in float64, max-shifted (R6)."""
+    X = np.asarray(X, dtype=np.float64)
+    g = X.max(axis=-1, keepdims=True)
+    s = np.exp(X - g).sum(axis=-1, keepdims=True)
+    return (g + np.log(s))[..., 0]
+
+
+def log_softmax_ref(X) -> np.ndarray:
+    """Row-wise log-softmax in float64: ``X - lse(X)``."""
+    X = np.asarray(X, dtype=np.float64)
+    return X - lse_ref(X)[..., None]
+
+
+def logprob_ref(H, W, ids, row_chunk: int = 256):
+    """Logprob of each row's sampled token under ``softmax(H W^T)``.
+
+    Returns ``(logprob[M], lse[M])`` in float64.  ``H`` is ``[M, K]``, ``W`` is
+    ``[V, K]``, ``ids`` is ``[M]``.  The logits are never rounded (R5); a row
+    whose id lies outside ``[0, V)`` gets NaN (R8).  Rows are processed in
+    chunks to bound memory; each row is computed whole (full contraction, then
+    max, then sum), so nothing is reordered.
+    """
+    H64 = as_f64(H)
+    W64 = as_f64(W)
+    ids = np.asarray(ids, dtype=np.int64)
+    M = H64.shape[0]
+    V = W64.shape[0]
+    if ids.shape != (M,):
+        raise ValueError("ids must have shape [M]")
+    lp = np.empty(M, dtype=np.float64)
+    lse = np.empty(M, dtype=np.float64)
+    WT = W64.T
+    for r0 in range(0, M, row_chunk):
+        r1 = min(M, r0 + row_chunk)
+        X = H64[r0:r1] @ WT
+        l = lse_ref(X)
+        lse[r0:r1] = l
+        rid = ids[r0:r1]
+        ok = (rid >= 0) & (rid < V)
+        picked = np.full(r1 - r0, np.nan)
+        rows = np.nonzero(ok)[0]
+        picked[rows] = X[rows, rid[rows]]
+        lp[r0:r1] = picked - l
+    return lp, lse
+
+
+def gumbel_max_ids(X, G) -> np.ndarray:
+    """Sample one id per row from ``softmax(X)`` by the Gumbel-max rule.
+
+    ``G`` holds standard Gumbel noise of the same shape (drawn by the seeded
+    input generator); ``argmax(X + G)`` is an exact sample from the softmax.
+    Ties go to the lower index (numpy's argmax).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    G = np.asarray(G, dtype=np.float64)
+    return np.argmax(X + G, axis=-1).astype(np.int64)
+
+
+# ---------------------------------------------------------------------------
+# MoE-shaped combine   [Bit-consistent RL, sections 4.4 and 4.5]
+# ---------------------------------------------------------------------------
+
+def moe_ref(H, W_experts, topk_ids, topk_w, row_chunk: int = 512) -> np.ndarray:
+    """``out[t] = sum_s topk_w[t, s] * (H[t] . W_{topk_ids[t, s]}^T)`` in float64.
+
+    ``H`` is ``[T, K]``, ``W_experts`` is ``[E, N, K]``, ``topk_ids`` and
+    ``topk_w`` are ``[T, topk]``.  In float64 the order of the expert terms
+    changes nothing at the tolerances used.
+    """
+    H64 = as_f64(H)
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    w = np.asarray(topk_w, dtype=np.float64)
+    T = H64.shape[0]
+    E, N, K = np.asarray(W_experts).shape
+    out = np.zeros((T, N), dtype=np.float64)
+    for e in range(E):
+        tok, slot = np.nonzero(ids == e)
+        if tok.size == 0:
+            continue
+        We = as_f64(W_experts[e])
+        for r0 in range(0, tok.size, row_chunk):
+            t = tok[r0:r0 + row_chunk]
+            s = slot[r0:r0 + row_chunk]
+            y = H64[t] @ We.T
+            np.add.at(out, t, w[t, s][:, None] * y)
+    return out
+
+
+def moe_combine_f32(Y, topk_ids, topk_w) -> np.ndarray:
+    """Float32 emulation of the fixed-order expert combine (reading R12).
+
+    ``Y[t, s, :]`` is the float32 output of expert ``topk_ids[t, s]`` for token
+    ``t``.  The terms are taken in ascending expert id (equal ids keep their slot
+    order), and ``acc = acc + w * y`` is a float32 multiply followed by a
+    float32 add, each rounded to nearest even, starting from ``acc = +0``.
+    """
+    Y = np.asarray(Y, dtype=np.float32)
+    ids = np.asarray(topk_ids, dtype=np.int64)
+    w = np.asarray(topk_w, dtype=np.float32)
+    T, S, N = Y.shape
+    out = np.zeros((T, N), dtype=np.float32)
+    order = np.argsort(ids, axis=1, kind="stable")
+    with np.errstate(over="ignore", invalid="ignore"):
+        for j in range(S):
+            s = order[:, j]
+            rows = np.arange(T)
+            term = np.multiply(w[rows, s][:, None], Y[rows, s], dtype=np.float32)
+            out = np.add(out, term, dtype=np.float32)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Harness metric   [Bit-consistent RL, section 3.2: the k3 estimator]
+# ---------------------------------------------------------------------------
+
+def k3_kl(logp_a, logp_b) -> float:
+    """Mean k3 estimator ``r - 1 - log r`` with ``r = exp(logp_b - logp_a)``."""
+    d = np.asarray(logp_b, dtype=np.float64) - np.asarray(logp_a, dtype=np.float64)
+    return float(np.mean(np.expm1(d) - d)) if d.size else 0.0

@@ -1,0 +1,379 @@
+"""Pins for the CPU oracle: brute force, closed forms, invariants (no GPU).
+
+Each test ties the oracle to something other than itself: exact rational
+arithmetic on tiny inputs, integer arithmetic, hand-derived float32 closed
+forms (tests/golden), and properties the mathematics fixes.  They are chosen so
+that a dropped term, a wrong sign or index, a transposed operand, a wrong leaf
+boundary or a wrong tree shape fails at least one of them.
+"""
+
+import math
+import os
+import re
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# helpers (independent of the oracle's own arithmetic)
+# ---------------------------------------------------------------------------
+
+def parse_dyadic(s: str) -> Fraction:
+    """Parse '1+3*2^-23', '-2^24', '2^-3' into an exact Fraction."""
+    s = s.replace(" ", "")
+    total = Fraction(0)
+    for sign, term in re.findall(r"([+-]?)([^+-]+(?:\^-?\d+)?)", s.replace("^-", "^~")):
+        term = term.replace("^~", "^-")
+        f = Fraction(1)
+        for factor in term.split("*"):
+            if "^" in factor:
+                b, e = factor.split("^")
+                f *= Fraction(int(b)) ** int(e)
+            else:
+                f *= Fraction(int(factor))
+        total += -f if sign == "-" else f
+    return total
+
+
+def load_golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            rows.append([c.strip() for c in line.split("|")])
+    return rows
+
+
+def bf16_value_independent(bits: int) -> Fraction:
+    """bf16 bit pattern -> exact value from sign / exponent / mantissa fields."""
+    s = (bits >> 15) & 1
+    e = (bits >> 7) & 0xFF
+    m = bits & 0x7F
+    assert e not in (0, 0xFF), "normal values only"
+    v = Fraction(128 + m, 128) * Fraction(2) ** (e - 127)
+    return -v if s else v
+
+
+def f32_exact(f: Fraction) -> np.float32:
+    x = np.float32(float(f))
+    assert Fraction(float(x)) == f, "closed form is not a float32 value"
+    return x
+
+
+# ---------------------------------------------------------------------------
+# bf16 storage
+# ---------------------------------------------------------------------------
+
+def test_bf16_decode_matches_field_formula():
+    rng = np.random.default_rng(7)
+    bits = wl.normal_bf16(rng, (4000,), std=3.0)
+    got = oracle.bf16_bits_to_f64(bits)
+    for b, g in zip(bits[:500], got[:500]):
+        if b & 0x7FFF == 0:
+            assert g == 0.0
+            continue
+        assert Fraction(float(g)) == bf16_value_independent(int(b))
+
+
+def test_bf16_rounding_of_generator_is_nearest_even():
+    # 1 + 2^-8 is halfway between bf16 1 and 1+2^-7: ties to the even (1).
+    # 1 + 3*2^-8 is halfway between 1+2^-7 and 1+2^-6: ties to 1+2^-6.
+    x = np.array([1.0, 1 + 2**-8, 1 + 3 * 2**-8, 1 + 2**-8 + 2**-20, -2.5, 2**-24],
+                 dtype=np.float32)
+    got = wl.f32_to_bf16_bits(x)
+    exp = [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC020, 0x3380]
+    assert [int(v) for v in got] == exp
+
+
+# ---------------------------------------------------------------------------
+# P1: brute force on tiny inputs with exact rational arithmetic
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_contraction_and_logprob_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    M, K, V = 3, 16, 8
+    H = wl.normal_bf16(rng, (M, K), 1.0)
+    W = wl.normal_bf16(rng, (V, K), 0.5)
+    ids = rng.integers(0, V, size=M)
+    Hq = [[bf16_value_independent(int(b)) if b & 0x7FFF else Fraction(0) for b in r] for r in H]
+    Wq = [[bf16_value_independent(int(b)) if b & 0x7FFF else Fraction(0) for b in r] for r in W]
+    X_exact = [[sum(h * w for h, w in zip(hr, wr)) for wr in Wq] for hr in Hq]
+
+    X = oracle.contraction_ref(H, W)
+    assert X.shape == (M, V)
+    for m in range(M):
+        for v in range(V):
+            assert abs(X[m, v] - float(X_exact[m][v])) <= 1e-12 * (1 + abs(float(X_exact[m][v])))
+
+    lp, lse = oracle.logprob_ref(H, W, ids)
+    for m in range(M):
+        xs = [float(x) for x in X_exact[m]]
+        g = max(xs)
+        lse_bf = g + math.log(math.fsum(math.exp(x - g) for x in xs))
+        assert abs(lse[m] - lse_bf) <= 1e-12 * (1 + abs(lse_bf))
+        assert abs(lp[m] - (xs[ids[m]] - lse_bf)) <= 1e-12 * (1 + abs(lse_bf))
+
+
+def test_contraction_exact_integers_not_transposed():
+    # Small integers: every partial sum is an integer, so float64 is exact and
+    # must equal int64 arithmetic; M != N != K catches a transposed operand.
+    rng = np.random.default_rng(3)
+    A = wl.integer_bf16(rng, (5, 24), -3, 3)
+    W = wl.integer_bf16(rng, (7, 24), -3, 3)
+    Ai = oracle.bf16_bits_to_f64(A).astype(np.int64)
+    Wi = oracle.bf16_bits_to_f64(W).astype(np.int64)
+    expect = np.einsum("mk,nk->mn", Ai, Wi)
+    got = oracle.contraction_ref(A, W)
+    assert np.array_equal(got, expect.astype(np.float64))
+
+
+def test_contraction_row_chunking_changes_nothing():
+    rng = np.random.default_rng(4)
+    A = wl.normal_bf16(rng, (37, 64))
+    W = wl.normal_bf16(rng, (11, 64), 0.02)
+    assert np.array_equal(oracle.contraction_ref(A, W, row_chunk=5),
+                          oracle.contraction_ref(A, W, row_chunk=1000))
+
+
+# ---------------------------------------------------------------------------
+# P2: invariants of the log-softmax and the logprob
+# ---------------------------------------------------------------------------
+
+def test_log_softmax_invariants():
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((6, 50)) * 4
+    L = oracle.log_softmax_ref(X)
+    assert np.allclose(oracle.lse_ref(L), 0.0, atol=1e-12)          # logsumexp of log-softmax
+    assert np.allclose(np.exp(L).sum(axis=1), 1.0, atol=1e-12)       # softmax sums to one
+    assert np.allclose(oracle.log_softmax_ref(X + 123.25), L, atol=1e-12)  # shift invariance
+    assert np.all(L <= 0)
+    # overflow-safe: equal huge logits give exactly log(V) above the logit
+    big = np.full((1, 4), 1000.0)
+    assert abs(oracle.lse_ref(big)[0] - (1000.0 + math.log(4))) < 1e-12
+
+
+def test_logprob_row_and_vocab_permutation():
+    rng = np.random.default_rng(6)
+    M, K, V = 9, 32, 40
+    H = wl.normal_bf16(rng, (M, K))
+    W = wl.normal_bf16(rng, (V, K), 0.1)
+    ids = rng.integers(0, V, size=M)
+    lp, _ = oracle.logprob_ref(H, W, ids)
+    # rows: permuting the batch permutes the outputs (each row stands alone)
+    p = rng.permutation(M)
+    lp_p, _ = oracle.logprob_ref(H[p], W, ids[p])
+    assert np.array_equal(lp_p, lp[p])
+    # vocabulary: permute W's rows and remap ids; logprobs are unchanged
+    q = rng.permutation(V)
+    inv = np.empty(V, dtype=np.int64)
+    inv[q] = np.arange(V)
+    lp_q, _ = oracle.logprob_ref(H, W[q], inv[ids])
+    assert np.allclose(lp_q, lp, atol=1e-12)
+    # one row alone equals the same row inside the batch
+    for r in (0, 4, 8):
+        one, _ = oracle.logprob_ref(H[r:r + 1], W, ids[r:r + 1])
+        assert abs(one[0] - lp[r]) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# P5 / P6: closed forms and special cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("V", [1, 7, 4096, 151936])
+def test_equal_logits_give_minus_log_V(V):
+    K = 8
+    rng = np.random.default_rng(V)
+    H = wl.normal_bf16(rng, (2, K))
+    row = wl.normal_bf16(rng, (1, K), 0.5)
+    W = np.repeat(row, V, axis=0)
+    ids = np.array([0, V - 1])
+    lp, _ = oracle.logprob_ref(H, W, ids)
+    assert np.allclose(lp, -math.log(V), atol=1e-12)
+    Wz = np.zeros((V, K), dtype=np.uint16)   # W = 0: all logits 0
+    lpz, lsez = oracle.logprob_ref(H, Wz, ids)
+    assert np.allclose(lpz, -math.log(V), atol=1e-12)
+    assert np.allclose(lsez, math.log(V), atol=1e-12)
+
+
+def test_one_distinct_logit_closed_form():
+    V, K, a = 1000, 4, 2.5
+    H = wl.f32_to_bf16_bits(np.array([[1.0, 0, 0, 0]], dtype=np.float32))
+    Wf = np.zeros((V, K), dtype=np.float32)
+    Wf[17, 0] = a
+    W = wl.f32_to_bf16_bits(Wf)
+    lp, _ = oracle.logprob_ref(H, W, np.array([17]))
+    assert abs(lp[0] - (a - math.log(math.exp(a) + V - 1))) < 1e-12
+    lp0, _ = oracle.logprob_ref(H, W, np.array([3]))
+    assert abs(lp0[0] - (0 - math.log(math.exp(a) + V - 1))) < 1e-12
+
+
+def test_one_hot_row_reads_a_column_of_W():
+    rng = np.random.default_rng(8)
+    K, V = 16, 30
+    W = wl.normal_bf16(rng, (V, K), 0.3)
+    Hf = np.zeros((1, K), dtype=np.float32)
+    Hf[0, 11] = 1.0
+    X = oracle.contraction_ref(wl.f32_to_bf16_bits(Hf), W)
+    assert np.array_equal(X[0], oracle.bf16_bits_to_f64(W[:, 11]))
+
+
+def test_invalid_id_is_nan_for_that_row_only():
+    rng = np.random.default_rng(9)
+    H = wl.normal_bf16(rng, (4, 8))
+    W = wl.normal_bf16(rng, (5, 8))
+    lp, lse = oracle.logprob_ref(H, W, np.array([0, -1, 5, 4]))
+    assert np.isfinite(lp[0]) and np.isfinite(lp[3])
+    assert np.isnan(lp[1]) and np.isnan(lp[2])
+    assert np.all(np.isfinite(lse))
+
+
+# ---------------------------------------------------------------------------
+# Fixed binary tree in float32 (closed forms in tests/golden)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("row", load_golden("tree_f32_closed_forms.txt"), ids=lambda r: r[0])
+def test_leaf_tree_closed_forms(row):
+    name, leaves, expected, _why = row
+    P = np.array([f32_exact(parse_dyadic(v)) for v in leaves.split(",")], dtype=np.float32)
+    got = oracle.leaf_tree_f32(P)
+    assert got.dtype == np.float32
+    assert Fraction(float(got)) == parse_dyadic(expected)
+
+
+def test_leaf_tree_closed_forms_have_power():
+    """The golden leaves separate the tree from plausible wrong schedules."""
+    rows = {r[0]: r for r in load_golden("tree_f32_closed_forms.txt")}
+    P = [f32_exact(parse_dyadic(v)) for v in rows["L8_adjacent"][1].split(",")]
+    seq = np.float32(0)
+    for p in P:
+        seq = np.float32(seq + p)
+    assert seq != oracle.leaf_tree_f32(np.array(P))
+    Q = [f32_exact(parse_dyadic(v)) for v in rows["L8_not_strided"][1].split(",")]
+    strided = [np.float32(Q[i] + Q[i + 4]) for i in range(4)]
+    strided = np.float32(np.float32(strided[0] + strided[2]) + np.float32(strided[1] + strided[3]))
+    assert strided != oracle.leaf_tree_f32(np.array(Q))
+
+
+@pytest.mark.parametrize("where", ["start", "end"])
+@pytest.mark.parametrize("leaves,K", [(8, 512), (16, 7168), (8, 64)])
+def test_leaf_tree_gemm_leaf_boundaries(where, leaves, K):
+    """One nonzero product per leaf: the leaf sums are exact, only the tree rounds."""
+    golden = {r[0]: r for r in load_golden("tree_f32_closed_forms.txt")}
+    key = "L8_adjacent" if leaves == 8 else "L16_adjacent"
+    vals = [f32_exact(parse_dyadic(v)) for v in golden[key][1].split(",")]
+    ell = K // leaves
+    A = np.zeros((2, K), dtype=np.float32)
+    W = np.zeros((3, K), dtype=np.float32)
+    for l in range(leaves):
+        k = l * ell if where == "start" else (l + 1) * ell - 1
+        A[:, k] = 1.0
+        W[1, k] = vals[l]
+    got = oracle.leaf_tree_gemm_f32(wl.f32_to_bf16_bits(A), wl.f32_to_bf16_bits(W), leaves)
+    assert got.dtype == np.float32 and got.shape == (2, 3)
+    assert np.all(got[:, [0, 2]] == 0)
+    assert np.all(np.array([Fraction(float(x)) for x in got[:, 1]]) == parse_dyadic(golden[key][2]))
+
+
+def test_leaf_tree_gemm_integers_equal_exact():
+    rng = np.random.default_rng(10)
+    A = wl.integer_bf16(rng, (6, 128), -4, 4)
+    W = wl.integer_bf16(rng, (5, 128), -4, 4)
+    got = oracle.leaf_tree_gemm_f32(A, W, 8)
+    assert np.array_equal(got.astype(np.float64), oracle.contraction_ref(A, W))
+
+
+def test_leaf_bounds_rejects_bad_counts():
+    with pytest.raises(ValueError):
+        oracle.leaf_bounds(96, 3)
+    with pytest.raises(ValueError):
+        oracle.leaf_bounds(100, 8)
+    assert oracle.leaf_bounds(64, 4) == [(0, 16), (16, 32), (32, 48), (48, 64)]
+
+
+# ---------------------------------------------------------------------------
+# MoE: fp64 definition and the float32 fixed-order combine
+# ---------------------------------------------------------------------------
+
+def test_moe_ref_brute_force():
+    rng = np.random.default_rng(11)
+    T, E, N, K, topk = 4, 5, 3, 8, 2
+    H = wl.normal_bf16(rng, (T, K))
+    We = wl.normal_bf16(rng, (E, N, K), 0.5)
+    ids, w = wl.route_topk(rng, T, E, topk)
+    got = oracle.moe_ref(H, We, ids, w)
+    for t in range(T):
+        for n in range(N):
+            acc = Fraction(0)
+            for s in range(topk):
+                e = ids[t, s]
+                y = sum(bf16_value_independent(int(h)) * bf16_value_independent(int(x))
+                        for h, x in zip(H[t], We[e, n]) if h & 0x7FFF and x & 0x7FFF)
+                acc += Fraction(float(w[t, s])) * y
+            assert abs(got[t, n] - float(acc)) <= 1e-12 * (1 + abs(float(acc)))
+
+
+def test_moe_top1_unit_gate_is_the_contraction():
+    rng = np.random.default_rng(12)
+    T, E, N, K = 6, 3, 4, 16
+    H = wl.normal_bf16(rng, (T, K))
+    We = wl.normal_bf16(rng, (E, N, K), 0.1)
+    ids = rng.integers(0, E, size=(T, 1)).astype(np.int32)
+    w = np.ones((T, 1), dtype=np.float32)
+    got = oracle.moe_ref(H, We, ids, w)
+    for t in range(T):
+        assert np.array_equal(got[t], oracle.contraction_ref(H[t:t + 1], We[ids[t, 0]])[0])
+
+
+@pytest.mark.parametrize("row", load_golden("moe_combine_closed_forms.txt"), ids=lambda r: r[0])
+def test_moe_combine_closed_forms(row):
+    name, ids, gates, ys, expected, _why = row
+    ids = np.array([[int(v) for v in ids.split(",")]])
+    w = np.array([[f32_exact(parse_dyadic(v)) for v in gates.split(",")]], dtype=np.float32)
+    Y = np.array([[[f32_exact(parse_dyadic(v))] for v in ys.split(",")]], dtype=np.float32)
+    got = oracle.moe_combine_f32(Y, ids, w)
+    assert got.shape == (1, 1) and got.dtype == np.float32
+    assert Fraction(float(got[0, 0])) == parse_dyadic(expected)
+
+
+def test_routing_input_is_valid():
+    rng = np.random.default_rng(13)
+    ids, w = wl.route_topk(rng, 100, 64, 8)
+    assert ids.shape == (100, 8) and ids.dtype == np.int32
+    for r in ids:
+        assert len(set(r.tolist())) == 8
+    assert np.allclose(w.sum(axis=1), 1.0, atol=1e-6)
+    assert np.all(np.diff(w, axis=1) <= 0)  # descending-logit slot order
+
+
+# ---------------------------------------------------------------------------
+# Gumbel-max sampling and the k3 metric
+# ---------------------------------------------------------------------------
+
+def test_gumbel_max_samples_the_softmax():
+    rng = np.random.default_rng(14)
+    n = 200_000
+    X = np.tile(np.log(np.array([1.0, 2.0, 3.0, 4.0])), (n, 1))
+    ids = oracle.gumbel_max_ids(X, wl.gumbel(rng, X.shape))
+    freq = np.bincount(ids, minlength=4) / n
+    assert np.allclose(freq, [0.1, 0.2, 0.3, 0.4], atol=0.005)
+    Y = np.zeros((3, 5))
+    Y[:, 2] = 60.0
+    assert np.all(oracle.gumbel_max_ids(Y, wl.gumbel(rng, Y.shape)) == 2)
+
+
+def test_k3_kl():
+    a = np.array([-1.0, -2.0, -0.5])
+    assert oracle.k3_kl(a, a) == 0.0
+    d = 1e-3
+    assert abs(oracle.k3_kl(a, a + d) - d * d / 2) < 1e-9
+    assert oracle.k3_kl(a, a - 0.3) > 0

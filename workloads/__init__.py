@@ -1,0 +1,164 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module produces inputs only: bf16 activations and weights, sampled-token
+ids, Gumbel noise, MoE routings and the row orders of the prefill / decode
+splits.  It holds none of the method's arithmetic (no contraction, no tree, no
+softmax over the vocabulary) and imports neither the oracle nor the product
+library.
+
+Recipe (each config has a fixed seed; children of ``SeedSequence(seed)`` feed
+the separate streams, so changing one stream never shifts another):
+
+* values: float32 draws from ``numpy.random.Generator(PCG64)``; activations
+  N(0, 1), weights N(0, 0.02) (the scaling multiply is float32), rounded to
+  bf16 by round-to-nearest-even on the bit pattern;
+* ids: uniform in ``[0, V)`` where a config says so; where ids must be drawn
+  from the softmax itself, this module supplies the Gumbel noise and the caller
+  takes the argmax with reference logits;
+* prefill / decode: ``n_seq`` sequences of ``n_pos`` positions; the prefill
+  chunk is sequence-major, decode step ``t`` holds position ``t`` of every
+  sequence (shuffled with a seeded permutation where a config asks for mixed
+  sequence origins);
+* MoE routing: router logits N(0, 1) in float64, the top-k experts by logit
+  (ties go to the lower expert id), gate weights are the softmax over the k
+  selected logits, stored as float32.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+__all__ = [
+    "f32_to_bf16_bits",
+    "normal_bf16",
+    "Config",
+    "CONFIGS",
+    "streams",
+    "uniform_ids",
+    "gumbel",
+    "route_topk",
+    "prefill_decode_rows",
+    "integer_bf16",
+]
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); return uint16 bits.
+
+    Finite inputs only.  Adding ``0x7FFF`` plus the lowest kept bit to the
+    32-bit pattern and keeping the upper 16 bits rounds the dropped half to
+    nearest with ties to even.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def normal_bf16(rng: np.random.Generator, shape, std: float = 1.0,
+                chunk: int = 1 << 24) -> np.ndarray:
+    """N(0, std) draws as bf16 bit patterns (uint16), generated in chunks."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+    s = np.float32(std)
+    for i in range(0, n, chunk):
+        j = min(n, i + chunk)
+        x = rng.standard_normal(j - i, dtype=np.float32)
+        if std != 1.0:
+            x *= s
+        out[i:j] = f32_to_bf16_bits(x)
+    return out.reshape(shape)
+
+
+def integer_bf16(rng: np.random.Generator, shape, lo: int, hi: int) -> np.ndarray:
+    """Uniform integers in ``[lo, hi]`` as bf16 bit patterns (exact for |v| <= 256)."""
+    v = rng.integers(lo, hi + 1, size=shape).astype(np.float32)
+    return f32_to_bf16_bits(v)
+
+
+@dataclass(frozen=True)
+class Config:
+    """One workload: sizes, leaf count and seed."""
+    name: str
+    K: int
+    N: int          # output columns (vocabulary size for the LM-head configs)
+    leaves: int
+    seed: int
+    M: tuple = ()   # row counts exercised
+    n_seq: int = 0  # prefill / decode split
+    n_pos: int = 0
+    experts: int = 0
+    topk: int = 0
+    tokens: int = 0
+
+
+CONFIGS = {
+    # Tiny: hidden 512, vocab 4096, 1..64 rows, uniform ids.
+    "tiny": Config("tiny", K=512, N=4096, leaves=8, seed=1000,
+                   M=tuple(range(1, 65))),
+    # Linear layer 4096 x 4096 with the row counts that straddle tile edges.
+    "linear": Config("linear", K=4096, N=4096, leaves=8, seed=1001,
+                     M=(1, 7, 64, 512, 4096, 4097)),
+    # LM head: hidden 4096, vocab 151936; 8192 tokens = 128 sequences x 64.
+    "lmhead": Config("lmhead", K=4096, N=151936, leaves=8, seed=1002,
+                     M=(8192,), n_seq=128, n_pos=64),
+    # MoE-shaped: 64 experts of 2048 -> 1408, top-8 of 4096 tokens.
+    "moe": Config("moe", K=2048, N=1408, leaves=8, seed=1003,
+                  experts=64, topk=8, tokens=4096),
+    # Large: hidden 7168, vocab 129280, 16 leaves; 16384 = 256 sequences x 64.
+    "large": Config("large", K=7168, N=129280, leaves=16, seed=1004,
+                    M=(16384,), n_seq=256, n_pos=64),
+}
+
+_STREAMS = ("H", "W", "ids", "perm", "route", "gumbel", "extra")
+
+
+def streams(seed: int) -> dict:
+    """Independent generators for one config, keyed by purpose."""
+    children = np.random.SeedSequence(seed).spawn(len(_STREAMS))
+    return {k: np.random.Generator(np.random.PCG64(c)) for k, c in zip(_STREAMS, children)}
+
+
+def uniform_ids(rng: np.random.Generator, M: int, V: int) -> np.ndarray:
+    """Sampled-token ids uniform in ``[0, V)``, int64."""
+    return rng.integers(0, V, size=M, dtype=np.int64)
+
+
+def gumbel(rng: np.random.Generator, shape) -> np.ndarray:
+    """Standard Gumbel noise ``-log(-log U)``, U uniform in (0, 1), float64."""
+    u = rng.random(shape)
+    u = np.clip(u, np.finfo(np.float64).tiny, 1.0 - np.finfo(np.float64).epsneg)
+    return -np.log(-np.log(u))
+
+
+def route_topk(rng: np.random.Generator, T: int, E: int, topk: int):
+    """MoE routing input: ``(topk_ids int32 [T, topk], topk_w float32 [T, topk])``.
+
+    Router logits are N(0, 1) in float64.  The selected experts are the ``topk``
+    largest logits, ties to the lower expert id, in descending-logit slot order.
+    Gate weights are the softmax over the selected logits.
+    """
+    logits = rng.standard_normal((T, E))
+    order = np.argsort(-logits, axis=1, kind="stable")[:, :topk]
+    sel = np.take_along_axis(logits, order, axis=1)
+    z = np.exp(sel - sel.max(axis=1, keepdims=True))
+    w = z / z.sum(axis=1, keepdims=True)
+    return order.astype(np.int32), w.astype(np.float32)
+
+
+def prefill_decode_rows(n_seq: int, n_pos: int, rng: np.random.Generator | None = None):
+    """Row orders for one prefill chunk and for ``n_pos`` decode steps.
+
+    Row ``r = s * n_pos + t`` is position ``t`` of sequence ``s``; the prefill
+    chunk holds every row in that sequence-major order.  Decode step ``t`` holds
+    position ``t`` of every sequence; with ``rng`` the sequences of each step are
+    put in a fresh seeded order (mixed sequence origins).  Returns
+    ``(prefill_rows [n_seq*n_pos], decode_steps [n_pos, n_seq])`` as int64.
+    """
+    prefill = np.arange(n_seq * n_pos, dtype=np.int64)
+    steps = np.empty((n_pos, n_seq), dtype=np.int64)
+    for t in range(n_pos):
+        seqs = np.arange(n_seq) if rng is None else rng.permutation(n_seq)
+        steps[t] = seqs * n_pos + t
+    return prefill, steps
