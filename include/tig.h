@@ -1,0 +1,175 @@
+/*
+ * tig.h -- batch-invariant token logprobs on AMD MI355X (gfx950), C ABI.
+ *
+ * The method (from three web pages; titles are given once here and shortened
+ * afterwards):
+ *   [IsoExec]  "IsoExec: Unified Execution to Eliminate Trainer-Inference
+ *              Mismatch in SkyRL", section "Parallelism-invariant kernels" and
+ *              its figure of the fixed binary reduction tree; the contract
+ *              example in "Unified execution contract" (leaves = 8, FP32
+ *              leaves).
+ *   [BitRL]    "Termina el entrenamiento RL mas rapido: Consistente a nivel de
+ *              bits, de alto rendimiento y dirigido por agentes", section 2
+ *              (diff = 0 per sampled token; batch independence; prefill/decode
+ *              consistency), 4.1 (one accumulation order for every M), 4.4 and
+ *              4.5 (expert outputs combined in FP32 in a fixed order), 4.6
+ *              (no host sync, workspaces sized from static bounds).
+ *   [RZero]    "REINFORCE Zero: ..." section 6 (MI355X): libraries that pick
+ *              kernels by shape (e.g. a different tile at 4096 vs 4097 rows)
+ *              break batch invariance.
+ *
+ * Numerical contract, fixed per (K, leaves) and never chosen from M or N:
+ *   - K is cut into `leaves` contiguous leaves of K/leaves columns;
+ *   - inside a leaf, one matrix-core instruction (v_mfma_f32_32x32x16_bf16)
+ *     accumulates 16-column k-steps in ascending order into an FP32 tile that
+ *     starts at +0;
+ *   - the leaves are combined by a balanced tree of adjacent pairs, level by
+ *     level, in FP32 (round to nearest even);
+ *   - for the log-softmax: per row and per 128-column vocabulary tile,
+ *     m_t = max and s_t = sum of exp2((x - m_t) * log2(e)) over the tile by a
+ *     balanced adjacent-pair tree (padded columns add exactly +0); then
+ *     g = max_t m_t and S = sum_t s_t * exp2((m_t - g) * log2(e)) by a balanced
+ *     adjacent-pair tree over the tiles zero-padded to a power of two, and
+ *     lse = g + log2(S) * ln(2); logprob = x[id] - lse.
+ * A row's bits therefore depend only on that row, the weights, K and leaves:
+ * not on M, on the row's position, or on how rows are split into calls.
+ *
+ * Conventions for every entry point:
+ *   - all matrices are row-major; bf16 operands are K-contiguous;
+ *   - every pointer argument is a device pointer the caller owns (for example
+ *     torch.empty(..., device="cuda")); the library allocates nothing and keeps
+ *     no pointer after the call returns;
+ *   - work is enqueued on `stream` (NULL = the default stream); no call waits
+ *     on the device or reads device memory back;
+ *   - arguments are validated on the host before any launch; a failing call
+ *     launches nothing and returns a status; tig_last_error() gives a message
+ *     for the calling thread's last failure;
+ *   - bf16 pointers must be 16-byte aligned and their row strides multiples of
+ *     8 elements (16 bytes), else TIG_ERR_UNSUPPORTED.
+ */
+#ifndef TIG_H
+#define TIG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TIG_OK = 0,
+  TIG_ERR_INVALID_ARG = 1, /* null pointer, negative size, leaves not a power of two, ... */
+  TIG_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels implement */
+  TIG_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the query says */
+  TIG_ERR_HIP = 4          /* a HIP runtime call or a launch failed */
+} tig_status;
+
+typedef enum { TIG_OUT_F32 = 0, TIG_OUT_BF16 = 1 } tig_out_dtype;
+
+/*
+ * Leaf-tree contraction  C[m, n] = tree_l( sum_{k in leaf l} A[m, k] * W[n, k] ).
+ * [IsoExec, Parallelism-invariant kernels]; [BitRL, 4.1].
+ *   A     bf16 [M, K], row stride lda (elements, >= K)
+ *   W     bf16 [N, K], row stride ldw (elements, >= K)   (a Linear weight)
+ *   C     [M, N], row stride ldc (elements, >= N); FP32 tree output, or that
+ *         value rounded once to bf16 (nearest even) when out_dtype is BF16
+ *   leaves  power of two in [1, 64]; K % leaves == 0
+ * Implemented: leaves <= 16 and K/leaves a multiple of 64 (else UNSUPPORTED).
+ * M == 0 or N == 0 is TIG_OK and launches nothing.  C must not overlap A or W.
+ */
+tig_status tig_tree_gemm(const void* A, int64_t lda, const void* W, int64_t ldw,
+                         void* C, int64_t ldc, tig_out_dtype out_dtype,
+                         int64_t M, int64_t N, int64_t K, int32_t leaves,
+                         hipStream_t stream);
+
+/*
+ * Fused LM-head logprob of the sampled tokens, the M x V logits never stored.
+ * [BitRL, section 2]: the logprob of each sampled token, identical bit for bit
+ * whatever the batch, position or prefill/decode split.
+ *   H            bf16 [M, K] contiguous (hidden states)
+ *   W            bf16 [n_vocab, K] contiguous (LM-head weight)
+ *   ids          int64 [M], sampled token per row; an id outside
+ *                [0, n_vocab) gives logprob NaN for that row only (checked
+ *                on the device, no error code: nothing is read back)
+ *   logprob_out  float [M]
+ *   lse_out      float [M] log-sum-exp of the row's logits, or NULL to skip
+ *   workspace    device scratch of at least tig_logprob_workspace_bytes()
+ *                bytes, 256-byte aligned; contents on entry are ignored
+ * Implemented: leaves <= 16, K/leaves a multiple of 64, n_vocab <= 2^23.
+ * M == 0 is TIG_OK and launches nothing.
+ */
+tig_status tig_logprob_gather(const void* H, const void* W, const int64_t* ids,
+                              float* logprob_out, float* lse_out,
+                              int64_t M, int64_t K, int64_t n_vocab, int32_t leaves,
+                              void* workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* Workspace bytes tig_logprob_gather needs for these sizes (written to *bytes). */
+tig_status tig_logprob_workspace_bytes(int64_t M, int64_t K, int64_t n_vocab,
+                                       int32_t leaves, size_t* bytes);
+
+/*
+ * MoE-shaped contraction with a fixed-order FP32 combine.
+ * [BitRL, 4.4] per-row expert result independent of layout; [BitRL, 4.5] and
+ * [IsoExec, Parallelism-invariant kernels] expert outputs combined in a fixed
+ * routing order.  Order used here: ascending expert id (equal ids keep slot
+ * order); acc = acc + w * y, an FP32 multiply then an FP32 add, from +0.
+ *   H          bf16 [T, K] contiguous (tokens)
+ *   W_experts  bf16 [n_experts, N, K] contiguous
+ *   topk_ids   int32 [T, topk], each in [0, n_experts); an id out of range
+ *              makes that token's output NaN (device-side check)
+ *   topk_w     float [T, topk] gate weights
+ *   out        float [T, N]
+ *   workspace  >= tig_moe_workspace_bytes() bytes, 256-byte aligned
+ * Each expert's rows are gathered on the device (stable by token index) and
+ * multiplied by the same leaf-tree kernel as tig_tree_gemm with FP32 output,
+ * so a token's expert output equals tig_tree_gemm on that token's row alone.
+ * The grid is sized from the static bound T*topk; nothing is read back.
+ * Implemented: leaves <= 16, K/leaves a multiple of 64, topk <= 16.
+ */
+tig_status tig_moe_tree_gemm_combine(const void* H, const void* W_experts, int32_t n_experts,
+                                     const int32_t* topk_ids, const float* topk_w, int32_t topk,
+                                     float* out, int64_t T, int64_t N, int64_t K, int32_t leaves,
+                                     void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/* Workspace bytes tig_moe_tree_gemm_combine needs (written to *bytes). */
+tig_status tig_moe_workspace_bytes(int64_t T, int64_t N, int64_t K, int32_t n_experts,
+                                   int32_t topk, size_t* bytes);
+
+/*
+ * The pinned numerical policy for (K, leaves): the constants that decide the
+ * bits, in the spirit of [IsoExec, Unified execution contract] (implementation
+ * and constants pinned per region; identities are SHA-256 digests).
+ * `policy` is a canonical NUL-terminated text; `digest` is SHA-256 of its bytes
+ * (without the NUL).  N and M never enter it.
+ */
+typedef struct {
+  int32_t version;     /* policy version */
+  int32_t leaves;      /* L */
+  int32_t leaf_len;    /* K / L */
+  int32_t block_m;     /* rows per workgroup tile */
+  int32_t block_n;     /* columns per workgroup tile = vocabulary tile width */
+  int32_t block_k;     /* k columns staged per LDS step (does not change bits) */
+  int32_t mfma_m, mfma_n, mfma_k; /* 32, 32, 16 */
+  int32_t tree_id;     /* 1 = balanced tree of adjacent pairs */
+  uint8_t digest[32];
+  char policy[512];
+} tig_plan;
+
+tig_status tig_plan_describe(int64_t K, int32_t leaves, tig_plan* out);
+
+/* Static text for a status code ("unknown status" for other values). */
+const char* tig_status_string(tig_status s);
+
+/* Message for the calling thread's most recent failing call ("" if none). */
+const char* tig_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TIG_H */

@@ -1,0 +1,280 @@
+"""Batch-invariant token logprobs on MI355X: Python binding of ``libtig.so``.
+
+The functions named ``tig_*`` mirror the C entry points of ``include/tig.h``
+one for one: they check that each tensor lives on the GPU with the dtype and
+shape the C call expects, then pass raw device pointers, sizes and the current
+HIP stream.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback: if ``libtig.so`` is missing or fails to load, every call
+raises.  PyTorch is used only for device memory and streams.
+
+``tree_gemm``, ``logprob_gather`` and ``moe_tree_gemm_combine`` are
+conveniences that allocate the outputs and the workspace with torch and then
+call the matching ``tig_*`` function.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "TigError", "load", "lib_path",
+    "tig_tree_gemm", "tig_logprob_gather", "tig_logprob_workspace_bytes",
+    "tig_moe_tree_gemm_combine", "tig_moe_workspace_bytes", "tig_plan_describe",
+    "tig_status_string", "tig_last_error",
+    "tree_gemm", "logprob_gather", "moe_tree_gemm_combine",
+    "TIG_OK", "TIG_ERR_INVALID_ARG", "TIG_ERR_UNSUPPORTED", "TIG_ERR_WORKSPACE", "TIG_ERR_HIP",
+    "TIG_OUT_F32", "TIG_OUT_BF16",
+]
+
+TIG_OK, TIG_ERR_INVALID_ARG, TIG_ERR_UNSUPPORTED, TIG_ERR_WORKSPACE, TIG_ERR_HIP = range(5)
+TIG_OUT_F32, TIG_OUT_BF16 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libtig.so")
+
+
+class TigError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {tig_status_string(status)} ({status}): {detail}")
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [
+        ("version", ctypes.c_int32), ("leaves", ctypes.c_int32), ("leaf_len", ctypes.c_int32),
+        ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32), ("block_k", ctypes.c_int32),
+        ("mfma_m", ctypes.c_int32), ("mfma_n", ctypes.c_int32), ("mfma_k", ctypes.c_int32),
+        ("tree_id", ctypes.c_int32), ("digest", ctypes.c_uint8 * 32), ("policy", ctypes.c_char * 512),
+    ]
+
+
+_i64, _i32, _vp, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t
+
+_SIGNATURES = {
+    "tig_tree_gemm": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _i32, _vp]),
+    "tig_logprob_gather": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
+    "tig_logprob_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, ctypes.POINTER(_sz)]),
+    "tig_moe_tree_gemm_combine": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i64, _i64, _i64,
+                                         _i32, _vp, _sz, _vp]),
+    "tig_moe_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, _i32, ctypes.POINTER(_sz)]),
+    "tig_plan_describe": (_i32, [_i64, _i32, ctypes.POINTER(_Plan)]),
+    "tig_status_string": (ctypes.c_char_p, [_i32]),
+    "tig_last_error": (ctypes.c_char_p, []),
+}
+
+
+def load():
+    """Load ``libtig.so`` (once).  Raises if it is missing or does not load."""
+    global _LIB
+    if _LIB is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built: run `python -m invariant_gemm_token_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def tig_status_string(status: int) -> str:
+    return load().tig_status_string(int(status)).decode()
+
+
+def tig_last_error() -> str:
+    return load().tig_last_error().decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != TIG_OK:
+        raise TigError(status, where, tig_last_error())
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _need(t, name, dtype, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (got device {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions (got shape {tuple(t.shape)})")
+
+
+def _rowmajor(t, name):
+    if t.numel() and t.stride(-1) != 1:
+        raise ValueError(f"{name} must have unit stride along its last dimension")
+
+
+def _contig(t, name):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _same_device(*ts):
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on different devices: {sorted(map(str, devs))}")
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def tig_tree_gemm(A, W, C, leaves: int, stream=None) -> None:
+    """``C[M, N] = leaf-tree(A[M, K] W[N, K]^T)``; C is float32 or bfloat16."""
+    torch = _torch()
+    _need(A, "A", torch.bfloat16, 2)
+    _need(W, "W", torch.bfloat16, 2)
+    if C.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("C must be float32 or bfloat16")
+    _need(C, "C", C.dtype, 2)
+    _same_device(A, W, C)
+    for t, n in ((A, "A"), (W, "W"), (C, "C")):
+        _rowmajor(t, n)
+    M, K = A.shape
+    N = W.shape[0]
+    if W.shape[1] != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shapes do not match: A {tuple(A.shape)}, W {tuple(W.shape)}, C {tuple(C.shape)}")
+    out_dtype = TIG_OUT_F32 if C.dtype == torch.float32 else TIG_OUT_BF16
+    # A single row has no row stride of its own: pass the packed one.
+    lda = A.stride(0) if M > 1 else K
+    ldw = W.stride(0) if N > 1 else K
+    ldc = C.stride(0) if M > 1 else N
+    st = load().tig_tree_gemm(A.data_ptr(), lda, W.data_ptr(), ldw, C.data_ptr(), ldc, out_dtype,
+                              M, N, K, int(leaves), _stream(stream))
+    _check(st, "tig_tree_gemm")
+
+
+def tig_logprob_workspace_bytes(M: int, K: int, n_vocab: int, leaves: int) -> int:
+    out = _sz(0)
+    _check(load().tig_logprob_workspace_bytes(int(M), int(K), int(n_vocab), int(leaves),
+                                              ctypes.byref(out)), "tig_logprob_workspace_bytes")
+    return int(out.value)
+
+
+def tig_logprob_gather(H, W, ids, logprob_out, lse_out, leaves: int, workspace, stream=None) -> None:
+    """Logprob of each row's sampled token under softmax(H W^T); see include/tig.h."""
+    torch = _torch()
+    _need(H, "H", torch.bfloat16, 2)
+    _need(W, "W", torch.bfloat16, 2)
+    _need(ids, "ids", torch.int64, 1)
+    _need(logprob_out, "logprob_out", torch.float32, 1)
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, 1)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _same_device(H, W, ids, logprob_out, lse_out, workspace)
+    for t, n in ((H, "H"), (W, "W"), (ids, "ids"), (logprob_out, "logprob_out"), (workspace, "workspace")):
+        _contig(t, n)
+    if lse_out is not None:
+        _contig(lse_out, "lse_out")
+    M, K = H.shape
+    V = W.shape[0]
+    if W.shape[1] != K or ids.shape[0] != M or logprob_out.shape[0] != M or (
+            lse_out is not None and lse_out.shape[0] != M):
+        raise ValueError("shapes do not match")
+    st = load().tig_logprob_gather(H.data_ptr(), W.data_ptr(), ids.data_ptr(), logprob_out.data_ptr(),
+                                   lse_out.data_ptr() if lse_out is not None else None, M, K, V,
+                                   int(leaves), workspace.data_ptr(), workspace.numel(),
+                                   _stream(stream))
+    _check(st, "tig_logprob_gather")
+
+
+def tig_moe_workspace_bytes(T: int, N: int, K: int, n_experts: int, topk: int) -> int:
+    out = _sz(0)
+    _check(load().tig_moe_workspace_bytes(int(T), int(N), int(K), int(n_experts), int(topk),
+                                          ctypes.byref(out)), "tig_moe_workspace_bytes")
+    return int(out.value)
+
+
+def tig_moe_tree_gemm_combine(H, W_experts, topk_ids, topk_w, out, leaves: int, workspace,
+                              stream=None) -> None:
+    """MoE-shaped leaf-tree contraction plus ascending-expert-id FP32 combine."""
+    torch = _torch()
+    _need(H, "H", torch.bfloat16, 2)
+    _need(W_experts, "W_experts", torch.bfloat16, 3)
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    _need(out, "out", torch.float32, 2)
+    _need(workspace, "workspace", torch.uint8, 1)
+    _same_device(H, W_experts, topk_ids, topk_w, out, workspace)
+    for t, n in ((H, "H"), (W_experts, "W_experts"), (topk_ids, "topk_ids"), (topk_w, "topk_w"),
+                 (out, "out"), (workspace, "workspace")):
+        _contig(t, n)
+    T, K = H.shape
+    E, N, K2 = W_experts.shape
+    topk = topk_ids.shape[1]
+    if K2 != K or tuple(topk_ids.shape) != (T, topk) or tuple(topk_w.shape) != (T, topk) or tuple(
+            out.shape) != (T, N):
+        raise ValueError("shapes do not match")
+    st = load().tig_moe_tree_gemm_combine(H.data_ptr(), W_experts.data_ptr(), E, topk_ids.data_ptr(),
+                                          topk_w.data_ptr(), topk, out.data_ptr(), T, N, K, int(leaves),
+                                          workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _check(st, "tig_moe_tree_gemm_combine")
+
+
+def tig_plan_describe(K: int, leaves: int) -> dict:
+    plan = _Plan()
+    _check(load().tig_plan_describe(int(K), int(leaves), ctypes.byref(plan)), "tig_plan_describe")
+    d = {f: getattr(plan, f) for f, _ in _Plan._fields_ if f not in ("digest", "policy")}
+    d["digest"] = bytes(plan.digest).hex()
+    d["policy"] = plan.policy.decode()
+    return d
+
+
+# ---------------------------------------------------------------------------
+# conveniences (allocate outputs / workspace with torch, then call the above)
+# ---------------------------------------------------------------------------
+
+def tree_gemm(A, W, leaves: int, out_dtype=None, stream=None):
+    torch = _torch()
+    C = torch.empty((A.shape[0], W.shape[0]), dtype=out_dtype or torch.float32, device=A.device)
+    tig_tree_gemm(A, W, C, leaves, stream)
+    return C
+
+
+def logprob_gather(H, W, ids, leaves: int, workspace=None, with_lse: bool = True, stream=None):
+    torch = _torch()
+    M, K = H.shape
+    need = tig_logprob_workspace_bytes(M, K, W.shape[0], leaves)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=H.device)
+    lp = torch.empty(M, dtype=torch.float32, device=H.device)
+    lse = torch.empty(M, dtype=torch.float32, device=H.device) if with_lse else None
+    tig_logprob_gather(H, W, ids, lp, lse, leaves, workspace, stream)
+    return lp, lse
+
+
+def moe_tree_gemm_combine(H, W_experts, topk_ids, topk_w, leaves: int, workspace=None, stream=None):
+    torch = _torch()
+    T, K = H.shape
+    E, N, _ = W_experts.shape
+    need = tig_moe_workspace_bytes(T, N, K, E, topk_ids.shape[1])
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=H.device)
+    out = torch.empty((T, N), dtype=torch.float32, device=H.device)
+    tig_moe_tree_gemm_combine(H, W_experts, topk_ids, topk_w, out, leaves, workspace, stream)
+    return out

@@ -1,0 +1,161 @@
+"""Host-side tests of the C ABI (no GPU): symbols, plan digest, error paths.
+
+Every call here fails validation on the host before any launch, or takes the
+M == 0 no-op path; nothing reaches a kernel.  Calls that pass fake (non-NULL)
+device pointers run only when no GPU is visible, so that a validation bug can
+never turn into a launch on a real device.
+"""
+
+import ctypes
+import hashlib
+import os
+import re
+
+import pytest
+
+import invariant_gemm_token_amd as tig
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tig.h")
+FAKE = 0x10000  # aligned, never dereferenced
+
+
+def _no_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() == 0
+    except Exception:
+        return True
+
+
+fake_ptrs = pytest.mark.skipif(not _no_gpu(), reason="fake pointers only where no GPU is visible")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tig_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"tig_tree_gemm", "tig_logprob_gather", "tig_moe_tree_gemm_combine",
+            "tig_plan_describe"} <= set(names)
+    lib = ctypes.CDLL(tig.lib_path())
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in tig.h but not exported"
+    tig.load()
+
+
+def test_status_strings():
+    assert tig.tig_status_string(tig.TIG_OK) == "ok"
+    assert tig.tig_status_string(tig.TIG_ERR_WORKSPACE) == "workspace too small"
+    assert tig.tig_status_string(99) == "unknown status"
+
+
+@pytest.mark.parametrize("K,leaves", [(512, 8), (4096, 8), (7168, 16), (2048, 8), (1024, 1), (1024, 16)])
+def test_plan_digest_is_sha256_of_policy(K, leaves):
+    p = tig.tig_plan_describe(K, leaves)
+    assert p["leaves"] == leaves and p["leaf_len"] == K // leaves
+    assert (p["block_m"], p["block_n"], p["block_k"]) == (128, 128, 64)
+    assert (p["mfma_m"], p["mfma_n"], p["mfma_k"]) == (32, 32, 16)
+    assert p["digest"] == hashlib.sha256(p["policy"].encode()).hexdigest()
+    assert f"K={K};leaves={leaves};" in p["policy"]
+
+
+def test_plan_digest_separates_policies():
+    d = {tig.tig_plan_describe(K, L)["digest"] for K, L in [(4096, 8), (4096, 4), (8192, 8), (512, 8)]}
+    assert len(d) == 4
+
+
+@pytest.mark.parametrize("K,leaves,status", [
+    (4096, 3, tig.TIG_ERR_INVALID_ARG),     # not a power of two
+    (4096, 0, tig.TIG_ERR_INVALID_ARG),
+    (4096, 128, tig.TIG_ERR_INVALID_ARG),   # above 64
+    (4096, 32, tig.TIG_ERR_UNSUPPORTED),    # valid, not implemented
+    (0, 8, tig.TIG_ERR_INVALID_ARG),
+    (4100, 4, tig.TIG_ERR_UNSUPPORTED),     # leaf length 1025 not a multiple of 64
+    (1000, 8, tig.TIG_ERR_UNSUPPORTED),     # 1000 / 8 = 125
+    (256, 8, tig.TIG_ERR_UNSUPPORTED),      # leaf of 32 columns
+])
+def test_plan_rejects(K, leaves, status):
+    with pytest.raises(tig.TigError) as e:
+        tig.tig_plan_describe(K, leaves)
+    assert e.value.status == status
+    assert tig.tig_last_error()
+
+
+def test_workspace_queries():
+    b = tig.tig_logprob_workspace_bytes(8192, 4096, 151936, 8)
+    assert b == 8192 * 1187 * 8 + 8192 * 4
+    assert tig.tig_logprob_workspace_bytes(0, 4096, 151936, 8) == 0
+    assert tig.tig_logprob_workspace_bytes(3, 512, 1, 8) == 256 + 256
+    m = tig.tig_moe_workspace_bytes(4096, 1408, 2048, 64, 8)
+    assert m >= 4096 * 8 * 1408 * 4
+    with pytest.raises(tig.TigError) as e:
+        tig.tig_logprob_workspace_bytes(8, 4096, 0, 8)
+    assert e.value.status == tig.TIG_ERR_INVALID_ARG
+    with pytest.raises(tig.TigError) as e:
+        tig.tig_logprob_workspace_bytes(8, 4096, 128 * 65536 + 1, 8)
+    assert e.value.status == tig.TIG_ERR_UNSUPPORTED
+    with pytest.raises(tig.TigError) as e:
+        tig.tig_moe_workspace_bytes(8, 8, 64, 4, 17)
+    assert e.value.status == tig.TIG_ERR_UNSUPPORTED
+
+
+def _raw():
+    return tig.load()
+
+
+def test_zero_rows_is_a_noop_even_with_null_pointers():
+    lib = _raw()
+    assert lib.tig_tree_gemm(None, 4096, None, 4096, None, 4096, 0, 0, 4096, 4096, 8, None) == tig.TIG_OK
+    assert lib.tig_tree_gemm(None, 4096, None, 4096, None, 0, 0, 5, 0, 4096, 8, None) == tig.TIG_OK
+    assert lib.tig_logprob_gather(None, None, None, None, None, 0, 4096, 151936, 8, None, 0, None) == tig.TIG_OK
+    assert lib.tig_moe_tree_gemm_combine(None, None, 64, None, None, 8, None, 0, 1408, 2048, 8,
+                                         None, 0, None) == tig.TIG_OK
+
+
+def test_null_pointers_rejected():
+    lib = _raw()
+    assert lib.tig_tree_gemm(None, 512, None, 512, None, 64, 0, 4, 64, 512, 8, None) == tig.TIG_ERR_INVALID_ARG
+    assert lib.tig_logprob_gather(None, None, None, None, None, 4, 512, 64, 8, None, 0, None) == tig.TIG_ERR_INVALID_ARG
+    assert "NULL" in tig.tig_last_error()
+
+
+def test_negative_sizes_and_bad_strides_rejected():
+    lib = _raw()
+    assert lib.tig_tree_gemm(None, 512, None, 512, None, 64, 0, -1, 64, 512, 8, None) == tig.TIG_ERR_INVALID_ARG
+    assert lib.tig_tree_gemm(None, 256, None, 512, None, 64, 0, 4, 64, 512, 8, None) == tig.TIG_ERR_INVALID_ARG
+    assert lib.tig_tree_gemm(None, 512, None, 512, None, 32, 0, 4, 64, 512, 8, None) == tig.TIG_ERR_INVALID_ARG
+    assert lib.tig_tree_gemm(None, 512, None, 512, None, 64, 7, 4, 64, 512, 8, None) == tig.TIG_ERR_INVALID_ARG
+
+
+@fake_ptrs
+def test_alignment_and_workspace_errors_with_fake_pointers():
+    lib = _raw()
+    F = FAKE
+    # misaligned A, odd row stride
+    assert lib.tig_tree_gemm(F + 2, 512, F, 512, F, 64, 0, 4, 64, 512, 8, None) == tig.TIG_ERR_UNSUPPORTED
+    assert lib.tig_tree_gemm(F, 516, F, 512, F, 64, 0, 4, 64, 512, 8, None) == tig.TIG_ERR_UNSUPPORTED
+    # workspace missing / too small / misaligned
+    need = tig.tig_logprob_workspace_bytes(4, 512, 64, 8)
+    assert lib.tig_logprob_gather(F, F, F, F, None, 4, 512, 64, 8, None, 0, None) == tig.TIG_ERR_WORKSPACE
+    assert lib.tig_logprob_gather(F, F, F, F, None, 4, 512, 64, 8, F, need - 1, None) == tig.TIG_ERR_WORKSPACE
+    assert lib.tig_logprob_gather(F, F, F, F, None, 4, 512, 64, 8, F + 16, need, None) == tig.TIG_ERR_INVALID_ARG
+    needm = tig.tig_moe_workspace_bytes(16, 128, 512, 4, 2)
+    assert lib.tig_moe_tree_gemm_combine(F, F, 4, F, F, 2, F, 16, 128, 512, 8, F, needm - 1,
+                                         None) == tig.TIG_ERR_WORKSPACE
+    assert lib.tig_moe_tree_gemm_combine(F, F, 4, F, F, 2, F, 16, 128, 512, 3, F, needm,
+                                         None) == tig.TIG_ERR_INVALID_ARG
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    A = torch.zeros((4, 512), dtype=torch.bfloat16)
+    W = torch.zeros((64, 512), dtype=torch.bfloat16)
+    C = torch.zeros((4, 64), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        tig.tig_tree_gemm(A, W, C, 8)
+    with pytest.raises((TypeError, ValueError)):
+        tig.tig_tree_gemm(A.float(), W, C, 8)

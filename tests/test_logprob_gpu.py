@@ -1,0 +1,162 @@
+"""GPU parity and invariance of tig_logprob_gather (fused LM-head logprob).
+
+[BitRL, section 2]: the logprob of every sampled token must be bit-identical
+whatever the batch composition, the row position and the prefill / decode
+split (diff = 0: max, mean, std of |delta| and k3 KL all exactly zero).
+Parity bar against the fp64 oracle: |delta logprob| <= 1e-3 absolute.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import assert_bitwise, dev_bf16, diff_stats, say
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-3
+
+
+def _parity(lp, lse, ref_lp, ref_lse, what):
+    lp = lp.cpu().double().numpy()
+    lse = lse.cpu().double().numpy()
+    e1 = np.max(np.abs(lp - ref_lp))
+    e2 = np.max(np.abs(lse - ref_lse))
+    say(f"{what}: max |dlogprob| {e1:.3e}  max |dlse| {e2:.3e}")
+    assert e1 <= TOL and e2 <= TOL, what
+    return e1
+
+
+def _tiny():
+    cfg = wl.CONFIGS["tiny"]
+    s = wl.streams(cfg.seed)
+    H = wl.normal_bf16(s["H"], (max(cfg.M), cfg.K), 1.0)
+    W = wl.normal_bf16(s["W"], (cfg.N, cfg.K), 0.02)
+    ids = wl.uniform_ids(s["ids"], max(cfg.M), cfg.N)
+    return cfg, H, W, ids
+
+
+def test_tiny_every_M_parity_and_invariance(gpu_lib):
+    cfg, H, W, ids = _tiny()
+    Hd, Wd, idd = dev_bf16(H), dev_bf16(W), torch.from_numpy(ids).cuda()
+    ref_lp, ref_lse = oracle.logprob_ref(H, W, ids)
+    full_lp, full_lse = gpu_lib.logprob_gather(Hd, Wd, idd, cfg.leaves)
+    _parity(full_lp, full_lse, ref_lp, ref_lse, "tiny M=64")
+    for M in cfg.M:
+        lp, lse = gpu_lib.logprob_gather(Hd[:M], Wd, idd[:M], cfg.leaves)
+        assert_bitwise(lp, full_lp[:M], f"tiny logprob M={M}")
+        assert_bitwise(lse, full_lse[:M], f"tiny lse M={M}")
+
+
+@pytest.mark.parametrize("V", [1, 2, 127, 128, 129, 255, 1000, 4097])
+@pytest.mark.parametrize("M", [1, 127, 128, 129, 300])
+def test_tile_edges_parity(gpu_lib, M, V):
+    rng = np.random.default_rng(M * 100003 + V)
+    K = 512
+    H = wl.normal_bf16(rng, (M, K), 1.0)
+    W = wl.normal_bf16(rng, (V, K), 0.05)
+    ids = rng.integers(0, V, size=M)
+    lp, lse = gpu_lib.logprob_gather(dev_bf16(H), dev_bf16(W), torch.from_numpy(ids).cuda(), 8)
+    ref_lp, ref_lse = oracle.logprob_ref(H, W, ids)
+    _parity(lp, lse, ref_lp, ref_lse, f"M={M} V={V}")
+
+
+@pytest.mark.parametrize("V", [4096, 151936, 1000, 129])
+def test_equal_logits_closed_form(gpu_lib, V):
+    """All W rows equal -> all logits equal -> logprob = -ln V (sum exp = V exactly)."""
+    rng = np.random.default_rng(V)
+    K = 512
+    H = wl.normal_bf16(rng, (70, K), 1.0)
+    row = wl.normal_bf16(rng, (1, K), 0.05)
+    W = np.repeat(row, V, axis=0)
+    ids = rng.integers(0, V, size=70)
+    lp, lse = gpu_lib.logprob_gather(dev_bf16(H), dev_bf16(W), torch.from_numpy(ids).cuda(), 8)
+    lp = lp.cpu().double().numpy()
+    assert np.max(np.abs(lp + math.log(V))) < 1e-5
+    # the logits themselves are the tree contraction's
+    X = gpu_lib.tree_gemm(dev_bf16(H), dev_bf16(row), 8).cpu().double().numpy()[:, 0]
+    assert np.max(np.abs(lse.cpu().double().numpy() - (X + math.log(V)))) < 1e-5
+
+
+def test_vocab_of_one(gpu_lib):
+    """V = 1: lse is the single logit bit for bit and the logprob is exactly 0."""
+    rng = np.random.default_rng(1)
+    H = wl.normal_bf16(rng, (200, 512), 1.0)
+    W = wl.normal_bf16(rng, (1, 512), 0.05)
+    Hd, Wd = dev_bf16(H), dev_bf16(W)
+    lp, lse = gpu_lib.logprob_gather(Hd, Wd, torch.zeros(200, dtype=torch.int64, device="cuda:0"), 8)
+    assert torch.all(lp == 0.0)
+    assert_bitwise(lse, gpu_lib.tree_gemm(Hd, Wd, 8)[:, 0], "lse == logit")
+
+
+def test_invalid_ids_give_nan_for_that_row_only(gpu_lib):
+    cfg, H, W, ids = _tiny()
+    ids = ids[:6].copy()
+    ids[1], ids[4] = -1, cfg.N
+    lp, lse = gpu_lib.logprob_gather(dev_bf16(H[:6]), dev_bf16(W), torch.from_numpy(ids).cuda(), 8)
+    lp = lp.cpu().numpy()
+    assert np.isnan(lp[1]) and np.isnan(lp[4])
+    assert np.all(np.isfinite(lp[[0, 2, 3, 5]]))
+    assert torch.all(torch.isfinite(lse))
+    ref, _ = oracle.logprob_ref(H[:6], W, ids)
+    assert np.max(np.abs(lp[[0, 2, 3, 5]] - ref[[0, 2, 3, 5]])) <= TOL
+
+
+def test_lse_optional_and_repeatable(gpu_lib):
+    cfg, H, W, ids = _tiny()
+    Hd, Wd, idd = dev_bf16(H), dev_bf16(W), torch.from_numpy(ids).cuda()
+    a, _ = gpu_lib.logprob_gather(Hd, Wd, idd, 8, with_lse=False)
+    for _ in range(5):
+        b, _ = gpu_lib.logprob_gather(Hd, Wd, idd, 8)
+        assert_bitwise(a, b, "repeat / lse optional")
+
+
+def _prefill_decode(gpu_lib, name, n_oracle_rows, shuffle):
+    cfg = wl.CONFIGS[name]
+    s = wl.streams(cfg.seed)
+    M = cfg.n_seq * cfg.n_pos
+    say(f"{name}: generating H[{M},{cfg.K}] W[{cfg.N},{cfg.K}]")
+    H = wl.normal_bf16(s["H"], (M, cfg.K), 1.0)
+    W = wl.normal_bf16(s["W"], (cfg.N, cfg.K), 0.02)
+    ids = wl.uniform_ids(s["ids"], M, cfg.N)
+    # rows checked against the oracle take ids drawn from the softmax itself
+    rows = np.sort(s["perm"].choice(M, size=n_oracle_rows, replace=False))
+    W64 = oracle.bf16_bits_to_f64(W)
+    X = oracle.contraction_ref(H[rows], W64)
+    ids[rows] = oracle.gumbel_max_ids(X, wl.gumbel(s["gumbel"], X.shape))
+    ref_lp, ref_lse = oracle.logprob_ref(H[rows], W64, ids[rows])
+    del X, W64
+
+    Hd, Wd, idd = dev_bf16(H), dev_bf16(W), torch.from_numpy(ids).cuda()
+    prefill_rows, steps = wl.prefill_decode_rows(cfg.n_seq, cfg.n_pos, s["extra"] if shuffle else None)
+    say(f"{name}: prefill M={M}")
+    lp, lse = gpu_lib.logprob_gather(Hd, Wd, idd, cfg.leaves)
+    _parity(lp[rows], lse[rows], ref_lp, ref_lse, f"{name} sampled rows vs oracle")
+    say(f"{name}: {cfg.n_pos} decode steps of {cfg.n_seq}")
+    dec_lp = torch.empty_like(lp)
+    dec_lse = torch.empty_like(lse)
+    ws = torch.empty(gpu_lib.tig_logprob_workspace_bytes(cfg.n_seq, cfg.K, cfg.N, cfg.leaves),
+                     dtype=torch.uint8, device="cuda:0")
+    for t in range(cfg.n_pos):
+        r = torch.from_numpy(steps[t]).cuda()
+        a, b = gpu_lib.logprob_gather(Hd[r].contiguous(), Wd, idd[r].contiguous(), cfg.leaves, workspace=ws)
+        dec_lp[r] = a
+        dec_lse[r] = b
+    st = diff_stats(lp.cpu().numpy(), dec_lp.cpu().numpy())
+    say(f"{name}: prefill vs decode diff {st}")
+    assert_bitwise(dec_lp, lp, f"{name} prefill vs decode logprob")
+    assert_bitwise(dec_lse, lse, f"{name} prefill vs decode lse")
+    assert st == {"max": 0.0, "mean": 0.0, "std": 0.0, "k3": 0.0}
+
+
+@pytest.mark.slow
+def test_lmhead_prefill_vs_decode(gpu_lib):
+    _prefill_decode(gpu_lib, "lmhead", n_oracle_rows=256, shuffle=False)
+
+
+@pytest.mark.slow
+def test_large_prefill_vs_decode(gpu_lib):
+    _prefill_decode(gpu_lib, "large", n_oracle_rows=128, shuffle=True)
