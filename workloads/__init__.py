@@ -44,6 +44,17 @@ __all__ = [
 ]
 
 
+def _round_bf16_into(x: np.ndarray, out: np.ndarray, tmp: np.ndarray) -> None:
+    """bf16 bits of float32 ``x`` into ``out`` (uint16), using ``tmp`` (uint32) as scratch."""
+    u = x.view(np.uint32)
+    np.right_shift(u, np.uint32(16), out=tmp)
+    np.bitwise_and(tmp, np.uint32(1), out=tmp)
+    np.add(tmp, np.uint32(0x7FFF), out=tmp)
+    np.add(tmp, u, out=tmp)
+    np.right_shift(tmp, np.uint32(16), out=tmp)
+    np.copyto(out, tmp, casting="unsafe")
+
+
 def f32_to_bf16_bits(x) -> np.ndarray:
     """Round float32 values to bf16 (nearest, ties to even); return uint16 bits.
 
@@ -51,23 +62,32 @@ def f32_to_bf16_bits(x) -> np.ndarray:
     32-bit pattern and keeping the upper 16 bits rounds the dropped half to
     nearest with ties to even.
     """
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
-    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _round_bf16_into(x.reshape(-1), out.reshape(-1), np.empty(x.size, dtype=np.uint32))
+    return out
 
 
 def normal_bf16(rng: np.random.Generator, shape, std: float = 1.0,
-                chunk: int = 1 << 24) -> np.ndarray:
-    """N(0, std) draws as bf16 bit patterns (uint16), generated in chunks."""
+                chunk: int = 1 << 22) -> np.ndarray:
+    """N(0, std) draws as bf16 bit patterns (uint16).
+
+    float32 standard normals are drawn in order, scaled by ``std`` in float32
+    and rounded to bf16; the chunking only bounds memory (the stream is consumed
+    identically for any chunk size).
+    """
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint16)
+    buf = np.empty(min(chunk, max(n, 1)), dtype=np.float32)
+    tmp = np.empty(buf.size, dtype=np.uint32)
     s = np.float32(std)
     for i in range(0, n, chunk):
         j = min(n, i + chunk)
-        x = rng.standard_normal(j - i, dtype=np.float32)
+        x = buf[: j - i]
+        rng.standard_normal(out=x, dtype=np.float32)
         if std != 1.0:
-            x *= s
-        out[i:j] = f32_to_bf16_bits(x)
+            np.multiply(x, s, out=x)
+        _round_bf16_into(x, out[i:j], tmp[: j - i])
     return out.reshape(shape)
 
 
