@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tig_internal.h"
 
 #pragma clang fp contract(off)
@@ -40,6 +42,13 @@ constexpr int MAIN_LDS = 2 * STAGE_BYTES;
 constexpr int EPI_LDS = BM * EPI_LD * 4;
 constexpr int LDS_BYTES = MAIN_LDS > EPI_LDS ? MAIN_LDS : EPI_LDS;
 constexpr int GROUP_M = 8;                    // m-tiles that share each W tile in L2
+constexpr int STAGES = 4;                     // LDS ring of k-tiles: 3 in flight, 1 in use
+constexpr int RING_BYTES = STAGES * STAGE_BYTES;   // 128 KiB
+constexpr int EPI_ROWS = 64;                  // epilogue transposes 64 rows per pass
+constexpr int EPI_REGION = EPI_ROWS * BN * 4; // 32 KiB
+constexpr int P_LDS = RING_BYTES + EPI_REGION;     // 160 KiB: the whole LDS of a CU
+constexpr uint32_t OOB_DMA = 0x80000000u;     // row offset past any tile (stays past it + K*2)
+#define LDS_AS __attribute__((address_space(3)))
 constexpr uint32_t OOB = 0xFFFFFFF0u;         // offset past every buffer's range
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format
 constexpr float LOG2E = 1.44269504088896340736f;
@@ -216,34 +225,278 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 }
 
 // ---------------------------------------------------------------------------
+// Persistent leaf-tree pipeline.
+//
+// One workgroup per CU walks its tiles; the k-tiles of all its tiles form one
+// stream that a 4-deep LDS ring keeps 3 k-tiles ahead of the matrix cores.
+// Loads go straight from global memory to LDS (buffer_load ... lds), so no
+// VGPRs hold staged data, and the waits are explicit vmcnt counts plus a bare
+// s_barrier (no fence, which would drain the ring).
+// ---------------------------------------------------------------------------
+
+// s_waitcnt immediates (gfx9 layout: vmcnt[3:0] + vmcnt_hi[15:14], expcnt[6:4], lgkmcnt[11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+// Barrier without a memory fence; the asm memory clobber keeps LDS accesses on their side.
+__device__ __forceinline__ void bar() { asm volatile("s_barrier" ::: "memory"); }
+// LDS writes of this wave complete, then barrier.
+__device__ __forceinline__ void lds_sync() {
+  wait_lgkm0();
+  bar();
+}
+
+// The tiles of one workgroup.  Blocks are dealt to the 8 XCDs round-robin;
+// the blocks of XCD x own the logical tiles [x P, (x+1) P) and take them
+// round-robin, so the ~32 workgroups running on one XCD always work on 32
+// consecutive logical tiles; the logical order walks GROUP_M m-tiles down each
+// n-tile so those 32 share A and W tiles in the XCD's L2.
+struct TileSched {
+  int n_mt, n_nt, slots, first, end;
+  __device__ __forceinline__ void init(int n_mt_, int n_nt_) {
+    n_mt = n_mt_;
+    n_nt = n_nt_;
+    const int total = n_mt * n_nt;
+    const int per_xcd = (total + 7) >> 3;
+    slots = int(gridDim.x) >> 3;
+    const int x = blockIdx.x & 7;
+    first = x * per_xcd + int(blockIdx.x >> 3);
+    end = min((x + 1) * per_xcd, total);
+  }
+  __device__ __forceinline__ int count() const {
+    return first < end ? (end - first + slots - 1) / slots : 0;
+  }
+  __device__ __forceinline__ void coords(int i, int& mt, int& nt) const {
+    const int lam = first + i * slots;
+    const int per_group = GROUP_M * n_nt;
+    const int group = lam / per_group;
+    const int f = group * GROUP_M;
+    const int gm = min(n_mt - f, GROUP_M);
+    const int local = lam - group * per_group;
+    mt = f + local % gm;
+    nt = local / gm;
+  }
+};
+
+// Dense operands of one launch: A [M, K] (row stride lda), W [N, K] (ldw).
+struct DenseOperands {
+  const uint16_t* A; int64_t lda; int64_t M;
+  const uint16_t* W; int64_t ldw; int64_t N;
+};
+
+// Where this lane's 8 DMA loads of a k-tile come from.  Wave w fills the
+// 1 KiB segments 4w..4w+3 of the A half and of the W half of a stage; lane i
+// of a segment writes LDS bytes 16 i.. of it, i.e. row r = 8 g + i/8 of the
+// operand, physical chunk i%8.  Logical chunk c of row r lives at physical
+// chunk c ^ ((r >> 1) & 7): with 64 four-byte banks a 256-byte bank line holds
+// two rows, and the 16 lanes a 128-bit read serves at once (16 consecutive
+// rows, one logical chunk) then hit 16 different 16-byte slots.
+struct Loader {
+  __amdgpu_buffer_rsrc_t ra, rw;
+  uint32_t va[4], vw[4];
+};
+
+__device__ __forceinline__ void loader_setup(Loader& L, const DenseOperands& op, int mt, int nt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t m0 = int64_t(mt) * BM, n0 = int64_t(nt) * BN;
+  const int64_t rows_a = op.M - m0 < BM ? op.M - m0 : BM;
+  const int64_t rows_w = op.N - n0 < BN ? op.N - n0 : BN;
+  L.ra = make_rsrc(op.A + m0 * op.lda, uint32_t(rows_a * op.lda * 2));
+  L.rw = make_rsrc(op.W + n0 * op.ldw, uint32_t(rows_w * op.ldw * 2));
+  const int rs = lane >> 3;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (wave * 4 + j) * 8 + rs;
+    const uint32_t chunk = uint32_t(((lane & 7) ^ ((row >> 1) & 7)) << 4);
+    L.va[j] = row < rows_a ? uint32_t(row * op.lda * 2) + chunk : OOB_DMA;
+    L.vw[j] = row < rows_w ? uint32_t(row * op.ldw * 2) + chunk : OOB_DMA;
+  }
+}
+
+// The wave index as a scalar, so LDS destinations are SGPR arithmetic (M0).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+__device__ __forceinline__ void loader_issue(const Loader& L, char* stage, int kt) {
+  const int wave = wave_id();
+  const int so = kt * (BK * 2);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(L.ra, (LDS_AS void*)(stage + (wave * 4 + j) * 1024), 16,
+                                             L.va[j], so, 0, 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        L.rw, (LDS_AS void*)(stage + OPER_BYTES + (wave * 4 + j) * 1024), 16, L.vw[j], so, 0, 0);
+}
+
+// Fragment registers of one k-step: A rows (2 blocks of 32) and W rows (2 blocks).
+struct Frags { bf16x8 a0, a1, b0, b1; };
+
+struct FragAddr {
+  uint32_t a0, a1, w0, w1;
+  int fr, fk;
+  __device__ __forceinline__ void read(Frags& f, const char* st, int s) const {
+    const uint32_t ch = uint32_t(((2 * s + fk) ^ ((fr >> 1) & 7)) << 4);
+    f.a0 = *reinterpret_cast<const bf16x8*>(st + a0 + ch);
+    f.a1 = *reinterpret_cast<const bf16x8*>(st + a1 + ch);
+    f.b0 = *reinterpret_cast<const bf16x8*>(st + w0 + ch);
+    f.b1 = *reinterpret_cast<const bf16x8*>(st + w1 + ch);
+  }
+};
+
+// First k-step of a leaf: the accumulator input is the constant +0.
+__device__ __forceinline__ void mfma4_first(Acc& c, const Frags& f) {
+  const f32x16 z = {};
+  c.c[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a0, f.b0, z, 0, 0, 0);
+  c.c[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a0, f.b1, z, 0, 0, 0);
+  c.c[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a1, f.b0, z, 0, 0, 0);
+  c.c[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a1, f.b1, z, 0, 0, 0);
+}
+
+__device__ __forceinline__ void mfma4(Acc& c, const Frags& f) {
+  c.c[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a0, f.b0, c.c[0][0], 0, 0, 0);
+  c.c[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a0, f.b1, c.c[0][1], 0, 0, 0);
+  c.c[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a1, f.b0, c.c[1][0], 0, 0, 0);
+  c.c[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a1, f.b1, c.c[1][1], 0, 0, 0);
+}
+
+// Scheduling hint for one step: the 4 reads of the next step interleaved with
+// the 4 MFMAs of this one.
+__device__ __forceinline__ void sched_step() {
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+}
+
+// Wait until the DMA loads of stage `q` have landed, given how many later
+// stages (at most STAGES - 2) have been issued after it.
+__device__ __forceinline__ void wait_stage(int later) {
+  if (later >= STAGES - 2) wait_vmcnt<8 * (STAGES - 2)>();
+  else if (later == 1) wait_vmcnt<8>();
+  else wait_vmcnt<0>();
+}
+
+// Runs every tile of this workgroup: leaf-tree main loop, then epi(acc, mt, nt).
+//
+// The k-tiles of all tiles form one stream q = 0 .. total-1, computed as a
+// software pipeline: while the last 4 MFMAs of stage q run, the wave has
+// already waited for stage q+1, passed the barrier, issued the DMA of stage
+// q+STAGES into the buffer stage q-1 just freed, and read the step-0 fragments
+// of stage q+1.  At leaf ends the accumulator folds into the pending tree; at
+// tile ends the epilogue runs.
+template <int LG, class Epi>
+__device__ __forceinline__ void leaf_tree_persistent(const DenseOperands& op, int ktiles,
+                                                     const TileSched& ts, Epi& epi, char* smem) {
+  const int n_my = ts.count();
+  if (n_my == 0) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  FragAddr fa;
+  fa.fr = lane & 31;
+  fa.fk = lane >> 5;
+  fa.a0 = uint32_t((wm * 64 + fa.fr) * 128);
+  fa.a1 = fa.a0 + 32 * 128;
+  fa.w0 = uint32_t(OPER_BYTES + (wn * 64 + fa.fr) * 128);
+  fa.w1 = fa.w0 + 32 * 128;
+  constexpr int L = 1 << LG;
+  const int kpl = ktiles >> LG;
+  const int total = n_my * ktiles;
+
+  Loader ld;
+  int l_tile = 0, l_kt = 0;
+  {
+    int mt, nt;
+    ts.coords(0, mt, nt);
+    loader_setup(ld, op, mt, nt);
+  }
+  auto issue_next = [&](int stage) {
+    loader_issue(ld, smem + (stage % STAGES) * STAGE_BYTES, l_kt);
+    if (++l_kt == ktiles) {
+      l_kt = 0;
+      if (++l_tile < n_my) {
+        int mt, nt;
+        ts.coords(l_tile, mt, nt);
+        loader_setup(ld, op, mt, nt);
+      }
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p)
+    if (p < total) issue_next(p);
+
+  Frags f0, f1;
+  wait_stage(min(STAGES - 2, total - 1));
+  bar();
+  if (STAGES - 1 < total) issue_next(STAGES - 1);
+  fa.read(f0, smem, 0);
+
+  // One k-tile of the stream: steps 0..2 with the next step's fragments read
+  // under the MFMAs; then the hand-over to stage q+1 (wait, barrier, DMA of
+  // stage q+STAGES, step-0 fragments of q+1) before the last 4 MFMAs.
+  auto stage = [&](Acc& cur, int q, auto first) {
+    const char* st = smem + (q % STAGES) * STAGE_BYTES;
+    fa.read(f1, st, 1);
+    if constexpr (decltype(first)::value) mfma4_first(cur, f0);
+    else mfma4(cur, f0);
+    sched_step();
+    fa.read(f0, st, 2);
+    mfma4(cur, f1);
+    sched_step();
+    fa.read(f1, st, 3);
+    mfma4(cur, f0);
+    sched_step();
+    if (q + 1 < total) {
+      wait_stage(min(STAGES - 2, total - 2 - q));
+      bar();
+      if (q + STAGES < total) issue_next(q + STAGES);
+      fa.read(f0, smem + ((q + 1) % STAGES) * STAGE_BYTES, 0);
+    }
+    mfma4(cur, f1);
+  };
+
+  int q = 0;
+  for (int ti = 0; ti < n_my; ++ti) {
+    Acc pend[LG > 0 ? LG : 1];
+    Acc cur;
+#pragma unroll 1
+    for (int leaf = 0; leaf < L; ++leaf) {
+      stage(cur, q++, std::true_type{});
+      for (int j = 1; j < kpl; ++j) stage(cur, q++, std::false_type{});
+      tree_fold<0, LG>(pend, cur, leaf);
+    }
+    int mt, nt;
+    ts.coords(ti, mt, nt);
+    epi(cur, mt, nt, smem + RING_BYTES);
+  }
+}
+
+// Epilogue: store the tile (FP32, or bf16 by RNE).
+template <int EPI>
+struct StoreEpi {
+  void* C; int64_t ldc; int64_t M, N;
+  __device__ __forceinline__ void operator()(const Acc& acc, int mt, int nt, char*) const;
+};
+
+// Epilogue: per (row, 128-column vocabulary tile) max and sum of exp2, plus
+// the sampled token's logit.  The 128 x 128 tile is transposed through LDS in
+// two passes of 64 rows; in a pass, thread t owns row t/4, columns 32 (t%4)..+31.
+struct LogprobEpi {
+  float2* part; float* xid; const int64_t* ids; int64_t M, V; int n_vt;
+  __device__ __forceinline__ void operator()(const Acc& acc, int mt, int nt, char* region) const;
+};
+
+// ---------------------------------------------------------------------------
 // tree_gemm: C = leaf-tree(A W^T), FP32 or bf16 out.
 // ---------------------------------------------------------------------------
-template <int LG, int EPI>
-__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void tree_gemm_kernel(const uint16_t* __restrict__ A, int64_t lda,
-                      const uint16_t* __restrict__ W, int64_t ldw,
-                      void* __restrict__ C, int64_t ldc,
-                      int64_t M, int64_t N, int ktiles_per_leaf, int n_mt, int n_nt) {
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
-  int mt, nt;
-  if (!tile_of(n_mt, n_nt, mt, nt)) return;
+template <int EPI>
+__device__ __forceinline__ void StoreEpi<EPI>::operator()(const Acc& acc, int mt, int nt, char*) const {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = int64_t(mt) * BM, n0 = int64_t(nt) * BN;
-  const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
-  const int64_t rows_w = N - n0 < BN ? N - n0 : BN;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(A + m0 * lda, uint32_t(rows_a * lda * 2));
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + n0 * ldw, uint32_t(rows_w * ldw * 2));
-  const int tid = threadIdx.x;
-  uint32_t aoff[4], woff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    aoff[i] = r < rows_a ? uint32_t(r * lda * 2 + (tid & 7) * 16) : OOB;
-    woff[i] = r < rows_w ? uint32_t(r * ldw * 2 + (tid & 7) * 16) : OOB;
-  }
-  Acc acc;
-  leaf_tree_mainloop<LG>(acc, ra, aoff, rw, woff, ktiles_per_leaf, smem);
-
-  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -262,86 +515,98 @@ void tree_gemm_kernel(const uint16_t* __restrict__ A, int64_t lda,
     }
 }
 
+template <int LG, int EPI>
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void tree_gemm_kernel(DenseOperands op, void* __restrict__ C, int64_t ldc, int ktiles, int n_mt,
+                      int n_nt) {
+  __shared__ __attribute__((aligned(1024))) char smem[P_LDS];
+  TileSched ts;
+  ts.init(n_mt, n_nt);
+  StoreEpi<EPI> epi{C, ldc, op.M, op.N};
+  leaf_tree_persistent<LG>(op, ktiles, ts, epi, smem);
+}
+
 // ---------------------------------------------------------------------------
 // logprob, pass 1: per (row, 128-column vocabulary tile) the max m_t and
-// s_t = sum exp2((x - m_t) log2 e), plus the sampled token's logit.
+// s_t = sum exp2((x - m_t) log2 e) by the balanced adjacent-pair tree over the
+// 128 columns (padded columns add +0), plus the sampled token's logit.
 // ---------------------------------------------------------------------------
 
-// Balanced adjacent-pair tree over 64 values: (v0+v1), (v2+v3), ... level by level.
-__device__ __forceinline__ float pair_tree_64(float (&e)[64]) {
+// Balanced adjacent-pair tree over 32 values: (v0+v1), (v2+v3), ... level by level.
+__device__ __forceinline__ float pair_tree_32(float (&e)[32]) {
 #pragma unroll
-  for (int w = 1; w < 64; w *= 2)
+  for (int w = 1; w < 32; w *= 2)
 #pragma unroll
-    for (int j = 0; j < 64; j += 2 * w) e[j] = e[j] + e[j + w];
+    for (int j = 0; j < 32; j += 2 * w) e[j] = e[j] + e[j + w];
   return e[0];
+}
+
+// [64][128] floats, 16-byte chunk index XOR (row % 32): a row's quarter read by
+// 16 rows at once spreads over all banks.
+__device__ __forceinline__ int epi_index(int r, int c) {
+  return r * BN + (((c >> 2) ^ (r & 31)) << 2) + (c & 3);
+}
+
+__device__ __forceinline__ void LogprobEpi::operator()(const Acc& acc, int mt, int nt,
+                                                       char* region) const {
+  float* E = reinterpret_cast<float*>(region);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = int64_t(mt) * BM, n0 = int64_t(nt) * BN;
+  const int valid = int(V - n0 < BN ? V - n0 : BN) - 32 * (tid & 3);  // columns of this quarter
+  const int r = tid >> 2, h = tid & 3;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int64_t row = m0 + pass * EPI_ROWS + r;
+    // Loaded and consumed on every path, so no load is left pending past the tile.
+    const int64_t id = ids[row < M ? row : M - 1];
+    const int64_t c = id - n0 - 32 * h;
+    const bool mine = row < M && id >= 0 && id < V && c >= 0 && c < 32;
+    if (wm == pass) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            E[epi_index(i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3), acc_col(wn, j, lane))] =
+                acc.c[i][j][v];
+    }
+    lds_sync();
+    float x[32];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float4 t4 = *reinterpret_cast<const float4*>(E + r * BN + (((8 * h + k) ^ (r & 31)) << 2));
+      x[4 * k + 0] = t4.x; x[4 * k + 1] = t4.y; x[4 * k + 2] = t4.z; x[4 * k + 3] = t4.w;
+    }
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int c = 0; c < 32; ++c)
+      if (c < valid) mx = fmaxf(mx, x[c]);
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));     // tile max (exact, any order)
+#pragma unroll
+    for (int c = 0; c < 32; ++c)
+      x[c] = c < valid ? __builtin_amdgcn_exp2f((x[c] - mx) * LOG2E) : 0.0f;
+    float sq = pair_tree_32(x);
+    float o = __shfl_xor(sq, 1);
+    sq = (h & 1) ? o + sq : sq + o;          // (q0 + q1), (q2 + q3)
+    o = __shfl_xor(sq, 2);
+    sq = (h & 2) ? o + sq : sq + o;          // (q0 + q1) + (q2 + q3)
+    if (row < M && h == 0) part[row * n_vt + nt] = make_float2(mx, sq);
+    if (mine) xid[row] = E[epi_index(r, int(32 * h + c))];
+    lds_sync();
+  }
 }
 
 template <int LG>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void logprob_tile_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ W,
-                         const int64_t* __restrict__ ids, float2* __restrict__ part,
-                         float* __restrict__ xid, int64_t M, int64_t K, int64_t V,
-                         int ktiles_per_leaf, int n_mt, int n_nt) {
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
-  int mt, nt;
-  if (!tile_of(n_mt, n_nt, mt, nt)) return;
-  const int64_t m0 = int64_t(mt) * BM, n0 = int64_t(nt) * BN;
-  const int64_t rows_a = M - m0 < BM ? M - m0 : BM;
-  const int64_t rows_w = V - n0 < BN ? V - n0 : BN;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(H + m0 * K, uint32_t(rows_a * K * 2));
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(W + n0 * K, uint32_t(rows_w * K * 2));
-  const int tid = threadIdx.x;
-  uint32_t aoff[4], woff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    aoff[i] = r < rows_a ? uint32_t(r * K * 2 + (tid & 7) * 16) : OOB;
-    woff[i] = r < rows_w ? uint32_t(r * K * 2 + (tid & 7) * 16) : OOB;
-  }
-  Acc acc;
-  leaf_tree_mainloop<LG>(acc, ra, aoff, rw, woff, ktiles_per_leaf, smem);
-
-  // Transpose the 128 x 128 FP32 tile through LDS so that each thread owns
-  // half a row: thread t takes row t / 2, columns 64 (t % 2) .. + 63.
-  float* E = reinterpret_cast<float*>(smem);
-  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v)
-        E[acc_row(wm, i, v, lane) * EPI_LD + acc_col(wn, j, lane)] = acc.c[i][j][v];
-  __syncthreads();
-
-  const int r = tid >> 1, h = tid & 1;
-  const int64_t row = m0 + r;
-  const int valid = int(rows_w) - 64 * h;   // valid columns in this half (may be <= 0)
-  const float* src = E + r * EPI_LD + 64 * h;
-  float x[64];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const float4 t4 = *reinterpret_cast<const float4*>(src + 4 * q);
-    x[4 * q + 0] = t4.x; x[4 * q + 1] = t4.y; x[4 * q + 2] = t4.z; x[4 * q + 3] = t4.w;
-  }
-  float mx = -__builtin_inff();
-#pragma unroll
-  for (int c = 0; c < 64; ++c)
-    if (c < valid) mx = fmaxf(mx, x[c]);
-  mx = fmaxf(mx, __shfl_xor(mx, 1));   // tile max over both halves (exact)
-#pragma unroll
-  for (int c = 0; c < 64; ++c)
-    x[c] = c < valid ? __builtin_amdgcn_exp2f((x[c] - mx) * LOG2E) : 0.0f;
-  const float s_half = pair_tree_64(x);
-  const float s_other = __shfl_xor(s_half, 1);
-  const float s_tile = h == 0 ? s_half + s_other : s_other + s_half;   // top node: half 0 + half 1
-  if (row < M) {
-    const int n_vt = n_nt;
-    if (h == 0) part[row * n_vt + nt] = make_float2(mx, s_tile);
-    const int64_t id = ids[row];
-    const int64_t c = id - n0 - 64 * h;
-    if (id >= 0 && id < V && c >= 0 && c < 64) xid[row] = src[c];
-  }
+void logprob_tile_kernel(DenseOperands op, int ktiles, int n_mt, int n_nt, float2* __restrict__ part,
+                         float* __restrict__ xid, const int64_t* __restrict__ ids) {
+  __shared__ __attribute__((aligned(1024))) char smem[P_LDS];
+  TileSched ts;
+  ts.init(n_mt, n_nt);
+  LogprobEpi epi{part, xid, ids, op.M, op.N, n_nt};
+  leaf_tree_persistent<LG>(op, ktiles, ts, epi, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -537,31 +802,47 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* __restr
   out[t * N + n] = bad ? __builtin_nanf("") : acc;
 }
 
+// Persistent grid: one workgroup per CU (multiple of 8 for the XCD deal), or
+// one per tile when there are fewer tiles.  Only the schedule depends on it.
+int persistent_grid(int64_t n_tiles) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
+  const int64_t full = int64_t(cus[dev] / 8) * 8 > 0 ? int64_t(cus[dev] / 8) * 8 : 8;
+  const int64_t want = ((n_tiles + 7) / 8) * 8;
+  return int(want < full ? want : full);
+}
+
 template <int LG>
 hipError_t launch_tree_gemm_lg(const TreeGemmLaunch& p, hipStream_t s) {
   const int n_mt = int(cdiv(p.M, BM)), n_nt = int(cdiv(p.N, BN));
-  const int kpl = int((p.K >> LG) / BK);
-  const dim3 grid(grid_blocks(int64_t(n_mt) * n_nt)), block(NTHREADS);
+  const DenseOperands op{static_cast<const uint16_t*>(p.A), p.lda, p.M,
+                         static_cast<const uint16_t*>(p.W), p.ldw, p.N};
+  const int ktiles = int(p.K / BK);
+  const dim3 grid(persistent_grid(int64_t(n_mt) * n_nt)), block(NTHREADS);
   if (p.epi == kEpiF32)
-    hipLaunchKernelGGL((tree_gemm_kernel<LG, kEpiF32>), grid, block, 0, s,
-                       static_cast<const uint16_t*>(p.A), p.lda, static_cast<const uint16_t*>(p.W),
-                       p.ldw, p.C, p.ldc, p.M, p.N, kpl, n_mt, n_nt);
+    hipLaunchKernelGGL((tree_gemm_kernel<LG, kEpiF32>), grid, block, 0, s, op, p.C, p.ldc, ktiles,
+                       n_mt, n_nt);
   else
-    hipLaunchKernelGGL((tree_gemm_kernel<LG, kEpiBF16>), grid, block, 0, s,
-                       static_cast<const uint16_t*>(p.A), p.lda, static_cast<const uint16_t*>(p.W),
-                       p.ldw, p.C, p.ldc, p.M, p.N, kpl, n_mt, n_nt);
+    hipLaunchKernelGGL((tree_gemm_kernel<LG, kEpiBF16>), grid, block, 0, s, op, p.C, p.ldc, ktiles,
+                       n_mt, n_nt);
   return hipGetLastError();
 }
 
 template <int LG>
 hipError_t launch_logprob_lg(const LogprobLaunch& p, hipStream_t s) {
   const int n_mt = int(cdiv(p.M, BM)), n_vt = int(cdiv(p.V, BN));
-  const int kpl = int((p.K >> LG) / BK);
+  const DenseOperands op{static_cast<const uint16_t*>(p.H), p.K, p.M,
+                         static_cast<const uint16_t*>(p.W), p.K, p.V};
   float2* part = static_cast<float2*>(p.partials);
-  hipLaunchKernelGGL((logprob_tile_kernel<LG>), dim3(grid_blocks(int64_t(n_mt) * n_vt)),
-                     dim3(NTHREADS), 0, s, static_cast<const uint16_t*>(p.H),
-                     static_cast<const uint16_t*>(p.W), p.ids, part, p.xid, p.M, p.K, p.V, kpl,
-                     n_mt, n_vt);
+  hipLaunchKernelGGL((logprob_tile_kernel<LG>), dim3(persistent_grid(int64_t(n_mt) * n_vt)),
+                     dim3(NTHREADS), 0, s, op, int(p.K / BK), n_mt, n_vt, part, p.xid, p.ids);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   int q = 0;
