@@ -41,6 +41,38 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_source_digest() -> str:
+    """SHA-256 of the kernel source, to tell whether stored counters still apply."""
+    import hashlib
+    path = os.path.join(ROOT, "invariant_gemm_token_amd", "csrc", "tig_kernels.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def measured_traffic(name: str):
+    """HBM-side bytes per launch of the fused kernel, from the committed counter summary.
+
+    profiles/<name>_traffic.md holds `traffic_bytes_per_launch:` (FETCH_SIZE +
+    WRITE_SIZE of one launch, each scaled by what the same counter reads for a
+    1 GiB copy) and the `kernel_source_sha256:` it was measured on; if the
+    kernel source has changed since, the figure no longer applies and None is
+    returned.
+    """
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.split(":", 1)[0].strip() in ("traffic_bytes_per_launch", "kernel_source_sha256"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -49,6 +81,10 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--phase", choices=("all", "prefill", "decode"), default="all",
+                    help="time only one configuration (for per-kernel profiles)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -85,28 +121,38 @@ def main():
     lse = torch.empty(M, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
+    if args.copy_probe:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE calibrate the counters.
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     def step():
         tig.tig_logprob_gather(Hd, Wd, idd, lp, lse, L, ws)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    ev[0].record(stream)
-    for i in range(args.steps):
-        step()
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    per_call = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
-    total_ms = ev[0].elapsed_time(ev[-1])
-    ms_step = total_ms / args.steps
-    tok_s = M * args.steps / (total_ms / 1e3)
+    tok_s = ms_step = tflops = None
     flops = 2.0 * M * K * V
-    avg_call_s = float(np.mean(per_call)) / 1e3
-    tflops = flops / avg_call_s / 1e12
-    log(f"prefill: {ms_step:.3f} ms/step, {tok_s:.4g} tok/s, {tflops:.1f} TFLOP/s "
-        f"(min {min(per_call):.3f} ms, max {max(per_call):.3f} ms)")
+    if args.phase in ("all", "prefill"):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(args.steps):
+            step()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per_call = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
+        total_ms = ev[0].elapsed_time(ev[-1])
+        ms_step = total_ms / args.steps
+        tok_s = M * args.steps / (total_ms / 1e3)
+        avg_call_s = float(np.mean(per_call)) / 1e3
+        tflops = flops / avg_call_s / 1e12
+        log(f"prefill: {ms_step:.3f} ms/step, {tok_s:.4g} tok/s, {tflops:.1f} TFLOP/s "
+            f"(min {min(per_call):.3f} ms, max {max(per_call):.3f} ms)")
 
     # decode: one step of 128 sequences against the same weights
     Md = cfg.n_seq
@@ -117,19 +163,24 @@ def main():
     def dstep():
         tig.tig_logprob_gather(Hdec, Wd, iddec, lpd, None, L, wsd)
 
-    for _ in range(args.warmup):
-        dstep()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.decode_steps):
-        dstep()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    dec_ms = e0.elapsed_time(e1) / args.decode_steps
-    dec_bytes = 2.0 * K * V + 2.0 * Md * K + 8.0 * Md + 4.0 * Md
-    dec_gbs = dec_bytes / (dec_ms / 1e3) / 1e9
-    log(f"decode M={Md}: {dec_ms * 1e3:.1f} us/step, {dec_gbs:.0f} GB/s")
+    decode = None
+    if args.phase in ("all", "decode"):
+        for _ in range(args.warmup):
+            dstep()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.decode_steps):
+            dstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dec_ms = e0.elapsed_time(e1) / args.decode_steps
+        dec_bytes = 2.0 * K * V + 2.0 * Md * K + 8.0 * Md + 4.0 * Md
+        dec_gbs = dec_bytes / (dec_ms / 1e3) / 1e9
+        log(f"decode M={Md}: {dec_ms * 1e3:.1f} us/step, {dec_gbs:.0f} GB/s")
+        decode = {"tokens": Md, "us_per_step": dec_ms * 1e3, "tokens_per_s": Md / (dec_ms / 1e3),
+                  "achieved_GBs": dec_gbs, "peak_GBs": PEAK_HBM_GBS, "hbm_frac": dec_gbs / PEAK_HBM_GBS,
+                  "algorithmic_bytes": dec_bytes}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -156,12 +207,13 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "lmhead_logprob_prefill", "hidden": K, "vocab": V, "tokens": M,
                    "leaves": L, "global_batch": M, "parallelism": "none"},
-        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tflops / PEAK_BF16_TFLOPS, "traffic": None},
-        "tree_gemm": {"tflops": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
-                      "shape": f"M={M} K={K} N={V} leaves={L}"},
-        "decode": {"tokens": Md, "us_per_step": dec_ms * 1e3, "tokens_per_s": Md / (dec_ms / 1e3),
-                   "achieved_GBs": dec_gbs, "peak_GBs": PEAK_HBM_GBS, "hbm_frac": dec_gbs / PEAK_HBM_GBS},
+        "roofline": None if tflops is None else {
+            "bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic("lmhead_prefill")},
+        "tree_gemm": None if tflops is None else {
+            "tflops": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
+            "shape": f"M={M} K={K} N={V} leaves={L}"},
+        "decode": decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
