@@ -20,7 +20,7 @@ Sources (the three web pages this method is described on):
   independent of layout) and section 4.5 (expert outputs summed in FP32 in a
   fixed order on the token's owner).
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
 
 * R1 tree shape: a balanced tree of adjacent pairs, level by level, over a
   power-of-two leaf count: for 8 leaves ``((P0+P1)+(P2+P3))+((P4+P5)+(P6+P7))``.

@@ -57,7 +57,7 @@ def diff_stats(a, b) -> dict:
 
 
 def assert_gemm_close(got: np.ndarray, ref: np.ndarray, rel: float = 2e-3, what: str = "gemm"):
-    """Elementwise |got - ref| <= rel * max(|ref|, rms(ref)) (spec GEMM bar)."""
+    """Elementwise |got - ref| <= rel * max(|ref|, rms(ref)) (the GEMM parity bar)."""
     got = np.asarray(got, dtype=np.float64)
     rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
     bound = rel * np.maximum(np.abs(ref), rms)

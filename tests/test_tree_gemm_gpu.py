@@ -8,7 +8,7 @@ Pins on the GPU path:
     the GPU must equal the float32 tree closed forms / emulator bit for bit
     (leaf boundaries, tree shape, FP32 leaves) [IsoExec, Parallelism-invariant
     kernels];
-  * random bf16 data within the north-star bound 2e-3 relative (floor: rms);
+  * random bf16 data within 2e-3 relative of the oracle (floor: rms);
   * diff = 0 across M, row permutations, single-row calls and repeated runs
     [BitRL, section 2; REINFORCE Zero, section 6: 4096 vs 4097 rows].
 """
