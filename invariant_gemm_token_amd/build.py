@@ -25,6 +25,9 @@ ARCH = "gfx950"
 DEVICE_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Matrix-core accumulators in VGPRs: the leaf-tree adds then need no
+    # AGPR<->VGPR copies, which frees ~80 registers per lane.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 HOST_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-Wall",
