@@ -159,7 +159,7 @@ tig_status tig_plan_describe(int64_t K, int32_t leaves, tig_plan* out) {
   out->version = tig::kPolicyVersion;
   out->leaves = leaves;
   out->leaf_len = int32_t(K / leaves);
-  out->block_m = tig::kBlockM;
+  out->block_m = tig::block_m_for_log2(log2i(leaves));
   out->block_n = tig::kBlockN;
   out->block_k = tig::kBlockK;
   out->mfma_m = tig::kMfmaM;
@@ -197,9 +197,10 @@ tig_status tig_tree_gemm(const void* A, int64_t lda, const void* W, int64_t ldw,
     return fail(TIG_ERR_UNSUPPORTED, "A and W must be 16-byte aligned with row strides a multiple of 8");
   if (!aligned(C, out_dtype == TIG_OUT_F32 ? 4 : 2))
     return fail(TIG_ERR_INVALID_ARG, "C is misaligned for its dtype");
-  if ((s = check_span("A tile", tig::kBlockM, lda)) != TIG_OK) return s;
+  const int bm = tig::block_m_for(M, log2i(leaves));
+  if ((s = check_span("A tile", bm, lda)) != TIG_OK) return s;
   if ((s = check_span("W tile", tig::kBlockN, ldw)) != TIG_OK) return s;
-  if (tig::cdiv(M, tig::kBlockM) * tig::cdiv(N, tig::kBlockN) >= (int64_t(1) << 31) - 8)
+  if (tig::cdiv(M, bm) * tig::cdiv(N, tig::kBlockN) >= (int64_t(1) << 31) - 8)
     return fail(TIG_ERR_UNSUPPORTED, "too many output tiles");
   tig::TreeGemmLaunch p{A, lda, W, ldw, C, ldc,
                         out_dtype == TIG_OUT_F32 ? tig::kEpiF32 : tig::kEpiBF16,
@@ -219,7 +220,7 @@ tig_status tig_logprob_workspace_bytes(int64_t M, int64_t K, int64_t n_vocab, in
   if (tig::cdiv(n_vocab, tig::kBlockN) > tig::kMaxVocabTiles)
     return fail(TIG_ERR_UNSUPPORTED, "n_vocab > %d not implemented",
                 tig::kMaxVocabTiles * tig::kBlockN);
-  *bytes = tig::logprob_ws_bytes(M, n_vocab);
+  *bytes = tig::logprob_ws_bytes(M, n_vocab, leaves);
   return ok();
 }
 
@@ -241,8 +242,9 @@ tig_status tig_logprob_gather(const void* H, const void* W, const int64_t* ids, 
     return fail(TIG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : size_t(0));
   if (!aligned(workspace, 256)) return fail(TIG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if ((s = check_span("H tile", tig::kBlockM, K)) != TIG_OK) return s;
-  if (tig::cdiv(M, tig::kBlockM) * tig::cdiv(n_vocab, tig::kBlockN) >= (int64_t(1) << 31) - 8)
+  const int bm = tig::block_m_for(M, log2i(leaves));
+  if ((s = check_span("H tile", bm, K)) != TIG_OK) return s;
+  if (tig::cdiv(M, bm) * tig::cdiv(n_vocab, tig::kBlockN) >= (int64_t(1) << 31) - 8)
     return fail(TIG_ERR_UNSUPPORTED, "too many output tiles");
   char* ws = static_cast<char*>(workspace);
   tig::LogprobLaunch p{H, W, ids, logprob_out, lse_out, M, K, n_vocab, log2i(leaves), ws,

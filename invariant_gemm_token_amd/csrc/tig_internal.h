@@ -11,7 +11,18 @@ namespace tig {
 
 // Workgroup tile and k staging: fixed for every (K, leaves) this library
 // accepts, never chosen from M or N.
-constexpr int kBlockM = 128;
+constexpr int kBlockM = 128;   // MoE expert tiles; the dense kernels' smaller tile
+// Tallest tile of the dense kernels: the leaf tree keeps log2(leaves) + 1
+// accumulators per output element in registers, so up to 8 leaves leave room
+// for 192 rows, 16 leaves for 128.
+constexpr int block_m_for_log2(int leaves_log2) { return leaves_log2 <= 3 ? 192 : 128; }
+// Rows per tile used for M rows: the tall tile where it needs fewer tiles
+// (fewer passes over W), else 128.  Only the schedule depends on it, never a
+// value: every output element is computed the same way in either tile.
+inline int block_m_for(int64_t M, int leaves_log2) {
+  if (block_m_for_log2(leaves_log2) == 192 && (M + 191) / 192 < (M + 127) / 128) return 192;
+  return 128;
+}
 constexpr int kBlockN = 128;   // also the vocabulary tile of the log-softmax
 constexpr int kBlockK = 64;
 constexpr int kMfmaM = 32, kMfmaN = 32, kMfmaK = 16;
@@ -37,7 +48,7 @@ struct LogprobLaunch {
   int64_t M, K, V;
   int leaves_log2;
   void* partials;   // float2 [M][n_vtiles]
-  float* xid;       // float [M]
+  float* xleaf;     // float [M][leaves]
 };
 
 struct MoeLaunch {
@@ -58,8 +69,9 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t logprob_partials_bytes(int64_t M, int64_t V) {
   return align256(size_t(M) * size_t(cdiv(V, kBlockN)) * 8);
 }
-inline size_t logprob_ws_bytes(int64_t M, int64_t V) {
-  return logprob_partials_bytes(M, V) + align256(size_t(M) * 4);
+// partials float2 [M][vocabulary tiles], then the picked logit's leaf values float [M][leaves]
+inline size_t logprob_ws_bytes(int64_t M, int64_t V, int leaves) {
+  return logprob_partials_bytes(M, V) + align256(size_t(M) * size_t(leaves) * 4);
 }
 inline size_t moe_counts_bytes(int n_experts) { return align256(size_t(n_experts) * 4); }
 inline size_t moe_rows_bytes(int64_t T, int topk, int n_experts) {

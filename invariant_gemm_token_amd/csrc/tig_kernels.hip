@@ -33,7 +33,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-constexpr int BM = kBlockM, BN = kBlockN, BK = kBlockK;
+constexpr int BM = kBlockM, BN = kBlockN, BK = kBlockK;   // BM: the MoE kernel's tile
 constexpr int NTHREADS = 256;                 // 4 waves of 64, 2 x 2 over the tile
 constexpr int OPER_BYTES = BM * BK * 2;       // one operand's k-tile: 16 KiB
 constexpr int STAGE_BYTES = 2 * OPER_BYTES;   // A and W
@@ -42,23 +42,22 @@ constexpr int MAIN_LDS = 2 * STAGE_BYTES;
 constexpr int EPI_LDS = BM * EPI_LD * 4;
 constexpr int LDS_BYTES = MAIN_LDS > EPI_LDS ? MAIN_LDS : EPI_LDS;
 constexpr int GROUP_M = 8;                    // m-tiles that share each W tile in L2
-constexpr int STAGES = 4;                     // LDS ring of k-tiles: 3 in flight, 1 in use
-constexpr int RING_BYTES = STAGES * STAGE_BYTES;   // 128 KiB
-constexpr int EPI_ROWS = 64;                  // epilogue transposes 64 rows per pass
-constexpr int EPI_REGION = EPI_ROWS * BN * 4; // 32 KiB
-constexpr int P_LDS = RING_BYTES + EPI_REGION;     // 160 KiB: the whole LDS of a CU
-constexpr uint32_t OOB_DMA = 0x80000000u;     // row offset past any tile (stays past it + K*2)
+constexpr int kLdsBytes = 160 * 1024;         // LDS of one CU: the persistent kernels' ring
 #define LDS_AS __attribute__((address_space(3)))
 constexpr uint32_t OOB = 0xFFFFFFF0u;         // offset past every buffer's range
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format
 constexpr float LOG2E = 1.44269504088896340736f;
 constexpr float LN2 = 0.69314718055994530942f;
 
-struct Acc { f32x16 c[2][2]; };   // one wave's 64 x 64 FP32 tile
+// One wave's (32 MI) x 64 FP32 tile: MI x 2 blocks of 32 x 32.
+template <int MI>
+struct AccT { f32x16 c[MI][2]; };
+using Acc = AccT<2>;
 
-__device__ __forceinline__ void acc_zero(Acc& a) {
+template <int MI>
+__device__ __forceinline__ void acc_zero(AccT<MI>& a) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -66,9 +65,10 @@ __device__ __forceinline__ void acc_zero(Acc& a) {
 }
 
 // right <- left + right, elementwise FP32 (one node of the leaf tree).
-__device__ __forceinline__ void acc_add_left(const Acc& left, Acc& right) {
+template <int MI>
+__device__ __forceinline__ void acc_add_left(const AccT<MI>& left, AccT<MI>& right) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -90,8 +90,8 @@ __device__ __forceinline__ i32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
 // its right sibling.  Walking up while `leaf` has a 1 bit combines
 // left + right; the first 0 bit parks the subtree.  After the last leaf (all
 // bits 1) `cur` is the root: ((P0+P1)+(P2+P3))+... for every leaf count.
-template <int LEV, int LG>
-__device__ __forceinline__ void tree_fold(Acc (&pend)[LG > 0 ? LG : 1], Acc& cur, int leaf) {
+template <int LEV, int LG, class A>
+__device__ __forceinline__ void tree_fold(A (&pend)[LG > 0 ? LG : 1], A& cur, int leaf) {
   if constexpr (LEV < LG) {
     if (((leaf >> LEV) & 1) == 0) {
       pend[LEV] = cur;
@@ -212,8 +212,10 @@ __device__ __forceinline__ void leaf_tree_mainloop(Acc& root, __amdgpu_buffer_rs
 // Output position of accumulator element (block i, j; register v) of a lane:
 // the 32 x 32 result puts column (lane & 31) in the lane and rows
 // 8 (v / 4) + 4 (lane / 32) + (v % 4) in the registers.
+// A wave's rows start at 32 MI wm.
+template <int MI = 2>
 __device__ __forceinline__ int acc_row(int wm, int i, int v, int lane) {
-  return wm * 64 + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+  return wm * (32 * MI) + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
 }
 __device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * 64 + j * 32 + (lane & 31); }
 
@@ -228,10 +230,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 // Persistent leaf-tree pipeline.
 //
 // One workgroup per CU walks its tiles; the k-tiles of all its tiles form one
-// stream that a 4-deep LDS ring keeps 3 k-tiles ahead of the matrix cores.
-// Loads go straight from global memory to LDS (buffer_load ... lds), so no
-// VGPRs hold staged data, and the waits are explicit vmcnt counts plus a bare
-// s_barrier (no fence, which would drain the ring).
+// stream that an LDS ring (the whole 160 KiB) keeps several k-tiles ahead of
+// the matrix cores.  Loads go straight from global memory to LDS
+// (buffer_load ... lds), so no VGPRs hold staged data, and the waits are
+// explicit vmcnt counts plus a bare s_barrier (no fence, which would drain
+// the ring).
+//
+// The tile is (64 MI) x 128 with 4 waves in 2 x 2, each (32 MI) x 64.  The
+// leaf tree keeps log2(L) + 1 accumulators of the wave tile live, which is
+// what bounds the tile: MI = 3 (192 x 128, 4 x 96 accumulator registers per
+// lane at 8 leaves) up to 8 leaves, MI = 2 (128 x 128) at 16 leaves.  Every
+// byte staged through L2 then feeds 77 instead of 64 flops.
 // ---------------------------------------------------------------------------
 
 // s_waitcnt immediates (gfx9 layout: vmcnt[3:0] + vmcnt_hi[15:14], expcnt[6:4], lgkmcnt[11:8]).
@@ -239,6 +248,12 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt out of range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// vmcnt <= N and lgkmcnt == 0 (this wave's LDS reads have returned).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 // Barrier without a memory fence; the asm memory clobber keeps LDS accesses on their side.
@@ -249,35 +264,73 @@ __device__ __forceinline__ void lds_sync() {
   bar();
 }
 
-// The tiles of one workgroup.  Blocks are dealt to the 8 XCDs round-robin;
-// the blocks of XCD x own the logical tiles [x P, (x+1) P) and take them
-// round-robin, so the ~32 workgroups running on one XCD always work on 32
-// consecutive logical tiles; the logical order walks GROUP_M m-tiles down each
-// n-tile so those 32 share A and W tiles in the XCD's L2.
+// threadIdx.x through an opaque move: address arithmetic derived from it is
+// redone where it is used instead of being hoisted out of the tile loop, where
+// it would hold registers through the whole main loop.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// Geometry of the persistent kernels for MI 32-row blocks per wave.
+template <int MI>
+struct Geo {
+  static constexpr int BM = 64 * MI;                    // tile rows
+  static constexpr int A_BYTES = BM * BK * 2;           // A k-tile
+  static constexpr int STAGE = A_BYTES + BN * BK * 2;   // A and W k-tiles
+  static constexpr int STAGES = kLdsBytes / STAGE;      // 5 (MI = 2) or 4 (MI = 3)
+  static constexpr int A_SEG = 2 * MI;                  // 1 KiB DMA segments of A per wave
+  static constexpr int VM_PER_STAGE = A_SEG + 4;        // DMA instructions per wave per k-tile
+  static_assert(STAGES >= 3, "ring too shallow");
+  static_assert(VM_PER_STAGE * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(64 * BN * 4 <= STAGE, "epilogue pass must fit one ring buffer");
+};
+
+
+// The tiles of one workgroup.  Blocks are dealt to the 8 XCDs round-robin
+// (block b runs on XCD b % 8).  When there are enough n-tiles, XCD x owns the
+// n-tiles [x N/8, (x+1) N/8) for every m: each W tile then comes from HBM
+// once and its re-reads, like all of A, from the memory-side cache.  Inside
+// an XCD the logical order walks GROUP_N n-tiles across each m-tile, so the
+// ~32 workgroups running there at once (consecutive logical tiles, dealt
+// round-robin) share 4 A tiles and 8 W tiles in its L2.  With few n-tiles
+// the XCDs split the logical order of the whole grid instead.
+constexpr int GROUP_N = 8;
+
 struct TileSched {
-  int n_mt, n_nt, slots, first, end;
+  int n_mt, n_nt, slots, first, end, nb, nn;
   __device__ __forceinline__ void init(int n_mt_, int n_nt_) {
     n_mt = n_mt_;
     n_nt = n_nt_;
-    const int total = n_mt * n_nt;
-    const int per_xcd = (total + 7) >> 3;
     slots = int(gridDim.x) >> 3;
     const int x = blockIdx.x & 7;
-    first = x * per_xcd + int(blockIdx.x >> 3);
-    end = min((x + 1) * per_xcd, total);
+    if (n_nt >= 4 * GROUP_N) {
+      nb = int(int64_t(n_nt) * x / 8);
+      nn = int(int64_t(n_nt) * (x + 1) / 8) - nb;
+      first = int(blockIdx.x >> 3);
+      end = nn * n_mt;
+    } else {
+      const int total = n_mt * n_nt;
+      const int per_xcd = (total + 7) >> 3;
+      nb = 0;
+      nn = n_nt;
+      first = x * per_xcd + int(blockIdx.x >> 3);
+      end = min((x + 1) * per_xcd, total);
+    }
   }
   __device__ __forceinline__ int count() const {
     return first < end ? (end - first + slots - 1) / slots : 0;
   }
   __device__ __forceinline__ void coords(int i, int& mt, int& nt) const {
     const int lam = first + i * slots;
-    const int per_group = GROUP_M * n_nt;
+    const int per_group = GROUP_N * n_mt;
     const int group = lam / per_group;
-    const int f = group * GROUP_M;
-    const int gm = min(n_mt - f, GROUP_M);
+    const int f = group * GROUP_N;
+    const int gn = min(nn - f, GROUP_N);
     const int local = lam - group * per_group;
-    mt = f + local % gm;
-    nt = local / gm;
+    nt = nb + f + local % gn;
+    mt = local / gn;
   }
 };
 
@@ -287,225 +340,286 @@ struct DenseOperands {
   const uint16_t* W; int64_t ldw; int64_t N;
 };
 
-// Where this lane's 8 DMA loads of a k-tile come from.  Wave w fills the
-// 1 KiB segments 4w..4w+3 of the A half and of the W half of a stage; lane i
-// of a segment writes LDS bytes 16 i.. of it, i.e. row r = 8 g + i/8 of the
-// operand, physical chunk i%8.  Logical chunk c of row r lives at physical
-// chunk c ^ ((r >> 1) & 7): with 64 four-byte banks a 256-byte bank line holds
-// two rows, and the 16 lanes a 128-bit read serves at once (16 consecutive
-// rows, one logical chunk) then hit 16 different 16-byte slots.
+// Where this lane's DMA loads of a k-tile come from.  Wave w fills the 1 KiB
+// segments g = A_SEG w .. A_SEG (w+1) - 1 of the A part and 4w .. 4w+3 of the
+// W part of a stage; lane i of segment g writes LDS bytes 16 i.. of it, i.e.
+// row r = 8 g + i/8 of the operand, physical chunk i%8.  Logical chunk c of
+// row r lives at physical chunk c ^ ((r >> 1) & 7): with 64 four-byte banks a
+// 256-byte bank line holds two rows, and the 16 lanes a 128-bit read serves at
+// once (16 consecutive rows, one logical chunk) then hit 16 different
+// 16-byte slots.  Since (r >> 1) & 7 = 4 (g & 1) + (i / 16), the lane's byte
+// offset is off[g & 1] + 16 g ld: two VGPRs per operand and a scalar stride.
+// Rows past the tile's last row have offsets past the resource's size and
+// read as zero.
+template <int MI>
 struct Loader {
+  using G = Geo<MI>;
   __amdgpu_buffer_rsrc_t ra, rw;
-  uint32_t va[4], vw[4];
+  uint32_t oa[2], ow[2];      // lane offsets for even / odd segments
+  uint32_t sa, sw;            // 16 * leading dimension in bytes / 2 (one segment of rows)
+
+  __device__ __forceinline__ void setup(const DenseOperands& op, int mt, int nt) {
+    const int lane = threadIdx.x & 63;
+    const int64_t m0 = int64_t(mt) * G::BM, n0 = int64_t(nt) * BN;
+    const int64_t rows_a = op.M - m0 < G::BM ? op.M - m0 : G::BM;
+    const int64_t rows_w = op.N - n0 < BN ? op.N - n0 : BN;
+    ra = make_rsrc(op.A + m0 * op.lda, uint32_t(rows_a * op.lda * 2));
+    rw = make_rsrc(op.W + n0 * op.ldw, uint32_t(rows_w * op.ldw * 2));
+    const int rs = lane >> 3;
+    const uint32_t c0 = uint32_t(((lane & 7) ^ (rs >> 1)) << 4), c1 = c0 ^ 64u;
+    oa[0] = uint32_t(rs * op.lda * 2) + c0;
+    oa[1] = uint32_t(rs * op.lda * 2) + c1;
+    ow[0] = uint32_t(rs * op.ldw * 2) + c0;
+    ow[1] = uint32_t(rs * op.ldw * 2) + c1;
+    sa = uint32_t(op.lda * 16);
+    sw = uint32_t(op.ldw * 16);
+  }
+
+  // Part P of the DMA of k-tile kt of the current tile into the ring buffer
+  // `stage`: 0 and 1 = the two halves of this wave's A segments, 2 = its W
+  // segments (so the issue can be spread between MFMA steps).
+  template <int P>
+  __device__ __forceinline__ void issue(char* stage, int kt) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar: M0 arithmetic
+    const int so = kt * (BK * 2);
+    if constexpr (P < 2) {
+      constexpr int H = G::A_SEG / 2;
+#pragma unroll
+      for (int j = P * H; j < (P + 1) * H; ++j) {
+        const int g = wave * G::A_SEG + j;   // A_SEG is even: g & 1 == j & 1
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LDS_AS void*)(stage + g * 1024), 16,
+                                                 oa[j & 1] + uint32_t(g) * sa, so, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int g = wave * 4 + j;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (LDS_AS void*)(stage + G::A_BYTES + g * 1024),
+                                                 16, ow[j & 1] + uint32_t(g) * sw, so, 0, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void issue_all(char* stage, int kt) const {
+    issue<0>(stage, kt);
+    issue<1>(stage, kt);
+    issue<2>(stage, kt);
+  }
 };
 
-__device__ __forceinline__ void loader_setup(Loader& L, const DenseOperands& op, int mt, int nt) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t m0 = int64_t(mt) * BM, n0 = int64_t(nt) * BN;
-  const int64_t rows_a = op.M - m0 < BM ? op.M - m0 : BM;
-  const int64_t rows_w = op.N - n0 < BN ? op.N - n0 : BN;
-  L.ra = make_rsrc(op.A + m0 * op.lda, uint32_t(rows_a * op.lda * 2));
-  L.rw = make_rsrc(op.W + n0 * op.ldw, uint32_t(rows_w * op.ldw * 2));
-  const int rs = lane >> 3;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = (wave * 4 + j) * 8 + rs;
-    const uint32_t chunk = uint32_t(((lane & 7) ^ ((row >> 1) & 7)) << 4);
-    L.va[j] = row < rows_a ? uint32_t(row * op.lda * 2) + chunk : OOB_DMA;
-    L.vw[j] = row < rows_w ? uint32_t(row * op.ldw * 2) + chunk : OOB_DMA;
-  }
-}
+// Fragment registers of one k-step: A rows (MI blocks of 32) and W rows (2 blocks).
+template <int MI>
+struct Frags { bf16x8 a[MI], b0, b1; };
 
-// The wave index as a scalar, so LDS destinations are SGPR arithmetic (M0).
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-
-__device__ __forceinline__ void loader_issue(const Loader& L, char* stage, int kt) {
-  const int wave = wave_id();
-  const int so = kt * (BK * 2);
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(L.ra, (LDS_AS void*)(stage + (wave * 4 + j) * 1024), 16,
-                                             L.va[j], so, 0, 0);
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        L.rw, (LDS_AS void*)(stage + OPER_BYTES + (wave * 4 + j) * 1024), 16, L.vw[j], so, 0, 0);
-}
-
-// Fragment registers of one k-step: A rows (2 blocks of 32) and W rows (2 blocks).
-struct Frags { bf16x8 a0, a1, b0, b1; };
-
+template <int MI>
 struct FragAddr {
-  uint32_t a0, a1, w0, w1;
+  uint32_t a0, w0, w1;
   int fr, fk;
-  __device__ __forceinline__ void read(Frags& f, const char* st, int s) const {
+  __device__ __forceinline__ void read(Frags<MI>& f, const char* st, int s) const {
     const uint32_t ch = uint32_t(((2 * s + fk) ^ ((fr >> 1) & 7)) << 4);
-    f.a0 = *reinterpret_cast<const bf16x8*>(st + a0 + ch);
-    f.a1 = *reinterpret_cast<const bf16x8*>(st + a1 + ch);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(st + a0 + i * 32 * 128 + ch);
     f.b0 = *reinterpret_cast<const bf16x8*>(st + w0 + ch);
     f.b1 = *reinterpret_cast<const bf16x8*>(st + w1 + ch);
   }
 };
 
-// First k-step of a leaf: the accumulator input is the constant +0.
-__device__ __forceinline__ void mfma4_first(Acc& c, const Frags& f) {
+// One k-step of 16 on the wave tile.  The first k-step of a leaf takes the
+// constant +0 as accumulator input.
+template <bool FIRST, int MI>
+__device__ __forceinline__ void mfma_step(AccT<MI>& c, const Frags<MI>& f) {
   const f32x16 z = {};
-  c.c[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a0, f.b0, z, 0, 0, 0);
-  c.c[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a0, f.b1, z, 0, 0, 0);
-  c.c[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a1, f.b0, z, 0, 0, 0);
-  c.c[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a1, f.b1, z, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    c.c[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b0, FIRST ? z : c.c[i][0], 0, 0, 0);
+    c.c[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b1, FIRST ? z : c.c[i][1], 0, 0, 0);
+  }
 }
 
-__device__ __forceinline__ void mfma4(Acc& c, const Frags& f) {
-  c.c[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a0, f.b0, c.c[0][0], 0, 0, 0);
-  c.c[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a0, f.b1, c.c[0][1], 0, 0, 0);
-  c.c[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a1, f.b0, c.c[1][0], 0, 0, 0);
-  c.c[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a1, f.b1, c.c[1][1], 0, 0, 0);
-}
-
-// Scheduling hint for one step: the 4 reads of the next step interleaved with
-// the 4 MFMAs of this one.
+// Scheduling hint for one step: the MI + 2 fragment reads of the next step
+// interleaved with the 2 MI MFMAs of this one.
+template <int MI>
 __device__ __forceinline__ void sched_step() {
-  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  if constexpr (MI == 2) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  } else {
+#pragma unroll
+    for (int t = 0; t < MI + 2; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * MI - (MI + 2), 0);
+  }
 }
 
-// Wait until the DMA loads of stage `q` have landed, given how many later
-// stages (at most STAGES - 2) have been issued after it.
+// Wait until the DMA loads of a stage have landed, given how many later
+// stages (0 .. STAGES - 2) have been issued after it (vmcnt <= later *
+// VM_PER_STAGE), and until this wave's LDS reads have returned.
+template <int MI, int N = 0>
 __device__ __forceinline__ void wait_stage(int later) {
-  if (later >= STAGES - 2) wait_vmcnt<8 * (STAGES - 2)>();
-  else if (later == 1) wait_vmcnt<8>();
-  else wait_vmcnt<0>();
+  using G = Geo<MI>;
+  if constexpr (N >= G::STAGES - 2) {
+    wait_vmcnt_lgkm0<G::VM_PER_STAGE * N>();
+  } else {
+    if (later <= N) wait_vmcnt_lgkm0<G::VM_PER_STAGE * N>();
+    else wait_stage<MI, N + 1>(later);
+  }
 }
 
-// Runs every tile of this workgroup: leaf-tree main loop, then epi(acc, mt, nt).
+// Runs every tile of this workgroup: leaf-tree main loop, then epi(acc, mt, nt, region).
 //
-// The k-tiles of all tiles form one stream q = 0 .. total-1, computed as a
-// software pipeline: while the last 4 MFMAs of stage q run, the wave has
-// already waited for stage q+1, passed the barrier, issued the DMA of stage
-// q+STAGES into the buffer stage q-1 just freed, and read the step-0 fragments
-// of stage q+1.  At leaf ends the accumulator folds into the pending tree; at
-// tile ends the epilogue runs.
-template <int LG, class Epi>
+// The k-tiles of all tiles form one stream q = 0 .. total-1 through a ring of
+// STAGES buffers.  Stage q+STAGES-1 is loaded into the buffer of stage q-1,
+// which every wave finished reading before the barrier that ended stage q-1
+// (each wave waits for its own LDS reads before that barrier); its DMA is
+// spread between the MFMA steps of stage q.  The end of stage q waits for
+// the DMA of stage q+1, passes the barrier and reads the step-0 fragments of
+// q+1 before the last MFMAs of q.  At leaf ends the accumulator folds into
+// the pending tree; at tile ends the epilogue borrows the buffer of the
+// tile's last stage, which no DMA targets until the next stage.
+template <int LG, int MI, class Epi>
 __device__ __forceinline__ void leaf_tree_persistent(const DenseOperands& op, int ktiles,
                                                      const TileSched& ts, Epi& epi, char* smem) {
+  using G = Geo<MI>;
+  constexpr int STAGES = G::STAGES;
   const int n_my = ts.count();
   if (n_my == 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  FragAddr fa;
+  FragAddr<MI> fa;
   fa.fr = lane & 31;
   fa.fk = lane >> 5;
-  fa.a0 = uint32_t((wm * 64 + fa.fr) * 128);
-  fa.a1 = fa.a0 + 32 * 128;
-  fa.w0 = uint32_t(OPER_BYTES + (wn * 64 + fa.fr) * 128);
+  fa.a0 = uint32_t((wm * 32 * MI + fa.fr) * 128);
+  fa.w0 = uint32_t(G::A_BYTES + (wn * 64 + fa.fr) * 128);
   fa.w1 = fa.w0 + 32 * 128;
   constexpr int L = 1 << LG;
   const int kpl = ktiles >> LG;
   const int total = n_my * ktiles;
 
-  Loader ld;
-  int l_tile = 0, l_kt = 0;
+  // DMA cursor: tile l_tile, leaf position l_pos, k-tile l_j inside the leaf.
+  // Odd tiles of this workgroup visit their leaves last to first, so that a
+  // new round of tiles starts on the k-slices the previous round used last
+  // (still in L2).  The pending-stack fold then meets every pair of subtrees
+  // in swapped operand order, which FP32 addition does not see (a + b == b + a
+  // bit for bit), so the tree value is the same.
+  Loader<MI> ld;
+  int l_tile = 0, l_pos = 0, l_j = 0;
   {
     int mt, nt;
     ts.coords(0, mt, nt);
-    loader_setup(ld, op, mt, nt);
+    ld.setup(op, mt, nt);
   }
-  auto issue_next = [&](int stage) {
-    loader_issue(ld, smem + (stage % STAGES) * STAGE_BYTES, l_kt);
-    if (++l_kt == ktiles) {
-      l_kt = 0;
-      if (++l_tile < n_my) {
-        int mt, nt;
-        ts.coords(l_tile, mt, nt);
-        loader_setup(ld, op, mt, nt);
+  auto kt_now = [&]() { return ((l_tile & 1) ? (L - 1 - l_pos) : l_pos) * kpl + l_j; };
+  auto advance = [&]() {
+    if (++l_j == kpl) {
+      l_j = 0;
+      if (++l_pos == L) {
+        l_pos = 0;
+        if (++l_tile < n_my) {
+          int mt, nt;
+          ts.coords(l_tile, mt, nt);
+          ld.setup(op, mt, nt);
+        }
       }
     }
   };
+  auto buf = [&](int q) { return smem + (q % STAGES) * G::STAGE; };
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p)
-    if (p < total) issue_next(p);
+    if (p < total) {
+      ld.issue_all(buf(p), kt_now());
+      advance();
+    }
 
-  Frags f0, f1;
-  wait_stage(min(STAGES - 2, total - 1));
+  Frags<MI> f0, f1;
+  wait_stage<MI>(min(STAGES - 2, total - 1));
   bar();
-  if (STAGES - 1 < total) issue_next(STAGES - 1);
   fa.read(f0, smem, 0);
 
-  // One k-tile of the stream: steps 0..2 with the next step's fragments read
-  // under the MFMAs; then the hand-over to stage q+1 (wait, barrier, DMA of
-  // stage q+STAGES, step-0 fragments of q+1) before the last 4 MFMAs.
-  auto stage = [&](Acc& cur, int q, auto first) {
-    const char* st = smem + (q % STAGES) * STAGE_BYTES;
+  auto stage = [&](AccT<MI>& cur, int q, auto first) {
+    const char* st = buf(q);
+    const bool pf = q + STAGES - 1 < total;
+    char* pb = buf(q + STAGES - 1);
     fa.read(f1, st, 1);
-    if constexpr (decltype(first)::value) mfma4_first(cur, f0);
-    else mfma4(cur, f0);
-    sched_step();
+    mfma_step<decltype(first)::value>(cur, f0);
+    const int kt = kt_now();
+    if (pf) ld.template issue<0>(pb, kt);
+    sched_step<MI>();
     fa.read(f0, st, 2);
-    mfma4(cur, f1);
-    sched_step();
+    mfma_step<false>(cur, f1);
+    if (pf) ld.template issue<1>(pb, kt);
+    sched_step<MI>();
     fa.read(f1, st, 3);
-    mfma4(cur, f0);
-    sched_step();
-    if (q + 1 < total) {
-      wait_stage(min(STAGES - 2, total - 2 - q));
-      bar();
-      if (q + STAGES < total) issue_next(q + STAGES);
-      fa.read(f0, smem + ((q + 1) % STAGES) * STAGE_BYTES, 0);
+    mfma_step<false>(cur, f0);
+    if (pf) {
+      ld.template issue<2>(pb, kt);
+      advance();
     }
-    mfma4(cur, f1);
+    sched_step<MI>();
+    if (q + 1 < total) {
+      wait_stage<MI>(min(STAGES - 2, total - 2 - q));
+      bar();
+      fa.read(f0, buf(q + 1), 0);
+    }
+    mfma_step<false>(cur, f1);
   };
 
   int q = 0;
   for (int ti = 0; ti < n_my; ++ti) {
-    Acc pend[LG > 0 ? LG : 1];
-    Acc cur;
+    AccT<MI> pend[LG > 0 ? LG : 1];
+    AccT<MI> cur;
 #pragma unroll 1
-    for (int leaf = 0; leaf < L; ++leaf) {
+    for (int pos = 0; pos < L; ++pos) {   // leaf pos, or L-1-pos on odd tiles
       stage(cur, q++, std::true_type{});
       for (int j = 1; j < kpl; ++j) stage(cur, q++, std::false_type{});
-      tree_fold<0, LG>(pend, cur, leaf);
+      tree_fold<0, LG>(pend, cur, pos);
     }
     int mt, nt;
     ts.coords(ti, mt, nt);
-    epi(cur, mt, nt, smem + RING_BYTES);
+    lds_sync();             // every wave's reads of the tile's last stage have completed
+    epi(cur, mt, nt, buf(q - 1));
   }
 }
 
 // Epilogue: store the tile (FP32, or bf16 by RNE).
-template <int EPI>
+template <int EPI, int MI>
 struct StoreEpi {
   void* C; int64_t ldc; int64_t M, N;
-  __device__ __forceinline__ void operator()(const Acc& acc, int mt, int nt, char*) const;
+  __device__ __forceinline__ void operator()(const AccT<MI>& acc, int mt, int nt, char*) const;
 };
 
-// Epilogue: per (row, 128-column vocabulary tile) max and sum of exp2, plus
-// the sampled token's logit.  The 128 x 128 tile is transposed through LDS in
-// two passes of 64 rows; in a pass, thread t owns row t/4, columns 32 (t%4)..+31.
+// Epilogue: per (row, 128-column vocabulary tile) max and sum of exp2.  The
+// tile is transposed through LDS in passes of 64 rows; in a pass, thread t
+// owns row t/4, columns 32 (t%4)..+31.  (The sampled token's logit is picked
+// by its own kernel: a global load here would have to wait for the whole DMA
+// ring, which returns in order.)
+template <int MI>
 struct LogprobEpi {
-  float2* part; float* xid; const int64_t* ids; int64_t M, V; int n_vt;
-  __device__ __forceinline__ void operator()(const Acc& acc, int mt, int nt, char* region) const;
+  float2* part; int64_t M, V; int n_vt;
+  __device__ __forceinline__ void operator()(const AccT<MI>& acc, int mt, int nt, char* region) const;
 };
 
 // ---------------------------------------------------------------------------
 // tree_gemm: C = leaf-tree(A W^T), FP32 or bf16 out.
 // ---------------------------------------------------------------------------
-template <int EPI>
-__device__ __forceinline__ void StoreEpi<EPI>::operator()(const Acc& acc, int mt, int nt, char*) const {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = int64_t(mt) * BM, n0 = int64_t(nt) * BN;
+template <int EPI, int MI>
+__device__ __forceinline__ void StoreEpi<EPI, MI>::operator()(const AccT<MI>& acc, int mt, int nt,
+                                                              char*) const {
+  const int tid = opaque_tid();
+  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = int64_t(mt) * Geo<MI>::BM, n0 = int64_t(nt) * BN;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int64_t col = n0 + acc_col(wn, j, lane);
       if (col >= N) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + acc_row(wm, i, v, lane);
+        const int64_t row = m0 + acc_row<MI>(wm, i, v, lane);
         if (row >= M) continue;
         if (EPI == kEpiF32)
           static_cast<float*>(C)[row * ldc + col] = acc.c[i][j][v];
@@ -515,15 +629,15 @@ __device__ __forceinline__ void StoreEpi<EPI>::operator()(const Acc& acc, int mt
     }
 }
 
-template <int LG, int EPI>
+template <int LG, int MI, int EPI>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void tree_gemm_kernel(DenseOperands op, void* __restrict__ C, int64_t ldc, int ktiles, int n_mt,
                       int n_nt) {
-  __shared__ __attribute__((aligned(1024))) char smem[P_LDS];
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   TileSched ts;
   ts.init(n_mt, n_nt);
-  StoreEpi<EPI> epi{C, ldc, op.M, op.N};
-  leaf_tree_persistent<LG>(op, ktiles, ts, epi, smem);
+  StoreEpi<EPI, MI> epi{C, ldc, op.M, op.N};
+  leaf_tree_persistent<LG, MI>(op, ktiles, ts, epi, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -547,29 +661,29 @@ __device__ __forceinline__ int epi_index(int r, int c) {
   return r * BN + (((c >> 2) ^ (r & 31)) << 2) + (c & 3);
 }
 
-__device__ __forceinline__ void LogprobEpi::operator()(const Acc& acc, int mt, int nt,
-                                                       char* region) const {
+template <int MI>
+__device__ __forceinline__ void LogprobEpi<MI>::operator()(const AccT<MI>& acc, int mt, int nt,
+                                                           char* region) const {
   float* E = reinterpret_cast<float*>(region);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = int64_t(mt) * BM, n0 = int64_t(nt) * BN;
+  const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = int64_t(mt) * Geo<MI>::BM, n0 = int64_t(nt) * BN;
   const int valid = int(V - n0 < BN ? V - n0 : BN) - 32 * (tid & 3);  // columns of this quarter
   const int r = tid >> 2, h = tid & 3;
 #pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    const int64_t row = m0 + pass * EPI_ROWS + r;
-    // Loaded and consumed on every path, so no load is left pending past the tile.
-    const int64_t id = ids[row < M ? row : M - 1];
-    const int64_t c = id - n0 - 32 * h;
-    const bool mine = row < M && id >= 0 && id < V && c >= 0 && c < 32;
-    if (wm == pass) {
+  for (int pass = 0; pass < MI; ++pass) {
+    const int64_t row = m0 + pass * 64 + r;
+    // 32-row block i of wave row wm is block b = MI wm + i of the tile, in pass b / 2.
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < MI; ++i) {
+      const int b = MI * wm + i;
+      if ((b >> 1) == pass) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int v = 0; v < 16; ++v)
-            E[epi_index(i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3), acc_col(wn, j, lane))] =
+            E[epi_index((b & 1) * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3), acc_col(wn, j, lane))] =
                 acc.c[i][j][v];
+      }
     }
     lds_sync();
     float x[32];
@@ -593,33 +707,84 @@ __device__ __forceinline__ void LogprobEpi::operator()(const Acc& acc, int mt, i
     o = __shfl_xor(sq, 2);
     sq = (h & 2) ? o + sq : sq + o;          // (q0 + q1) + (q2 + q3)
     if (row < M && h == 0) part[row * n_vt + nt] = make_float2(mx, sq);
-    if (mine) xid[row] = E[epi_index(r, int(32 * h + c))];
     lds_sync();
   }
 }
 
-template <int LG>
+template <int LG, int MI>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void logprob_tile_kernel(DenseOperands op, int ktiles, int n_mt, int n_nt, float2* __restrict__ part,
-                         float* __restrict__ xid, const int64_t* __restrict__ ids) {
-  __shared__ __attribute__((aligned(1024))) char smem[P_LDS];
+void logprob_tile_kernel(DenseOperands op, int ktiles, int n_mt, int n_nt, float2* __restrict__ part) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   TileSched ts;
   ts.init(n_mt, n_nt);
-  LogprobEpi epi{part, xid, ids, op.M, op.N, n_nt};
-  leaf_tree_persistent<LG>(op, ktiles, ts, epi, smem);
+  LogprobEpi<MI> epi{part, op.M, op.N, n_nt};
+  leaf_tree_persistent<LG, MI>(op, ktiles, ts, epi, smem);
 }
 
 // ---------------------------------------------------------------------------
-// logprob, pass 2: one wave per row combines the vocabulary tiles.
-//   g = max_t m_t (exact); S = sum_t s_t exp2((m_t - g) log2 e) by the
-//   balanced adjacent-pair tree over the tiles zero-padded to P = 64 * 2^q:
-//   lane l owns tiles [l 2^q, (l+1) 2^q) and folds them with a pending stack;
-//   the xor butterfly over lanes (masks 1, 2, ..., 32) forms the upper levels.
+// logprob: the sampled token's logit x[row, id[row]], computed exactly as the
+// tile kernels compute that element.  One wave per (32 rows, leaf): it forms
+// the 32 x 32 block H[rows] W[ids]^T of its leaf with the same
+// v_mfma_f32_32x32x16_bf16 k-steps (ascending, from +0) and keeps the
+// diagonal; the combine pass folds the leaves in the same balanced
+// adjacent-pair tree.  An MFMA result element depends only on its own A row,
+// B column and C input, so the diagonal holds the very bits the tile kernel
+// produced for (row, id[row]).  Rows whose id is out of range read W row 0;
+// their logprob becomes NaN in the combine.
 // ---------------------------------------------------------------------------
-constexpr int MAX_Q = 10;   // 2^10 tiles per lane: up to 65536 tiles
+constexpr int PICK_U = 32;   // k-steps loaded at once (a whole leaf of 512)
 
-// Same pending-stack fold as tree_fold, on one float per lane, for a chunk of
-// 2^q terms (q <= MAX_Q): term i parks at its lowest 0 bit below q; the last
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void logprob_pick_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ W,
+                         const int64_t* __restrict__ ids, float* __restrict__ xleaf, int64_t M,
+                         int64_t K, int64_t V) {
+  const int lane = threadIdx.x, leaf = blockIdx.y, leaves = gridDim.y;
+  const int i = lane & 31, half = lane >> 5;
+  const int64_t row0 = int64_t(blockIdx.x) * 32;
+  const int64_t row = row0 + i < M ? row0 + i : M - 1;
+  int64_t id = ids[row];
+  if (id < 0 || id >= V) id = 0;
+  const int64_t len = K / leaves;
+  const bf16x8* pa = reinterpret_cast<const bf16x8*>(H + row * K + leaf * len + 8 * half);
+  const bf16x8* pb = reinterpret_cast<const bf16x8*>(W + id * K + leaf * len + 8 * half);
+  const int steps = int(len / kMfmaK);
+  f32x16 c = {};
+  for (int s0 = 0; s0 < steps; s0 += PICK_U) {
+    bf16x8 a[PICK_U], b[PICK_U];
+#pragma unroll
+    for (int u = 0; u < PICK_U; ++u)
+      if (s0 + u < steps) {
+        a[u] = pa[(s0 + u) * 2];
+        b[u] = pb[(s0 + u) * 2];
+      }
+#pragma unroll
+    for (int u = 0; u < PICK_U; ++u)
+      if (s0 + u < steps) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[u], b[u], c, 0, 0, 0);
+  }
+  // Element (i, i) sits in lane i + 32 ((i >> 2) & 1), register 4 (i >> 3) + (i & 3).
+  if (((i >> 2) & 1) == half && row0 + i < M) {
+    const int vsel = 4 * (i >> 3) + (i & 3);
+    float d = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (v == vsel) d = c[v];
+    xleaf[(row0 + i) * leaves + leaf] = d;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// logprob, pass 2: one workgroup of 256 per row combines the vocabulary tiles.
+//   g = max_t m_t (exact); S = sum_t s_t exp2((m_t - g) log2 e) by the
+//   balanced adjacent-pair tree over the tiles zero-padded to P = 256 2^q
+//   (padding beyond the next power of two only adds +0 subtrees): thread t
+//   owns tiles [t 2^q, (t+1) 2^q) and folds them with a pending stack; the
+//   xor butterfly over lanes and then the pair tree over the 4 waves form the
+//   upper levels.  x = the picked logit's leaves folded by the leaf tree.
+// ---------------------------------------------------------------------------
+constexpr int MAX_Q = 8;   // 2^8 tiles per thread: up to 65536 tiles
+
+// Same pending-stack fold as tree_fold, on one float, for a chunk of 2^q
+// terms (q <= MAX_Q): term i parks at its lowest 0 bit below q; the last
 // term (all q bits 1) leaves the chunk's root in `cur`.
 template <int LEV>
 __device__ __forceinline__ void scalar_fold(float (&pend)[MAX_Q], float& cur, int i, int q) {
@@ -635,26 +800,32 @@ __device__ __forceinline__ void scalar_fold(float (&pend)[MAX_Q], float& cur, in
 }
 
 __global__ __launch_bounds__(256) void logprob_combine_kernel(
-    const float2* __restrict__ part, const float* __restrict__ xid,
+    const float2* __restrict__ part, const float* __restrict__ xleaf,
     const int64_t* __restrict__ ids, float* __restrict__ logprob, float* __restrict__ lse,
-    int64_t M, int n_vt, int q, int64_t V) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;
+    int n_vt, int q, int64_t V, int leaves) {
+  __shared__ float red[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
   const float2* pr = part + row * n_vt;
+  const int c = 1 << q;
+  const int t0 = tid * c;
+
   float g = -__builtin_inff();
-  for (int t = lane; t < n_vt; t += 64) g = fmaxf(g, pr[t].x);
+  for (int i = 0; i < c; ++i)
+    if (t0 + i < n_vt) g = fmaxf(g, pr[t0 + i].x);
 #pragma unroll
   for (int m = 1; m < 64; m *= 2) g = fmaxf(g, __shfl_xor(g, m));
+  if (lane == 0) red[wave] = g;
+  __syncthreads();
+  g = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));   // exact, any order
+  __syncthreads();
 
-  const int c = 1 << q;
   float pend[MAX_Q];
   float cur = 0.0f;
   for (int i = 0; i < c; ++i) {
-    const int t = lane * c + i;
     float term = 0.0f;
-    if (t < n_vt) {
-      const float2 p = pr[t];
+    if (t0 + i < n_vt) {
+      const float2 p = pr[t0 + i];
       term = p.y * __builtin_amdgcn_exp2f((p.x - g) * LOG2E);
     }
     cur = term;
@@ -666,11 +837,22 @@ __global__ __launch_bounds__(256) void logprob_combine_kernel(
     const float o = __shfl_xor(S, m);
     S = (lane & m) ? o + S : S + o;   // lower lane's subtree on the left
   }
-  if (lane == 0) {
+  if (lane == 0) red[wave] = S;
+  __syncthreads();
+  if (tid == 0) {
+    S = (red[0] + red[1]) + (red[2] + red[3]);
     const float l = g + __builtin_amdgcn_logf(S) * LN2;
+    float x[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = j < leaves ? xleaf[row * leaves + j] : 0.0f;
+#pragma unroll
+    for (int w = 1; w < 16; w *= 2)
+#pragma unroll
+      for (int j = 0; j + w < 16; j += 2 * w)
+        if (j + w < leaves) x[j] = x[j] + x[j + w];
     const int64_t id = ids[row];
     const bool ok = id >= 0 && id < V;
-    logprob[row] = ok ? xid[row] - l : __builtin_nanf("");
+    logprob[row] = ok ? x[0] - l : __builtin_nanf("");
     if (lse) lse[row] = l;
   }
 }
@@ -819,37 +1001,58 @@ int persistent_grid(int64_t n_tiles) {
   return int(want < full ? want : full);
 }
 
-template <int LG>
-hipError_t launch_tree_gemm_lg(const TreeGemmLaunch& p, hipStream_t s) {
-  const int n_mt = int(cdiv(p.M, BM)), n_nt = int(cdiv(p.N, BN));
+template <int LG, int MI>
+hipError_t launch_tree_gemm_mi(const TreeGemmLaunch& p, hipStream_t s) {
+  const int n_mt = int(cdiv(p.M, 64 * MI)), n_nt = int(cdiv(p.N, BN));
   const DenseOperands op{static_cast<const uint16_t*>(p.A), p.lda, p.M,
                          static_cast<const uint16_t*>(p.W), p.ldw, p.N};
   const int ktiles = int(p.K / BK);
   const dim3 grid(persistent_grid(int64_t(n_mt) * n_nt)), block(NTHREADS);
   if (p.epi == kEpiF32)
-    hipLaunchKernelGGL((tree_gemm_kernel<LG, kEpiF32>), grid, block, 0, s, op, p.C, p.ldc, ktiles,
-                       n_mt, n_nt);
+    hipLaunchKernelGGL((tree_gemm_kernel<LG, MI, kEpiF32>), grid, block, 0, s, op, p.C, p.ldc,
+                       ktiles, n_mt, n_nt);
   else
-    hipLaunchKernelGGL((tree_gemm_kernel<LG, kEpiBF16>), grid, block, 0, s, op, p.C, p.ldc, ktiles,
-                       n_mt, n_nt);
+    hipLaunchKernelGGL((tree_gemm_kernel<LG, MI, kEpiBF16>), grid, block, 0, s, op, p.C, p.ldc,
+                       ktiles, n_mt, n_nt);
+  return hipGetLastError();
+}
+
+template <int LG>
+hipError_t launch_tree_gemm_lg(const TreeGemmLaunch& p, hipStream_t s) {
+  if constexpr (block_m_for_log2(LG) == 192) {
+    if (block_m_for(p.M, LG) == 192) return launch_tree_gemm_mi<LG, 3>(p, s);
+  }
+  return launch_tree_gemm_mi<LG, 2>(p, s);
+}
+
+template <int LG, int MI>
+hipError_t launch_logprob_mi(const LogprobLaunch& p, hipStream_t s) {
+  const int n_mt = int(cdiv(p.M, 64 * MI)), n_vt = int(cdiv(p.V, BN));
+  const DenseOperands op{static_cast<const uint16_t*>(p.H), p.K, p.M,
+                         static_cast<const uint16_t*>(p.W), p.K, p.V};
+  float2* part = static_cast<float2*>(p.partials);
+  hipLaunchKernelGGL(logprob_pick_kernel, dim3(unsigned(cdiv(p.M, 32)), 1u << LG), dim3(64), 0, s,
+                     static_cast<const uint16_t*>(p.H), static_cast<const uint16_t*>(p.W), p.ids,
+                     p.xleaf, p.M, p.K, p.V);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((logprob_tile_kernel<LG, MI>), dim3(persistent_grid(int64_t(n_mt) * n_vt)),
+                     dim3(NTHREADS), 0, s, op, int(p.K / BK), n_mt, n_vt, part);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  int q = 0;
+  while ((256 << q) < n_vt) ++q;
+  hipLaunchKernelGGL(logprob_combine_kernel, dim3(unsigned(p.M)), dim3(256), 0, s, part, p.xleaf,
+                     p.ids, p.logprob, p.lse, n_vt, q, p.V, 1 << LG);
   return hipGetLastError();
 }
 
 template <int LG>
 hipError_t launch_logprob_lg(const LogprobLaunch& p, hipStream_t s) {
-  const int n_mt = int(cdiv(p.M, BM)), n_vt = int(cdiv(p.V, BN));
-  const DenseOperands op{static_cast<const uint16_t*>(p.H), p.K, p.M,
-                         static_cast<const uint16_t*>(p.W), p.K, p.V};
-  float2* part = static_cast<float2*>(p.partials);
-  hipLaunchKernelGGL((logprob_tile_kernel<LG>), dim3(persistent_grid(int64_t(n_mt) * n_vt)),
-                     dim3(NTHREADS), 0, s, op, int(p.K / BK), n_mt, n_vt, part, p.xid, p.ids);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  int q = 0;
-  while ((64 << q) < n_vt) ++q;
-  hipLaunchKernelGGL(logprob_combine_kernel, dim3(unsigned(cdiv(p.M, 4))), dim3(256), 0, s,
-                     part, p.xid, p.ids, p.logprob, p.lse, p.M, n_vt, q, p.V);
-  return hipGetLastError();
+  if constexpr (block_m_for_log2(LG) == 192) {
+    if (block_m_for(p.M, LG) == 192) return launch_logprob_mi<LG, 3>(p, s);
+  }
+  return launch_logprob_mi<LG, 2>(p, s);
 }
 
 template <int LG>

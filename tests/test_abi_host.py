@@ -57,7 +57,8 @@ def test_status_strings():
 def test_plan_digest_is_sha256_of_policy(K, leaves):
     p = tig.tig_plan_describe(K, leaves)
     assert p["leaves"] == leaves and p["leaf_len"] == K // leaves
-    assert (p["block_m"], p["block_n"], p["block_k"]) == (128, 128, 64)
+    # the dense kernels' tile: 192 rows while log2(leaves) + 1 accumulators fit, else 128
+    assert (p["block_m"], p["block_n"], p["block_k"]) == (192 if leaves <= 8 else 128, 128, 64)
     assert (p["mfma_m"], p["mfma_n"], p["mfma_k"]) == (32, 32, 16)
     assert p["digest"] == hashlib.sha256(p["policy"].encode()).hexdigest()
     assert f"K={K};leaves={leaves};" in p["policy"]
@@ -86,8 +87,10 @@ def test_plan_rejects(K, leaves, status):
 
 
 def test_workspace_queries():
+    # per-row partials of every 128-column vocabulary tile, then the picked logit's leaf values
     b = tig.tig_logprob_workspace_bytes(8192, 4096, 151936, 8)
-    assert b == 8192 * 1187 * 8 + 8192 * 4
+    assert b == 8192 * 1187 * 8 + 8192 * 8 * 4
+    assert tig.tig_logprob_workspace_bytes(8192, 4096, 151936, 16) == 8192 * 1187 * 8 + 8192 * 16 * 4
     assert tig.tig_logprob_workspace_bytes(0, 4096, 151936, 8) == 0
     assert tig.tig_logprob_workspace_bytes(3, 512, 1, 8) == 256 + 256
     m = tig.tig_moe_workspace_bytes(4096, 1408, 2048, 64, 8)
