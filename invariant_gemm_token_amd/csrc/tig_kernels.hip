@@ -455,20 +455,6 @@ __device__ __forceinline__ void sched_step() {
   }
 }
 
-// Wait until the DMA loads of a stage have landed, given how many later
-// stages (0 .. STAGES - 2) have been issued after it (vmcnt <= later *
-// VM_PER_STAGE), and until this wave's LDS reads have returned.
-template <int MI, int N = 0>
-__device__ __forceinline__ void wait_stage(int later) {
-  using G = Geo<MI>;
-  if constexpr (N >= G::STAGES - 2) {
-    wait_vmcnt_lgkm0<G::VM_PER_STAGE * N>();
-  } else {
-    if (later <= N) wait_vmcnt_lgkm0<G::VM_PER_STAGE * N>();
-    else wait_stage<MI, N + 1>(later);
-  }
-}
-
 // Runs every tile of this workgroup: leaf-tree main loop, then epi(acc, mt, nt, region).
 //
 // The k-tiles of all tiles form one stream q = 0 .. total-1 through a ring of
@@ -477,14 +463,18 @@ __device__ __forceinline__ void wait_stage(int later) {
 // (each wave waits for its own LDS reads before that barrier); its DMA is
 // spread between the MFMA steps of stage q.  The end of stage q waits for
 // the DMA of stage q+1, passes the barrier and reads the step-0 fragments of
-// q+1 before the last MFMAs of q.  At leaf ends the accumulator folds into
-// the pending tree; at tile ends the epilogue borrows the buffer of the
-// tile's last stage, which no DMA targets until the next stage.
+// q+1 before the last MFMAs of q.  Past the end of the stream every stage
+// still issues one k-tile (the last one again, into a buffer already
+// consumed), so each stage carries the same number of loads, the wait count
+// is a constant and the stage has no branch.  At leaf ends the accumulator
+// folds into the pending tree; at tile ends the epilogue borrows the buffer of
+// the tile's last stage, which no DMA targets until the next stage.
 template <int LG, int MI, class Epi>
 __device__ __forceinline__ void leaf_tree_persistent(const DenseOperands& op, int ktiles,
                                                      const TileSched& ts, Epi& epi, char* smem) {
   using G = Geo<MI>;
   constexpr int STAGES = G::STAGES;
+  constexpr uint32_t RING = uint32_t(STAGES * G::STAGE);
   const int n_my = ts.count();
   if (n_my == 0) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -499,89 +489,86 @@ __device__ __forceinline__ void leaf_tree_persistent(const DenseOperands& op, in
   const int kpl = ktiles >> LG;
   const int total = n_my * ktiles;
 
-  // DMA cursor: tile l_tile, leaf position l_pos, k-tile l_j inside the leaf.
-  // Odd tiles of this workgroup visit their leaves last to first, so that a
-  // new round of tiles starts on the k-slices the previous round used last
-  // (still in L2).  The pending-stack fold then meets every pair of subtrees
-  // in swapped operand order, which FP32 addition does not see (a + b == b + a
-  // bit for bit), so the tree value is the same.
+  // DMA cursor: tile l_tile, leaf position l_pos, k-tile kt.  Odd tiles of
+  // this workgroup visit their leaves last to first, so that a new round of
+  // tiles starts on the k-slices the previous round used last (still in L2).
+  // The pending-stack fold then meets every pair of subtrees in swapped
+  // operand order, which FP32 addition does not see (a + b == b + a bit for
+  // bit), so the tree value is the same.
   Loader<MI> ld;
-  int l_tile = 0, l_pos = 0, l_j = 0;
+  int l_tile = 0, l_pos = 0, l_j = 0, kt = 0, issued = 0;
   {
     int mt, nt;
     ts.coords(0, mt, nt);
     ld.setup(op, mt, nt);
   }
-  auto kt_now = [&]() { return ((l_tile & 1) ? (L - 1 - l_pos) : l_pos) * kpl + l_j; };
   auto advance = [&]() {
+    if (++issued >= total) return;   // past the end: keep re-issuing the last k-tile
+    ++kt;
     if (++l_j == kpl) {
       l_j = 0;
       if (++l_pos == L) {
         l_pos = 0;
-        if (++l_tile < n_my) {
-          int mt, nt;
-          ts.coords(l_tile, mt, nt);
-          ld.setup(op, mt, nt);
-        }
+        ++l_tile;
+        int mt, nt;
+        ts.coords(l_tile, mt, nt);
+        ld.setup(op, mt, nt);
       }
+      kt = ((l_tile & 1) ? (L - 1 - l_pos) : l_pos) * kpl;
     }
   };
-  auto buf = [&](int q) { return smem + (q % STAGES) * G::STAGE; };
 #pragma unroll
-  for (int p = 0; p < STAGES - 1; ++p)
-    if (p < total) {
-      ld.issue_all(buf(p), kt_now());
-      advance();
-    }
+  for (int p = 0; p < STAGES - 1; ++p) {
+    ld.issue_all(smem + p * G::STAGE, kt);
+    advance();
+  }
 
+  // Ring offsets of stage q and of the buffer being refilled (stage q-1).
+  uint32_t off_q = 0, off_pf = RING - uint32_t(G::STAGE);
   Frags<MI> f0, f1;
-  wait_stage<MI>(min(STAGES - 2, total - 1));
+  wait_vmcnt_lgkm0<G::VM_PER_STAGE * (STAGES - 2)>();
   bar();
   fa.read(f0, smem, 0);
 
-  auto stage = [&](AccT<MI>& cur, int q, auto first) {
-    const char* st = buf(q);
-    const bool pf = q + STAGES - 1 < total;
-    char* pb = buf(q + STAGES - 1);
+  auto stage = [&](AccT<MI>& cur, auto first) {
+    const char* st = smem + off_q;
+    char* pb = smem + off_pf;
+    const uint32_t off_n = off_q + G::STAGE == RING ? 0u : off_q + uint32_t(G::STAGE);
     fa.read(f1, st, 1);
     mfma_step<decltype(first)::value>(cur, f0);
-    const int kt = kt_now();
-    if (pf) ld.template issue<0>(pb, kt);
+    ld.template issue<0>(pb, kt);
     sched_step<MI>();
     fa.read(f0, st, 2);
     mfma_step<false>(cur, f1);
-    if (pf) ld.template issue<1>(pb, kt);
+    ld.template issue<1>(pb, kt);
     sched_step<MI>();
     fa.read(f1, st, 3);
     mfma_step<false>(cur, f0);
-    if (pf) {
-      ld.template issue<2>(pb, kt);
-      advance();
-    }
+    ld.template issue<2>(pb, kt);
+    advance();
     sched_step<MI>();
-    if (q + 1 < total) {
-      wait_stage<MI>(min(STAGES - 2, total - 2 - q));
-      bar();
-      fa.read(f0, buf(q + 1), 0);
-    }
+    wait_vmcnt_lgkm0<G::VM_PER_STAGE * (STAGES - 2)>();   // stage q+1 landed, own reads returned
+    bar();
+    fa.read(f0, smem + off_n, 0);
     mfma_step<false>(cur, f1);
+    off_pf = off_q;
+    off_q = off_n;
   };
 
-  int q = 0;
   for (int ti = 0; ti < n_my; ++ti) {
     AccT<MI> pend[LG > 0 ? LG : 1];
     AccT<MI> cur;
 #pragma unroll 1
     for (int pos = 0; pos < L; ++pos) {   // leaf pos, or L-1-pos on odd tiles
-      stage(cur, q++, std::true_type{});
-      for (int j = 1; j < kpl; ++j) stage(cur, q++, std::false_type{});
+      stage(cur, std::true_type{});
+      for (int j = 1; j < kpl; ++j) stage(cur, std::false_type{});
       tree_fold<0, LG>(pend, cur, pos);
     }
     int mt, nt;
     ts.coords(ti, mt, nt);
-    lds_sync();             // every wave's reads of the tile's last stage have completed
-    epi(cur, mt, nt, buf(q - 1));
+    epi(cur, mt, nt, smem + off_pf);   // the tile's last stage: read by all waves before the barrier
   }
+  wait_vmcnt<0>();   // no LDS DMA may still be landing when the workgroup ends
 }
 
 // Epilogue: store the tile (FP32, or bf16 by RNE).
