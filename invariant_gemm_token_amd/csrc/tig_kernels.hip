@@ -642,60 +642,107 @@ __device__ __forceinline__ float pair_tree_32(float (&e)[32]) {
   return e[0];
 }
 
-// [64][128] floats, 16-byte chunk index XOR (row % 32): a row's quarter read by
-// 16 rows at once spreads over all banks.
-__device__ __forceinline__ int epi_index(int r, int c) {
-  return r * BN + (((c >> 2) ^ (r & 31)) << 2) + (c & 3);
+// The two 32-lane halves of a wave exchange one float: lo = the value of lane
+// l & 31, hi = that of lane (l & 31) + 32, on every lane.
+__device__ __forceinline__ void halves(float x, float& lo, float& hi) {
+  const float o = __shfl_xor(x, 32);
+  const bool upper = (threadIdx.x & 32) != 0;
+  lo = upper ? o : x;
+  hi = upper ? x : o;
 }
 
+// Wave-private transpose area: 32 rows x 64 floats, 16-byte chunk index XOR
+// (row % 16), so the 16 rows a 128-bit read serves at once hit all 64 banks.
+__device__ __forceinline__ int tr_index(int r, int c) {
+  return r * 64 + (((c >> 2) ^ (r & 15)) << 2) + (c & 3);
+}
+
+// Wave (wm, wn) owns rows 32 MI wm .. +32 MI and columns 64 wn .. +63 of the
+// tile.  It transposes its blocks of 32 rows through its own 8 KiB of the
+// borrowed buffer (no barrier: a wave's LDS operations execute in order), so
+// lane l then holds row l % 32 of the block, columns 32 (l / 32) .. +31: the
+// pair tree over those 32, then the two lane halves (one exchange) give
+// the wave's 64-column max and sum; the two waves of a row pair meet through
+// LDS.  Tree over the 128 columns: ((q0 + q1) + (q2 + q3)), q = 32-column
+// quarters, the same as every other placement of this epilogue.
 template <int MI>
 __device__ __forceinline__ void LogprobEpi<MI>::operator()(const AccT<MI>& acc, int mt, int nt,
                                                            char* region) const {
-  float* E = reinterpret_cast<float*>(region);
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = int64_t(mt) * Geo<MI>::BM, n0 = int64_t(nt) * BN;
-  const int valid = int(V - n0 < BN ? V - n0 : BN) - 32 * (tid & 3);  // columns of this quarter
-  const int r = tid >> 2, h = tid & 3;
+  float* P = reinterpret_cast<float*>(region + wave * 8192);
+  const float* Q = reinterpret_cast<const float*>(region + (wave ^ 1) * 8192);
+  const int r = lane & 31, h = lane >> 5;
+  const int64_t m0 = int64_t(mt) * Geo<MI>::BM + wm * 32 * MI, n0 = int64_t(nt) * BN;
+  const bool full = n0 + BN <= V;
+  const int valid = int(V - n0) - 64 * wn - 32 * h;   // columns of this lane's 32 (when !full)
+  float x[MI][32];
+  float mw[MI];
 #pragma unroll
-  for (int pass = 0; pass < MI; ++pass) {
-    const int64_t row = m0 + pass * 64 + r;
-    // 32-row block i of wave row wm is block b = MI wm + i of the tile, in pass b / 2.
+  for (int i = 0; i < MI; ++i) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int b = MI * wm + i;
-      if ((b >> 1) == pass) {
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            E[epi_index((b & 1) * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3), acc_col(wn, j, lane))] =
-                acc.c[i][j][v];
-      }
-    }
-    lds_sync();
-    float x[32];
+      for (int v = 0; v < 16; ++v)
+        P[tr_index((v >> 2) * 8 + h * 4 + (v & 3), j * 32 + r)] = acc.c[i][j][v];
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const float4 t4 = *reinterpret_cast<const float4*>(E + r * BN + (((8 * h + k) ^ (r & 31)) << 2));
-      x[4 * k + 0] = t4.x; x[4 * k + 1] = t4.y; x[4 * k + 2] = t4.z; x[4 * k + 3] = t4.w;
+      const float4 t4 = *reinterpret_cast<const float4*>(P + r * 64 + (((8 * h + k) ^ (r & 15)) << 2));
+      x[i][4 * k + 0] = t4.x; x[i][4 * k + 1] = t4.y; x[i][4 * k + 2] = t4.z; x[i][4 * k + 3] = t4.w;
     }
+    asm volatile("" ::: "memory");
     float mx = -__builtin_inff();
+    if (full) {
 #pragma unroll
-    for (int c = 0; c < 32; ++c)
-      if (c < valid) mx = fmaxf(mx, x[c]);
-    mx = fmaxf(mx, __shfl_xor(mx, 1));
-    mx = fmaxf(mx, __shfl_xor(mx, 2));     // tile max (exact, any order)
+      for (int c = 0; c < 32; ++c) mx = fmaxf(mx, x[i][c]);
+    } else {
 #pragma unroll
-    for (int c = 0; c < 32; ++c)
-      x[c] = c < valid ? __builtin_amdgcn_exp2f((x[c] - mx) * LOG2E) : 0.0f;
-    float sq = pair_tree_32(x);
-    float o = __shfl_xor(sq, 1);
-    sq = (h & 1) ? o + sq : sq + o;          // (q0 + q1), (q2 + q3)
-    o = __shfl_xor(sq, 2);
-    sq = (h & 2) ? o + sq : sq + o;          // (q0 + q1) + (q2 + q3)
-    if (row < M && h == 0) part[row * n_vt + nt] = make_float2(mx, sq);
-    lds_sync();
+      for (int c = 0; c < 32; ++c)
+        if (c < valid) mx = fmaxf(mx, x[i][c]);
+    }
+    float lo, hi;
+    halves(mx, lo, hi);
+    mw[i] = fmaxf(lo, hi);
   }
+  // Publish this wave's 64-column maxes in its own area (the block data there
+  // has been read: the writes queue behind those reads).
+  if (h == 0) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) P[i * 32 + r] = mw[i];
+  }
+  lds_sync();
+  float sw[MI], mtile[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    mtile[i] = fmaxf(mw[i], Q[i * 32 + r]);   // tile max (exact, any order)
+    float e[32];
+    if (full) {
+#pragma unroll
+      for (int c = 0; c < 32; ++c) e[c] = __builtin_amdgcn_exp2f((x[i][c] - mtile[i]) * LOG2E);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 32; ++c)
+        e[c] = c < valid ? __builtin_amdgcn_exp2f((x[i][c] - mtile[i]) * LOG2E) : 0.0f;
+    }
+    const float sq = pair_tree_32(e);
+    float lo, hi;
+    halves(sq, lo, hi);
+    sw[i] = lo + hi;   // (q0 + q1) or (q2 + q3)
+  }
+  if (h == 0) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) P[128 + i * 32 + r] = sw[i];
+  }
+  lds_sync();
+  if (wn == 0 && h == 0) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const float st = sw[i] + Q[128 + i * 32 + r];   // (q0 + q1) + (q2 + q3)
+      const int64_t row = m0 + i * 32 + r;
+      if (row < M) part[row * n_vt + nt] = make_float2(mtile[i], st);
+    }
+  }
+  lds_sync();   // the partner's slots are read before the buffer is refilled
 }
 
 template <int LG, int MI>
