@@ -458,12 +458,13 @@ __device__ __forceinline__ void sched_step() {
 // Runs every tile of this workgroup: leaf-tree main loop, then epi(acc, mt, nt, region).
 //
 // The k-tiles of all tiles form one stream q = 0 .. total-1 through a ring of
-// STAGES buffers.  Stage q+STAGES-1 is loaded into the buffer of stage q-1,
-// which every wave finished reading before the barrier that ended stage q-1
-// (each wave waits for its own LDS reads before that barrier); its DMA is
-// spread between the MFMA steps of stage q.  The end of stage q waits for
-// the DMA of stage q+1, passes the barrier and reads the step-0 fragments of
-// q+1 before the last MFMAs of q.  Past the end of the stream every stage
+// STAGES buffers.  Fragments are read two k-steps ahead of their MFMAs.  In
+// the middle of stage q (after the MFMAs of steps 0 and 1) each wave waits
+// for its DMA of stage q+1 and for its own reads of stage q, then passes the
+// barrier: stage q+1 has landed everywhere and stage q's buffer is no longer
+// read.  Stage q+STAGES-1 is loaded into the buffer of stage q-1 (free since
+// the barrier of stage q-1), its DMA spread between the MFMA steps of stage
+// q.  Past the end of the stream every stage
 // still issues one k-tile (the last one again, into a buffer already
 // consumed), so each stage carries the same number of loads, the wait count
 // is a constant and the stage has no branch.  At leaf ends the accumulator
@@ -525,32 +526,37 @@ __device__ __forceinline__ void leaf_tree_persistent(const DenseOperands& op, in
 
   // Ring offsets of stage q and of the buffer being refilled (stage q-1).
   uint32_t off_q = 0, off_pf = RING - uint32_t(G::STAGE);
-  Frags<MI> f0, f1;
+  // Fragment registers of the four k-steps of a stage, read two steps ahead.
+  Frags<MI> F0, F1, F2, F3;
   wait_vmcnt_lgkm0<G::VM_PER_STAGE * (STAGES - 2)>();
   bar();
-  fa.read(f0, smem, 0);
+  fa.read(F0, smem, 0);
+  fa.read(F1, smem, 1);
 
+  // vmcnt once stage q+1 has landed, at the mid-stage wait of stage q: the
+  // later stages q+2 .. q+STAGES-2 and the A part of stage q+STAGES-1.
+  constexpr int MID_WAIT = G::VM_PER_STAGE * (STAGES - 3) + G::A_SEG;
   auto stage = [&](AccT<MI>& cur, auto first) {
     const char* st = smem + off_q;
     char* pb = smem + off_pf;
     const uint32_t off_n = off_q + G::STAGE == RING ? 0u : off_q + uint32_t(G::STAGE);
-    fa.read(f1, st, 1);
-    mfma_step<decltype(first)::value>(cur, f0);
+    fa.read(F2, st, 2);
+    mfma_step<decltype(first)::value>(cur, F0);
     ld.template issue<0>(pb, kt);
     sched_step<MI>();
-    fa.read(f0, st, 2);
-    mfma_step<false>(cur, f1);
+    fa.read(F3, st, 3);
+    mfma_step<false>(cur, F1);
     ld.template issue<1>(pb, kt);
     sched_step<MI>();
-    fa.read(f1, st, 3);
-    mfma_step<false>(cur, f0);
+    wait_vmcnt_lgkm0<MID_WAIT>();   // stage q+1 landed; this wave's reads of stage q returned
+    bar();                          // every wave is done with stage q's buffer
+    fa.read(F0, smem + off_n, 0);
+    mfma_step<false>(cur, F2);
     ld.template issue<2>(pb, kt);
     advance();
     sched_step<MI>();
-    wait_vmcnt_lgkm0<G::VM_PER_STAGE * (STAGES - 2)>();   // stage q+1 landed, own reads returned
-    bar();
-    fa.read(f0, smem + off_n, 0);
-    mfma_step<false>(cur, f1);
+    fa.read(F1, smem + off_n, 1);
+    mfma_step<false>(cur, F3);
     off_pf = off_q;
     off_q = off_n;
   };
