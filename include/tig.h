@@ -128,7 +128,7 @@ tig_status tig_logprob_workspace_bytes(int64_t M, int64_t K, int64_t n_vocab,
  * multiplied by the same leaf-tree kernel as tig_tree_gemm with FP32 output,
  * so a token's expert output equals tig_tree_gemm on that token's row alone.
  * The grid is sized from the static bound T*topk; nothing is read back.
- * Implemented: leaves <= 16, K/leaves a multiple of 64, topk <= 16.
+ * Implemented: leaves <= 16, K/leaves a multiple of 64, topk <= 16, n_experts <= 4096.
  */
 tig_status tig_moe_tree_gemm_combine(const void* H, const void* W_experts, int32_t n_experts,
                                      const int32_t* topk_ids, const float* topk_w, int32_t topk,

@@ -262,6 +262,10 @@ tig_status tig_moe_workspace_bytes(int64_t T, int64_t N, int64_t K, int32_t n_ex
     return fail(TIG_ERR_INVALID_ARG, "n_experts and topk must be >= 1");
   if (topk > tig::kMaxTopk)
     return fail(TIG_ERR_UNSUPPORTED, "topk > %d not implemented", tig::kMaxTopk);
+  if (n_experts > tig::kMaxExperts)
+    return fail(TIG_ERR_UNSUPPORTED, "n_experts > %d not implemented", tig::kMaxExperts);
+  if (int64_t(n_experts) * T * topk >= (int64_t(1) << 31))
+    return fail(TIG_ERR_UNSUPPORTED, "n_experts * T * topk too large for 32-bit row lists");
   *bytes = tig::moe_ws_bytes(T, N, n_experts, topk);
   return ok();
 }
@@ -292,11 +296,12 @@ tig_status tig_moe_tree_gemm_combine(const void* H, const void* W_experts, int32
   if (T * topk >= (int64_t(1) << 30) || T >= 65536)
     return fail(TIG_ERR_UNSUPPORTED, "T or T*topk too large");
   char* ws = static_cast<char*>(workspace);
-  const size_t c_bytes = tig::moe_counts_bytes(n_experts);
-  const size_t r_bytes = tig::moe_rows_bytes(T, topk, n_experts);
+  const tig::MoeWorkspace w = tig::moe_ws_layout(T, N, n_experts, topk);
   tig::MoeLaunch p{H, W_experts, topk_ids, topk_w, out, T, N, K, n_experts, topk, log2i(leaves),
-                   reinterpret_cast<int32_t*>(ws), reinterpret_cast<int32_t*>(ws + c_bytes),
-                   reinterpret_cast<float*>(ws + c_bytes + r_bytes)};
+                   reinterpret_cast<int32_t*>(ws + w.hist), reinterpret_cast<int32_t*>(ws + w.counts), reinterpret_cast<int32_t*>(ws + w.prefix),
+                   reinterpret_cast<int32_t*>(ws + w.n_items), reinterpret_cast<int32_t*>(ws + w.items),
+                   reinterpret_cast<int32_t*>(ws + w.tok), reinterpret_cast<int32_t*>(ws + w.pos),
+                   reinterpret_cast<float*>(ws + w.Y)};
   const hipError_t e = tig::launch_moe(p, stream);
   if (e != hipSuccess) return fail(TIG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();

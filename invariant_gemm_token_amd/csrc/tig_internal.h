@@ -29,6 +29,7 @@ constexpr int kMfmaM = 32, kMfmaN = 32, kMfmaK = 16;
 constexpr int kMaxLeavesLog2 = 4;  // leaves <= 16 implemented
 constexpr int kMaxVocabTiles = 65536;
 constexpr int kMaxTopk = 16;
+constexpr int kMaxExperts = 4096;   // per-chunk expert histogram in LDS
 constexpr int kPolicyVersion = 1;
 
 enum Epilogue { kEpiF32 = 0, kEpiBF16 = 1 };
@@ -57,9 +58,15 @@ struct MoeLaunch {
   float* out;
   int64_t T, N, K;
   int n_experts, topk, leaves_log2;
-  int32_t* counts;  // [n_experts]
-  int32_t* rows;    // [n_experts][T*topk] pair indices, stable order
-  float* Y;         // [T*topk][N] expert outputs (FP32 tree result)
+  int32_t* hist;     // [pair chunks of 256][n_experts] counts, then first rows
+  int32_t* counts;   // [n_experts] rows routed to each expert
+  int32_t* prefix;   // [n_experts + 1] first row of each expert in Y, then the total
+  int32_t* n_items;  // [1] number of (expert, m-tile) work items
+  int32_t* items;    // [max items][4]: expert, m-tile, rows of the expert, its first row in Y
+  int32_t* tok;      // [n_experts][T*topk] (+ one tile of padding): token of each of the
+                     // expert's rows, in ascending (token, slot) order
+  int32_t* pos;      // [T*topk] row of (token, slot) inside its expert's list
+  float* Y;          // [T*topk][N] expert outputs (FP32 tree result), rows sorted by expert
 };
 
 // Workspace layout helpers (bytes, 256-aligned sections).
@@ -73,13 +80,29 @@ inline size_t logprob_partials_bytes(int64_t M, int64_t V) {
 inline size_t logprob_ws_bytes(int64_t M, int64_t V, int leaves) {
   return logprob_partials_bytes(M, V) + align256(size_t(M) * size_t(leaves) * 4);
 }
-inline size_t moe_counts_bytes(int n_experts) { return align256(size_t(n_experts) * 4); }
-inline size_t moe_rows_bytes(int64_t T, int topk, int n_experts) {
-  return align256(size_t(n_experts) * size_t(T) * size_t(topk) * 4);
+// MoE workspace, in this order (each part 256-byte aligned).
+inline int64_t moe_max_items(int64_t T, int topk, int n_experts) {
+  return cdiv(T * topk, kBlockM) + n_experts;   // m-tiles of 128 or more rows, one partial per expert
+}
+struct MoeWorkspace {
+  size_t hist, counts, prefix, n_items, items, tok, pos, Y, total;
+};
+inline MoeWorkspace moe_ws_layout(int64_t T, int64_t N, int n_experts, int topk) {
+  MoeWorkspace w;
+  const size_t pairs = size_t(T) * size_t(topk);
+  w.hist = 0;
+  w.counts = w.hist + align256(size_t(cdiv(int64_t(pairs), 256)) * size_t(n_experts) * 4);
+  w.prefix = w.counts + align256(size_t(n_experts) * 4);
+  w.n_items = w.prefix + align256(size_t(n_experts + 1) * 4);
+  w.items = w.n_items + 256;
+  w.tok = w.items + align256(size_t(moe_max_items(T, topk, n_experts)) * 16);
+  w.pos = w.tok + align256((size_t(n_experts) * pairs + 256) * 4);
+  w.Y = w.pos + align256(pairs * 4);
+  w.total = w.Y + align256(pairs * size_t(N) * 4);
+  return w;
 }
 inline size_t moe_ws_bytes(int64_t T, int64_t N, int n_experts, int topk) {
-  return moe_counts_bytes(n_experts) + moe_rows_bytes(T, topk, n_experts) +
-         align256(size_t(T) * size_t(topk) * size_t(N) * 4);
+  return moe_ws_layout(T, N, n_experts, topk).total;
 }
 
 // Launchers: enqueue on `stream`, return the first HIP error (hipSuccess if none).

@@ -35,15 +35,11 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int BM = kBlockM, BN = kBlockN, BK = kBlockK;   // BM: the MoE kernel's tile
 constexpr int NTHREADS = 256;                 // 4 waves of 64, 2 x 2 over the tile
-constexpr int OPER_BYTES = BM * BK * 2;       // one operand's k-tile: 16 KiB
-constexpr int STAGE_BYTES = 2 * OPER_BYTES;   // A and W
-constexpr int EPI_LD = BN + 4;                // padded row of the epilogue tile (floats)
-constexpr int MAIN_LDS = 2 * STAGE_BYTES;
-constexpr int EPI_LDS = BM * EPI_LD * 4;
-constexpr int LDS_BYTES = MAIN_LDS > EPI_LDS ? MAIN_LDS : EPI_LDS;
 constexpr int GROUP_M = 8;                    // m-tiles that share each W tile in L2
 constexpr int kLdsBytes = 160 * 1024;         // LDS of one CU: the persistent kernels' ring
 #define LDS_AS __attribute__((address_space(3)))
+// Read-only for the whole launch: uniform loads through it become scalar loads.
+#define CONST_AS __attribute__((address_space(4)))
 constexpr uint32_t OOB = 0xFFFFFFF0u;         // offset past every buffer's range
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer, 32-bit data format
 constexpr float LOG2E = 1.44269504088896340736f;
@@ -100,113 +96,6 @@ __device__ __forceinline__ void tree_fold(A (&pend)[LG > 0 ? LG : 1], A& cur, in
       tree_fold<LEV + 1, LG>(pend, cur, leaf);
     }
   }
-}
-
-// Workgroup -> output tile.  Workgroups are dealt to the 8 XCDs round-robin,
-// so the blocks of one XCD get one contiguous run of the logical order; that
-// order walks GROUP_M m-tiles down each n-tile, so the ~32 workgroups live on
-// one XCD share W tiles and A tiles in its L2.  Returns false for padding blocks.
-__device__ __forceinline__ bool tile_of(int n_mt, int n_nt, int& mt, int& nt) {
-  const int total = n_mt * n_nt;
-  const int per_xcd = (total + 7) >> 3;
-  const int b = blockIdx.x;
-  const int lam = (b & 7) * per_xcd + (b >> 3);
-  if (lam >= total) return false;
-  const int per_group = GROUP_M * n_nt;
-  const int group = lam / per_group;
-  const int first = group * GROUP_M;
-  const int gm = min(n_mt - first, GROUP_M);
-  const int local = lam - group * per_group;
-  mt = first + local % gm;
-  nt = local / gm;
-  return true;
-}
-
-inline int grid_blocks(int64_t n_tiles) { return int(((n_tiles + 7) >> 3) << 3); }
-
-// The leaf-tree main loop for one 128 x 128 tile.
-//   aoff[i], woff[i]: byte offset of this thread's i-th staged row (rows
-//   (tid>>3) + 32 i of the tile) plus its 16-byte column chunk, relative to the
-//   resources ra / rw; OOB for a row that does not exist (reads zeros).
-// On return `root` holds this wave's 64 x 64 part of the tree result; every
-// wave has passed the last barrier, so the LDS may be reused.
-template <int LG>
-__device__ __forceinline__ void leaf_tree_mainloop(Acc& root, __amdgpu_buffer_rsrc_t ra,
-                                                   const uint32_t (&aoff)[4],
-                                                   __amdgpu_buffer_rsrc_t rw,
-                                                   const uint32_t (&woff)[4],
-                                                   int ktiles_per_leaf, char* smem) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  // Staging: row r = tid>>3 (+32 i), 16-byte chunk c = tid&7 stored at chunk
-  // c ^ (r & 7) of the 128-byte LDS row, so the 32 rows one fragment read
-  // touches fall in distinct banks.
-  const int srow = tid >> 3;
-  const uint32_t st_off = uint32_t(srow * 128 + (((tid & 7) ^ (srow & 7)) << 4));
-  // Fragments: lane reads row (lane & 31) of a 32-row block at k-chunk
-  // 2 s + (lane >> 5) of k-step s.
-  const int fr = lane & 31, fk = lane >> 5;
-  const uint32_t a_rd0 = uint32_t((wm * 64 + fr) * 128), a_rd1 = a_rd0 + 32 * 128;
-  const uint32_t w_rd0 = uint32_t(OPER_BYTES + (wn * 64 + fr) * 128), w_rd1 = w_rd0 + 32 * 128;
-
-  constexpr int L = 1 << LG;
-  const int T = L * ktiles_per_leaf;
-
-  i32x4 ga[4], gw[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ga[i] = load16(ra, aoff[i]);
-    gw[i] = load16(rw, woff[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    *reinterpret_cast<i32x4*>(smem + st_off + i * 4096) = ga[i];
-    *reinterpret_cast<i32x4*>(smem + OPER_BYTES + st_off + i * 4096) = gw[i];
-  }
-  __syncthreads();
-
-  Acc pend[LG > 0 ? LG : 1];
-  Acc cur;
-  int g = 0;
-  for (int leaf = 0; leaf < L; ++leaf) {
-    acc_zero(cur);
-    for (int j = 0; j < ktiles_per_leaf; ++j, ++g) {
-      const bool more = (g + 1) < T;
-      if (more) {
-        const uint32_t kb = uint32_t(g + 1) * (BK * 2);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ga[i] = load16(ra, aoff[i] == OOB ? OOB : aoff[i] + kb);
-          gw[i] = load16(rw, woff[i] == OOB ? OOB : woff[i] + kb);
-        }
-      }
-      const char* base = smem + (g & 1) * STAGE_BYTES;
-#pragma unroll
-      for (int s = 0; s < BK / kMfmaK; ++s) {
-        const uint32_t ch = uint32_t(((2 * s + fk) ^ (fr & 7)) << 4);
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(base + a_rd0 + ch);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(base + a_rd1 + ch);
-        const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(base + w_rd0 + ch);
-        const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(base + w_rd1 + ch);
-        cur.c[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b0, cur.c[0][0], 0, 0, 0);
-        cur.c[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, b1, cur.c[0][1], 0, 0, 0);
-        cur.c[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b0, cur.c[1][0], 0, 0, 0);
-        cur.c[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, b1, cur.c[1][1], 0, 0, 0);
-      }
-      if (more) {
-        char* nb = smem + ((g + 1) & 1) * STAGE_BYTES;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *reinterpret_cast<i32x4*>(nb + st_off + i * 4096) = ga[i];
-          *reinterpret_cast<i32x4*>(nb + OPER_BYTES + st_off + i * 4096) = gw[i];
-        }
-      }
-      __syncthreads();
-    }
-    tree_fold<0, LG>(pend, cur, leaf);
-  }
-  root = cur;
 }
 
 // Output position of accumulator element (block i, j; register v) of a lane:
@@ -354,11 +243,12 @@ struct DenseOperands {
 template <int MI>
 struct Loader {
   using G = Geo<MI>;
+  DenseOperands op;
   __amdgpu_buffer_rsrc_t ra, rw;
   uint32_t oa[2], ow[2];      // lane offsets for even / odd segments
   uint32_t sa, sw;            // 16 * leading dimension in bytes / 2 (one segment of rows)
 
-  __device__ __forceinline__ void setup(const DenseOperands& op, int mt, int nt) {
+  __device__ __forceinline__ void setup(int mt, int nt) {
     const int lane = threadIdx.x & 63;
     const int64_t m0 = int64_t(mt) * G::BM, n0 = int64_t(nt) * BN;
     const int64_t rows_a = op.M - m0 < G::BM ? op.M - m0 : G::BM;
@@ -470,9 +360,9 @@ __device__ __forceinline__ void sched_step() {
 // is a constant and the stage has no branch.  At leaf ends the accumulator
 // folds into the pending tree; at tile ends the epilogue borrows the buffer of
 // the tile's last stage, which no DMA targets until the next stage.
-template <int LG, int MI, class Epi>
-__device__ __forceinline__ void leaf_tree_persistent(const DenseOperands& op, int ktiles,
-                                                     const TileSched& ts, Epi& epi, char* smem) {
+template <int LG, int MI, class Ld, class Epi>
+__device__ __forceinline__ void leaf_tree_persistent(Ld& ld, int ktiles, const TileSched& ts, Epi& epi,
+                                                     char* smem) {
   using G = Geo<MI>;
   constexpr int STAGES = G::STAGES;
   constexpr uint32_t RING = uint32_t(STAGES * G::STAGE);
@@ -496,12 +386,11 @@ __device__ __forceinline__ void leaf_tree_persistent(const DenseOperands& op, in
   // The pending-stack fold then meets every pair of subtrees in swapped
   // operand order, which FP32 addition does not see (a + b == b + a bit for
   // bit), so the tree value is the same.
-  Loader<MI> ld;
   int l_tile = 0, l_pos = 0, l_j = 0, kt = 0, issued = 0;
   {
     int mt, nt;
     ts.coords(0, mt, nt);
-    ld.setup(op, mt, nt);
+    ld.setup(mt, nt);
   }
   auto advance = [&]() {
     if (++issued >= total) return;   // past the end: keep re-issuing the last k-tile
@@ -513,7 +402,7 @@ __device__ __forceinline__ void leaf_tree_persistent(const DenseOperands& op, in
         ++l_tile;
         int mt, nt;
         ts.coords(l_tile, mt, nt);
-        ld.setup(op, mt, nt);
+        ld.setup(mt, nt);
       }
       kt = ((l_tile & 1) ? (L - 1 - l_pos) : l_pos) * kpl;
     }
@@ -630,7 +519,8 @@ void tree_gemm_kernel(DenseOperands op, void* __restrict__ C, int64_t ldc, int k
   TileSched ts;
   ts.init(n_mt, n_nt);
   StoreEpi<EPI, MI> epi{C, ldc, op.M, op.N};
-  leaf_tree_persistent<LG, MI>(op, ktiles, ts, epi, smem);
+  Loader<MI> ld{op};
+  leaf_tree_persistent<LG, MI>(ld, ktiles, ts, epi, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -758,7 +648,8 @@ void logprob_tile_kernel(DenseOperands op, int ktiles, int n_mt, int n_nt, float
   TileSched ts;
   ts.init(n_mt, n_nt);
   LogprobEpi<MI> epi{part, op.M, op.N, n_nt};
-  leaf_tree_persistent<LG, MI>(op, ktiles, ts, epi, smem);
+  Loader<MI> ld{op};
+  leaf_tree_persistent<LG, MI>(ld, ktiles, ts, epi, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -898,130 +789,245 @@ __global__ __launch_bounds__(256) void logprob_combine_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// MoE: route (stable per-expert row lists), per-expert leaf-tree GEMM with
-// indirect rows, fixed-order FP32 combine.
+// MoE: route (stable per-expert token lists), plan (work items), per-expert
+// leaf-tree GEMM on the persistent pipeline with gathered A rows, and the
+// fixed-order FP32 combine.
 // ---------------------------------------------------------------------------
 
-// One workgroup per expert: scan the (token, slot) pairs in index order and
-// list the ones routed to this expert, keeping that order.
-__global__ __launch_bounds__(256) void moe_route_kernel(const int32_t* __restrict__ topk_ids,
-                                                        int64_t n_pairs, int32_t* __restrict__ counts,
-                                                        int32_t* __restrict__ rows) {
-  __shared__ int wave_tot[4];
-  const int e = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int32_t* out = rows + int64_t(e) * n_pairs;
-  int base = 0;
-  for (int64_t p0 = 0; p0 < n_pairs; p0 += 256) {
-    const int64_t p = p0 + tid;
-    const bool hit = p < n_pairs && topk_ids[p] == e;
-    const uint64_t mask = __ballot(hit);
-    const int before = __popcll(mask & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_tot[wave] = __popcll(mask);
-    __syncthreads();
-    int off = base;
-    for (int w = 0; w < wave; ++w) off += wave_tot[w];
-    if (hit) out[off + before] = int32_t(p);
-    base += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
-    __syncthreads();
-  }
-  if (tid == 0) counts[e] = base;
-}
+// Routing is a stable partition of the (token, slot) pairs p = t * topk + s
+// by expert, in three steps: per-chunk expert histograms, a scan that gives
+// every (chunk, expert) its first row and plans the work items, and a scatter
+// that keeps pair order inside each expert.  The order of an expert's rows
+// does not reach any value (a row's result depends on that row alone); it
+// only keeps the workspace reproducible.
+constexpr int ROUTE_CHUNK = 256;
 
-// Work item -> (expert, m-tile of that expert's rows).  Every workgroup reads
-// the expert counts and walks their m-tile counts; items past the end exit.
-__device__ __forceinline__ bool moe_item(const int32_t* counts, int n_experts, int item, int& e,
-                                         int& mt) {
-  int acc = 0;
-  for (int x = 0; x < n_experts; ++x) {
-    const int tiles = (counts[x] + BM - 1) / BM;
-    if (item < acc + tiles) {
-      e = x;
-      mt = item - acc;
-      return true;
-    }
-    acc += tiles;
-  }
-  return false;
-}
-
-template <int LG>
-__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void moe_gemm_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wx,
-                     const int32_t* __restrict__ counts, const int32_t* __restrict__ rows,
-                     float* __restrict__ Y, int64_t T, int64_t N, int64_t K, int topk,
-                     int n_experts, int64_t n_pairs, int ktiles_per_leaf, int n_items, int n_nt) {
-  __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
-  __shared__ int32_t rowmap[BM];
-  int item, nt;
-  if (!tile_of(n_items, n_nt, item, nt)) return;
-  int e, mt;
-  if (!moe_item(counts, n_experts, item, e, mt)) return;
-  const int cnt = counts[e];
-  const int64_t r0 = int64_t(mt) * BM;
-  const int64_t n0 = int64_t(nt) * BN;
-  const int tid = threadIdx.x;
-  if (tid < BM) rowmap[tid] = r0 + tid < cnt ? rows[int64_t(e) * n_pairs + r0 + tid] : -1;
+// Chunk c of 256 pairs: hist[c][e] = pairs of the chunk routed to expert e.
+__global__ __launch_bounds__(256) void moe_hist_kernel(const int32_t* __restrict__ topk_ids,
+                                                       int64_t n_pairs, int n_experts,
+                                                       int32_t* __restrict__ hist) {
+  extern __shared__ int h[];
+  for (int e = threadIdx.x; e < n_experts; e += 256) h[e] = 0;
   __syncthreads();
-  const int64_t rows_w = N - n0 < BN ? N - n0 : BN;
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(H, uint32_t(T * K * 2));
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(Wx + (int64_t(e) * N + n0) * K, uint32_t(rows_w * K * 2));
-  uint32_t aoff[4], woff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (tid >> 3) + 32 * i;
-    const int pr = rowmap[r];
-    aoff[i] = pr >= 0 ? uint32_t((pr / topk) * K * 2 + (tid & 7) * 16) : OOB;
-    woff[i] = r < rows_w ? uint32_t(r * K * 2 + (tid & 7) * 16) : OOB;
+  const int64_t p = int64_t(blockIdx.x) * ROUTE_CHUNK + threadIdx.x;
+  if (p < n_pairs) {
+    const int e = topk_ids[p];
+    if (e >= 0 && e < n_experts) atomicAdd(&h[e], 1);   // a count: the order of adds does not matter
   }
-  Acc acc;
-  leaf_tree_mainloop<LG>(acc, ra, aoff, rw, woff, ktiles_per_leaf, smem);
+  __syncthreads();
+  for (int e = threadIdx.x; e < n_experts; e += 256) hist[int64_t(blockIdx.x) * n_experts + e] = h[e];
+}
 
-  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+// One workgroup: hist[c][e] becomes the first row of chunk c inside expert e's
+// list (exclusive scan over chunks); counts, first row of each expert in Y,
+// and the work items (expert, m-tile of bm rows, rows of the expert, first row).
+__global__ __launch_bounds__(256) void moe_plan_kernel(int32_t* __restrict__ hist, int n_chunks,
+                                                       int n_experts, int bm,
+                                                       int32_t* __restrict__ counts,
+                                                       int32_t* __restrict__ prefix,
+                                                       int4* __restrict__ items,
+                                                       int32_t* __restrict__ n_items) {
+  for (int e = threadIdx.x; e < n_experts; e += 256) {
+    int acc = 0;
+    for (int c = 0; c < n_chunks; ++c) {
+      const int v = hist[int64_t(c) * n_experts + e];
+      hist[int64_t(c) * n_experts + e] = acc;
+      acc += v;
+    }
+    counts[e] = acc;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  int acc = 0, k = 0;
+  for (int e = 0; e < n_experts; ++e) {
+    const int c = counts[e];
+    prefix[e] = acc;
+    for (int mt = 0; mt * bm < c; ++mt) items[k++] = make_int4(e, mt, c, acc);
+    acc += c;
+  }
+  prefix[n_experts] = acc;
+  *n_items = k;
+}
+
+// Chunk c: each pair's row = first row of (c, e) + pairs of the chunk before
+// it with the same expert; tok[e][row] = its token, pos[p] = row.
+__global__ __launch_bounds__(256) void moe_scatter_kernel(const int32_t* __restrict__ topk_ids,
+                                                          int64_t n_pairs, int n_experts, int topk,
+                                                          const int32_t* __restrict__ first,
+                                                          int32_t* __restrict__ tok,
+                                                          int32_t* __restrict__ pos) {
+  __shared__ int ids[ROUTE_CHUNK];
+  const int64_t p = int64_t(blockIdx.x) * ROUTE_CHUNK + threadIdx.x;
+  const int e = p < n_pairs ? topk_ids[p] : -1;
+  ids[threadIdx.x] = e;
+  __syncthreads();
+  if (e < 0 || e >= n_experts) return;
+  int before = 0;
+  for (int i = 0; i < int(threadIdx.x); ++i) before += ids[i] == e;
+  const int row = first[int64_t(blockIdx.x) * n_experts + e] + before;
+  tok[int64_t(e) * n_pairs + row] = int32_t(p / topk);
+  pos[p] = row;
+}
+
+// Operands of the MoE GEMM: A rows are gathered tokens of H, W is the expert's slice.
+struct MoeOperands {
+  const uint16_t* H; const uint16_t* W;
+  const int32_t* tok; const int4* items;
+  float* Y;
+  int64_t T, N, K, n_pairs;
+};
+
+// DMA loader for a work item (expert e, m-tile mt) and n-tile nt: the lane's
+// A rows come from the expert's token list (the eight consecutive rows of a
+// segment read by scalar loads), W rows as in the dense loader.  Rows past the
+// expert's count read as zero.
+template <int MI>
+struct MoeLoader {
+  using G = Geo<MI>;
+  MoeOperands op;
+  __amdgpu_buffer_rsrc_t ra, rw;
+  uint32_t oa[G::A_SEG], ow[2];
+  uint32_t sw;
+
+  __device__ __forceinline__ void setup(int item, int nt) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const CONST_AS int32_t* it = (const CONST_AS int32_t*)op.items + 4 * item;
+    const int e = it[0], mt = it[1], count = it[2];
+    const int64_t n0 = int64_t(nt) * BN;
+    const int64_t rows_w = op.N - n0 < BN ? op.N - n0 : BN;
+    ra = make_rsrc(op.H, uint32_t(op.T * op.K * 2));
+    rw = make_rsrc(op.W + (int64_t(e) * op.N + n0) * op.K, uint32_t(rows_w * op.K * 2));
+    const int rs = lane >> 3;
+    const uint32_t c0 = uint32_t(((lane & 7) ^ (rs >> 1)) << 4), c1 = c0 ^ 64u;
+    ow[0] = uint32_t(rs * op.K * 2) + c0;
+    ow[1] = uint32_t(rs * op.K * 2) + c1;
+    sw = uint32_t(op.K * 16);
+    const CONST_AS int32_t* tl =
+        (const CONST_AS int32_t*)op.tok + int64_t(e) * op.n_pairs + int64_t(mt) * G::BM;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < G::A_SEG; ++j) {
+      const int g = wave * G::A_SEG + j;
+      int t8[8];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = n0 + acc_col(wn, j, lane);
-      if (col >= N) continue;
+      for (int k = 0; k < 8; ++k) t8[k] = tl[g * 8 + k];
+      int t = t8[0];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int pr = rowmap[acc_row(wm, i, v, lane)];
-        if (pr < 0) continue;
-        Y[int64_t(pr) * N + col] = acc.c[i][j][v];
+      for (int k = 1; k < 8; ++k) t = rs == k ? t8[k] : t;
+      const int slot = mt * G::BM + g * 8 + rs;
+      oa[j] = slot < count ? uint32_t(t) * uint32_t(op.K * 2) + ((j & 1) ? c1 : c0) : OOB;
+    }
+  }
+
+  template <int P>
+  __device__ __forceinline__ void issue(char* stage, int kt) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int so = kt * (BK * 2);
+    if constexpr (P < 2) {
+      constexpr int H = G::A_SEG / 2;
+#pragma unroll
+      for (int j = P * H; j < (P + 1) * H; ++j) {
+        const int g = wave * G::A_SEG + j;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LDS_AS void*)(stage + g * 1024), 16,
+                                                 uint32_t(oa[j]), so, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int g = wave * 4 + j;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (LDS_AS void*)(stage + G::A_BYTES + g * 1024),
+                                                 16, ow[j & 1] + uint32_t(g) * sw, so, 0, 0);
       }
     }
+  }
+  __device__ __forceinline__ void issue_all(char* stage, int kt) const {
+    issue<0>(stage, kt);
+    issue<1>(stage, kt);
+    issue<2>(stage, kt);
+  }
+};
+
+// Epilogue: the item's rows go to Y rows prefix[e] + mt * BM + r (FP32).
+template <int MI>
+struct MoeStoreEpi {
+  MoeOperands op;
+  __device__ __forceinline__ void operator()(const AccT<MI>& acc, int item, int nt, char*) const {
+    const int tid = opaque_tid();
+    const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+    const CONST_AS int32_t* it = (const CONST_AS int32_t*)op.items + 4 * item;
+    const int rows = it[2] - it[1] * Geo<MI>::BM;
+    float* C = op.Y + (int64_t(it[3]) + int64_t(it[1]) * Geo<MI>::BM) * op.N;
+    const int64_t n0 = int64_t(nt) * BN;
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t col = n0 + acc_col(wn, j, lane);
+        if (col >= op.N) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = acc_row<MI>(wm, i, v, lane);
+          if (row < rows) C[int64_t(row) * op.N + col] = acc.c[i][j][v];
+        }
+      }
+  }
+};
+
+template <int LG, int MI>
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void moe_tile_kernel(MoeOperands op, const int32_t* __restrict__ n_items, int ktiles, int n_nt) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  TileSched ts;
+  ts.init(*(const CONST_AS int32_t*)n_items, n_nt);
+  MoeLoader<MI> ld{op};
+  MoeStoreEpi<MI> epi{op};
+  leaf_tree_persistent<LG, MI>(ld, ktiles, ts, epi, smem);
 }
 
 // out[t, n] = sum over the token's experts in ascending id (ties: slot order)
-// of w * y, an FP32 multiply then an FP32 add, from +0.
+// of w * y, an FP32 multiply then an FP32 add, from +0.  One workgroup per
+// token: the order and the Y rows are found once, then every thread walks
+// its columns.
 __global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* __restrict__ topk_ids,
                                                           const float* __restrict__ topk_w,
                                                           const float* __restrict__ Y,
+                                                          const int32_t* __restrict__ prefix,
+                                                          const int32_t* __restrict__ pos,
                                                           float* __restrict__ out, int64_t N,
                                                           int topk, int n_experts) {
-  const int64_t t = blockIdx.y;
-  const int64_t n = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (n >= N) return;
-  int order[kMaxTopk];
-  bool bad = false;
-  for (int s = 0; s < topk; ++s) {
-    const int e = topk_ids[t * topk + s];
-    bad |= e < 0 || e >= n_experts;
-    int j = s;
-    while (j > 0 && topk_ids[t * topk + order[j - 1]] > e) {   // stable insertion
-      order[j] = order[j - 1];
-      --j;
+  __shared__ int64_t rows[kMaxTopk];
+  __shared__ float wts[kMaxTopk];
+  __shared__ int bad;
+  const int64_t t = blockIdx.x;
+  if (threadIdx.x == 0) {
+    int order[kMaxTopk];
+    int b = 0;
+    for (int s = 0; s < topk; ++s) {
+      const int e = topk_ids[t * topk + s];
+      b |= e < 0 || e >= n_experts;
+      int j = s;
+      while (j > 0 && topk_ids[t * topk + order[j - 1]] > e) {   // stable insertion
+        order[j] = order[j - 1];
+        --j;
+      }
+      order[j] = s;
     }
-    order[j] = s;
+    bad = b;
+    for (int k = 0; k < topk; ++k) {
+      const int64_t p = t * topk + order[k];
+      rows[k] = b ? 0 : (int64_t(prefix[topk_ids[p]]) + pos[p]) * N;
+      wts[k] = topk_w[p];
+    }
   }
-  float acc = 0.0f;
-  for (int k = 0; k < topk; ++k) {
-    const int s = order[k];
-    const float term = topk_w[t * topk + s] * Y[(t * topk + s) * N + n];
-    acc = acc + term;
+  __syncthreads();
+  for (int64_t n = threadIdx.x; n < N; n += 256) {
+    float acc = 0.0f;
+    for (int k = 0; k < topk; ++k) {
+      const float term = wts[k] * Y[rows[k] + n];
+      acc = acc + term;
+    }
+    out[t * N + n] = bad ? __builtin_nanf("") : acc;
   }
-  out[t * N + n] = bad ? __builtin_nanf("") : acc;
 }
 
 // Persistent grid: one workgroup per CU (multiple of 8 for the XCD deal), or
@@ -1095,26 +1101,41 @@ hipError_t launch_logprob_lg(const LogprobLaunch& p, hipStream_t s) {
   return launch_logprob_mi<LG, 2>(p, s);
 }
 
-template <int LG>
-hipError_t launch_moe_lg(const MoeLaunch& p, hipStream_t s) {
+template <int LG, int MI>
+hipError_t launch_moe_mi(const MoeLaunch& p, hipStream_t s) {
   const int64_t n_pairs = p.T * p.topk;
-  hipLaunchKernelGGL(moe_route_kernel, dim3(p.n_experts), dim3(256), 0, s, p.topk_ids, n_pairs,
-                     p.counts, p.rows);
+  const int n_chunks = int(cdiv(n_pairs, ROUTE_CHUNK));
+  hipLaunchKernelGGL(moe_hist_kernel, dim3(n_chunks), dim3(256), size_t(p.n_experts) * 4, s, p.topk_ids,
+                     n_pairs, p.n_experts, p.hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // Static bound on the m-tiles of all experts together.
-  const int n_items = int(cdiv(n_pairs, BM) + p.n_experts);
-  const int n_nt = int(cdiv(p.N, BN));
-  const int kpl = int((p.K >> LG) / BK);
-  hipLaunchKernelGGL((moe_gemm_kernel<LG>), dim3(grid_blocks(int64_t(n_items) * n_nt)),
-                     dim3(NTHREADS), 0, s, static_cast<const uint16_t*>(p.H),
-                     static_cast<const uint16_t*>(p.W), p.counts, p.rows, p.Y, p.T, p.N, p.K,
-                     p.topk, p.n_experts, n_pairs, kpl, n_items, n_nt);
+  hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(256), 0, s, p.hist, n_chunks, p.n_experts, 64 * MI,
+                     p.counts, p.prefix, reinterpret_cast<int4*>(p.items), p.n_items);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(moe_combine_kernel, dim3(unsigned(cdiv(p.N, 256)), unsigned(p.T)), dim3(256),
-                     0, s, p.topk_ids, p.topk_w, p.Y, p.out, p.N, p.topk, p.n_experts);
+  hipLaunchKernelGGL(moe_scatter_kernel, dim3(n_chunks), dim3(256), 0, s, p.topk_ids, n_pairs,
+                     p.n_experts, p.topk, p.hist, p.tok, p.pos);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int n_nt = int(cdiv(p.N, BN));
+  const MoeOperands op{static_cast<const uint16_t*>(p.H), static_cast<const uint16_t*>(p.W), p.tok,
+                       reinterpret_cast<const int4*>(p.items), p.Y, p.T, p.N, p.K, n_pairs};
+  // The grid is sized from the static bound on work items; workgroups without
+  // a tile exit at once.
+  const int64_t max_tiles = moe_max_items(p.T, p.topk, p.n_experts) * n_nt;
+  hipLaunchKernelGGL((moe_tile_kernel<LG, MI>), dim3(persistent_grid(max_tiles)), dim3(NTHREADS), 0, s,
+                     op, p.n_items, int(p.K / BK), n_nt);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(moe_combine_kernel, dim3(unsigned(p.T)), dim3(256), 0, s, p.topk_ids, p.topk_w, p.Y,
+                     p.prefix, p.pos, p.out, p.N, p.topk, p.n_experts);
   return hipGetLastError();
+}
+
+template <int LG>
+hipError_t launch_moe_lg(const MoeLaunch& p, hipStream_t s) {
+  if constexpr (block_m_for_log2(LG) == 192) return launch_moe_mi<LG, 3>(p, s);
+  else return launch_moe_mi<LG, 2>(p, s);
 }
 
 }  // namespace
