@@ -298,7 +298,8 @@ tig_status tig_moe_tree_gemm_combine(const void* H, const void* W_experts, int32
   char* ws = static_cast<char*>(workspace);
   const tig::MoeWorkspace w = tig::moe_ws_layout(T, N, n_experts, topk);
   tig::MoeLaunch p{H, W_experts, topk_ids, topk_w, out, T, N, K, n_experts, topk, log2i(leaves),
-                   reinterpret_cast<int32_t*>(ws + w.hist), reinterpret_cast<int32_t*>(ws + w.counts), reinterpret_cast<int32_t*>(ws + w.prefix),
+                   reinterpret_cast<int32_t*>(ws + w.hist), reinterpret_cast<int32_t*>(ws + w.first),
+                   reinterpret_cast<int32_t*>(ws + w.counts), reinterpret_cast<int32_t*>(ws + w.prefix),
                    reinterpret_cast<int32_t*>(ws + w.n_items), reinterpret_cast<int32_t*>(ws + w.items),
                    reinterpret_cast<int32_t*>(ws + w.tok), reinterpret_cast<int32_t*>(ws + w.pos),
                    reinterpret_cast<float*>(ws + w.Y)};

@@ -58,7 +58,8 @@ struct MoeLaunch {
   float* out;
   int64_t T, N, K;
   int n_experts, topk, leaves_log2;
-  int32_t* hist;     // [pair chunks of 256][n_experts] counts, then first rows
+  int32_t* hist;     // [pair chunks of 256][n_experts] pairs of the chunk routed to each expert
+  int32_t* first;    // [pair chunks of 256][n_experts] first row of the chunk in the expert's list
   int32_t* counts;   // [n_experts] rows routed to each expert
   int32_t* prefix;   // [n_experts + 1] first row of each expert in Y, then the total
   int32_t* n_items;  // [1] number of (expert, m-tile) work items
@@ -85,13 +86,15 @@ inline int64_t moe_max_items(int64_t T, int topk, int n_experts) {
   return cdiv(T * topk, kBlockM) + n_experts;   // m-tiles of 128 or more rows, one partial per expert
 }
 struct MoeWorkspace {
-  size_t hist, counts, prefix, n_items, items, tok, pos, Y, total;
+  size_t hist, first, counts, prefix, n_items, items, tok, pos, Y, total;
 };
 inline MoeWorkspace moe_ws_layout(int64_t T, int64_t N, int n_experts, int topk) {
   MoeWorkspace w;
   const size_t pairs = size_t(T) * size_t(topk);
+  const size_t chunk_table = align256(size_t(cdiv(int64_t(pairs), 256)) * size_t(n_experts) * 4);
   w.hist = 0;
-  w.counts = w.hist + align256(size_t(cdiv(int64_t(pairs), 256)) * size_t(n_experts) * 4);
+  w.first = w.hist + chunk_table;
+  w.counts = w.first + chunk_table;
   w.prefix = w.counts + align256(size_t(n_experts) * 4);
   w.n_items = w.prefix + align256(size_t(n_experts + 1) * 4);
   w.items = w.n_items + 256;

@@ -818,29 +818,67 @@ __global__ __launch_bounds__(256) void moe_hist_kernel(const int32_t* __restrict
   for (int e = threadIdx.x; e < n_experts; e += 256) hist[int64_t(blockIdx.x) * n_experts + e] = h[e];
 }
 
-// One workgroup: hist[c][e] becomes the first row of chunk c inside expert e's
-// list (exclusive scan over chunks); counts, first row of each expert in Y,
-// and the work items (expert, m-tile of bm rows, rows of the expert, first row).
-__global__ __launch_bounds__(256) void moe_plan_kernel(int32_t* __restrict__ hist, int n_chunks,
+// One workgroup: first[c][e] = first row of chunk c inside expert e's list
+// (exclusive scan of hist over chunks; four threads per expert, each owning a
+// quarter of the chunks); counts, first row of each expert in Y, and the work
+// items (expert, m-tile of bm rows, rows of the expert, first row).
+__global__ __launch_bounds__(256) void moe_plan_kernel(const int32_t* __restrict__ hist,
+                                                       int32_t* __restrict__ first, int n_chunks,
                                                        int n_experts, int bm,
                                                        int32_t* __restrict__ counts,
                                                        int32_t* __restrict__ prefix,
                                                        int4* __restrict__ items,
                                                        int32_t* __restrict__ n_items) {
-  for (int e = threadIdx.x; e < n_experts; e += 256) {
-    int acc = 0;
-    for (int c = 0; c < n_chunks; ++c) {
-      const int v = hist[int64_t(c) * n_experts + e];
-      hist[int64_t(c) * n_experts + e] = acc;
-      acc += v;
+  __shared__ int part[256];
+  __shared__ int cnt[kMaxExperts];
+  const int q = threadIdx.x & 3;
+  const int per = (n_chunks + 3) >> 2;
+  const int c0 = q * per, c1 = min(n_chunks, c0 + per);
+  for (int e0 = 0; e0 < n_experts; e0 += 64) {
+    const int e = e0 + (threadIdx.x >> 2);
+    int sum = 0;
+    if (e < n_experts) {
+      int c = c0;
+      for (; c + 8 <= c1; c += 8) {   // eight loads in flight
+        int v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = hist[int64_t(c + k) * n_experts + e];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sum += v[k];
+      }
+      for (; c < c1; ++c) sum += hist[int64_t(c) * n_experts + e];
     }
-    counts[e] = acc;
+    part[threadIdx.x] = sum;
+    __syncthreads();
+    if (e < n_experts) {
+      int acc = 0;
+      for (int k = 0; k < q; ++k) acc += part[(threadIdx.x & ~3) + k];
+      int c = c0;
+      for (; c + 8 <= c1; c += 8) {
+        int v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = hist[int64_t(c + k) * n_experts + e];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          first[int64_t(c + k) * n_experts + e] = acc;
+          acc += v[k];
+        }
+      }
+      for (; c < c1; ++c) {
+        first[int64_t(c) * n_experts + e] = acc;
+        acc += hist[int64_t(c) * n_experts + e];
+      }
+      if (q == 3) {
+        cnt[e] = acc;
+        counts[e] = acc;
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
   if (threadIdx.x != 0) return;
   int acc = 0, k = 0;
   for (int e = 0; e < n_experts; ++e) {
-    const int c = counts[e];
+    const int c = cnt[e];
     prefix[e] = acc;
     for (int mt = 0; mt * bm < c; ++mt) items[k++] = make_int4(e, mt, c, acc);
     acc += c;
@@ -1109,12 +1147,12 @@ hipError_t launch_moe_mi(const MoeLaunch& p, hipStream_t s) {
                      n_pairs, p.n_experts, p.hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(256), 0, s, p.hist, n_chunks, p.n_experts, 64 * MI,
-                     p.counts, p.prefix, reinterpret_cast<int4*>(p.items), p.n_items);
+  hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(256), 0, s, p.hist, p.first, n_chunks, p.n_experts,
+                     64 * MI, p.counts, p.prefix, reinterpret_cast<int4*>(p.items), p.n_items);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(moe_scatter_kernel, dim3(n_chunks), dim3(256), 0, s, p.topk_ids, n_pairs,
-                     p.n_experts, p.topk, p.hist, p.tok, p.pos);
+                     p.n_experts, p.topk, p.first, p.tok, p.pos);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int n_nt = int(cdiv(p.N, BN));
