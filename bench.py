@@ -7,18 +7,24 @@ line carries:
 
 * value: whole-job tokens/s over the timed steps (HIP events on the stream the
   kernels run on, bracketed by device synchronisation);
-* roofline: the fused kernel is bound by the matrix cores at this size; achieved
-  = 2 M K V flops per call / the event-timed duration of one call;
-* tree_gemm: the same contraction rate as TFLOP/s and fraction of the bf16
-  dense peak;
+* roofline: the fused LM-head kernel is bound by the matrix cores at this
+  size; achieved = 2 M K V flops per call / the event-timed duration of one
+  call, against the bf16 dense peak; traffic = HBM-side bytes per launch from
+  the committed counter summary, when it was taken on this kernel source;
+* tree_gemm: the same contraction rate as TFLOP/s and fraction of the peak;
 * decode: one 128-row decode step of the same LM head (bound by streaming the
   1.245 GB weight from HBM), tokens/s and fraction of 8 TB/s;
+* linear, moe, large: the other workloads of the path, each with its own
+  roofline: the 4096 x 4096 linear layer at 4096 and 4097 rows (matrix
+  cores), the MoE-shaped contraction (64 experts 2048 -> 1408, top-8 of 4096
+  tokens, matrix cores), and the hidden-7168 / vocabulary-129280 LM head at
+  16 leaves (16384-row prefill: matrix cores; 256-row decode: both);
 * cpu_baseline: the fp64 CPU oracle timed on a bounded sample of rows of the
-  same workload, on this host's cores (skipped with --no-cpu-baseline).
+  headline workload, on this host's cores (skipped with --no-cpu-baseline).
 
-Inputs are seeded and synthetic (bf16 N(0,1) activations, N(0,0.02) weights);
-sampled ids are uniform in [0, V) here (the kernel's cost does not depend on
-their values).
+Inputs are seeded and synthetic (workloads: bf16 N(0,1) activations,
+N(0,0.02) weights, uniform sampled ids, top-8 routing of N(0,1) router
+logits); a kernel's cost does not depend on the values.
 """
 
 from __future__ import annotations
@@ -80,9 +86,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048)
+    ap.add_argument("--cpu-rows", type=int, default=8192)
+    ap.add_argument("--no-extra", action="store_true", help="skip the linear / moe / large lines")
     ap.add_argument("--phase", choices=("all", "prefill", "decode"), default="all",
-                    help="time only one configuration (for per-kernel profiles)")
+                    help="time only one LM-head configuration (for per-kernel profiles)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -103,6 +110,35 @@ def main():
         sys.exit(1)
     tig.load()
     dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def timed(fn, steps, warmup):
+        """Mean ms per call over `steps` calls (events on the launch stream) and per-call times."""
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(stream)
+        for i in range(steps):
+            fn()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        return ev[0].elapsed_time(ev[-1]) / steps, per
+
+    def mfma_line(flops, ms):
+        tf = flops / (ms / 1e3) / 1e12
+        return {"bound": "mfma", "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": tf / PEAK_BF16_TFLOPS}
+
+    def hbm_line(nbytes, ms):
+        gbs = nbytes / (ms / 1e3) / 1e9
+        return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}
+
+    # ---------------- headline: LM-head prefill ----------------
     cfg = wl.CONFIGS["lmhead"]
     M, K, V, L = cfg.n_seq * cfg.n_pos, cfg.K, cfg.N, cfg.leaves
     s = wl.streams(cfg.seed)
@@ -110,16 +146,11 @@ def main():
     H = wl.normal_bf16(s["H"], (M, K), 1.0)
     W = wl.normal_bf16(s["W"], (V, K), 0.02)
     ids = wl.uniform_ids(s["ids"], M, V)
-    log(f"inputs generated in {time.time() - t0:.1f}s")
-
-    def to_dev(bits):
-        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
-
+    log(f"lm-head inputs generated in {time.time() - t0:.1f}s")
     Hd, Wd, idd = to_dev(H), to_dev(W), torch.from_numpy(ids).to(dev)
     ws = torch.empty(tig.tig_logprob_workspace_bytes(M, K, V, L), dtype=torch.uint8, device=dev)
     lp = torch.empty(M, dtype=torch.float32, device=dev)
     lse = torch.empty(M, dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
 
     if args.copy_probe:
         # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE calibrate the counters.
@@ -129,61 +160,33 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step():
-        tig.tig_logprob_gather(Hd, Wd, idd, lp, lse, L, ws)
-
     tok_s = ms_step = tflops = None
     flops = 2.0 * M * K * V
     if args.phase in ("all", "prefill"):
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-        torch.cuda.synchronize()
-        ev[0].record(stream)
-        for i in range(args.steps):
-            step()
-            ev[i + 1].record(stream)
-        torch.cuda.synchronize()
-        per_call = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
-        total_ms = ev[0].elapsed_time(ev[-1])
-        ms_step = total_ms / args.steps
-        tok_s = M * args.steps / (total_ms / 1e3)
-        avg_call_s = float(np.mean(per_call)) / 1e3
-        tflops = flops / avg_call_s / 1e12
+        ms_step, per_call = timed(lambda: tig.tig_logprob_gather(Hd, Wd, idd, lp, lse, L, ws),
+                                  args.steps, args.warmup)
+        tok_s = M / (ms_step / 1e3)
+        tflops = flops / (float(np.mean(per_call)) / 1e3) / 1e12
         log(f"prefill: {ms_step:.3f} ms/step, {tok_s:.4g} tok/s, {tflops:.1f} TFLOP/s "
             f"(min {min(per_call):.3f} ms, max {max(per_call):.3f} ms)")
 
-    # decode: one step of 128 sequences against the same weights
-    Md = cfg.n_seq
-    Hdec, iddec = Hd[:Md].contiguous(), idd[:Md].contiguous()
-    lpd = torch.empty(Md, dtype=torch.float32, device=dev)
-    wsd = torch.empty(tig.tig_logprob_workspace_bytes(Md, K, V, L), dtype=torch.uint8, device=dev)
-
-    def dstep():
-        tig.tig_logprob_gather(Hdec, Wd, iddec, lpd, None, L, wsd)
-
     decode = None
     if args.phase in ("all", "decode"):
-        for _ in range(args.warmup):
-            dstep()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.decode_steps):
-            dstep()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        dec_ms = e0.elapsed_time(e1) / args.decode_steps
+        Md = cfg.n_seq
+        Hdec, iddec = Hd[:Md].contiguous(), idd[:Md].contiguous()
+        lpd = torch.empty(Md, dtype=torch.float32, device=dev)
+        wsd = torch.empty(tig.tig_logprob_workspace_bytes(Md, K, V, L), dtype=torch.uint8, device=dev)
+        dec_ms, _ = timed(lambda: tig.tig_logprob_gather(Hdec, Wd, iddec, lpd, None, L, wsd),
+                          args.decode_steps, args.warmup)
         dec_bytes = 2.0 * K * V + 2.0 * Md * K + 8.0 * Md + 4.0 * Md
-        dec_gbs = dec_bytes / (dec_ms / 1e3) / 1e9
-        log(f"decode M={Md}: {dec_ms * 1e3:.1f} us/step, {dec_gbs:.0f} GB/s")
+        r = hbm_line(dec_bytes, dec_ms)
+        log(f"decode M={Md}: {dec_ms * 1e3:.1f} us/step, {r['achieved']:.0f} GB/s")
         decode = {"tokens": Md, "us_per_step": dec_ms * 1e3, "tokens_per_s": Md / (dec_ms / 1e3),
-                  "achieved_GBs": dec_gbs, "peak_GBs": PEAK_HBM_GBS, "hbm_frac": dec_gbs / PEAK_HBM_GBS,
-                  "algorithmic_bytes": dec_bytes}
+                  "achieved_GBs": r["achieved"], "peak_GBs": PEAK_HBM_GBS, "hbm_frac": r["frac"],
+                  "algorithmic_bytes": dec_bytes, "roofline": r}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.phase == "all":
         import oracle
         try:
             from threadpoolctl import threadpool_info
@@ -199,6 +202,61 @@ def main():
                "sample": f"first {args.cpu_rows} of the {M} prefill rows, full vocabulary {V}, "
                          f"fp64 numpy (includes converting W to fp64), {dt:.1f}s"}
         log(f"cpu oracle: {cpu['value']:.3g} tok/s on {threads} threads")
+    del H, W
+    del Hd, Wd, idd, ws
+
+    # ---------------- the other workloads of the path ----------------
+    linear = moe = large = None
+    if not args.no_extra and args.phase == "all":
+        c = wl.CONFIGS["linear"]
+        sl = wl.streams(c.seed)
+        A = to_dev(wl.normal_bf16(sl["H"], (4097, c.K), 1.0))
+        Wl = to_dev(wl.normal_bf16(sl["W"], (c.N, c.K), 0.02))
+        linear = {}
+        for Mr in (4096, 4097):
+            Ar = A[:Mr]
+            C = torch.empty(Mr, c.N, dtype=torch.float32, device=dev)
+            ms, _ = timed(lambda: tig.tig_tree_gemm(Ar, Wl, C, c.leaves), 20, 3)
+            linear[f"M{Mr}"] = {"ms": ms, "roofline": mfma_line(2.0 * Mr * c.K * c.N, ms)}
+            log(f"linear M={Mr}: {ms * 1e3:.1f} us, {linear[f'M{Mr}']['roofline']['achieved']:.0f} TFLOP/s")
+        del A, Wl, C
+
+        c = wl.CONFIGS["moe"]
+        sm = wl.streams(c.seed)
+        Hm = to_dev(wl.normal_bf16(sm["H"], (c.tokens, c.K), 1.0))
+        We = to_dev(wl.normal_bf16(sm["W"], (c.experts, c.N, c.K), 0.02))
+        tid, tw = wl.route_topk(sm["route"], c.tokens, c.experts, c.topk)
+        tid, tw = torch.from_numpy(tid).to(dev), torch.from_numpy(tw).to(dev)
+        out = torch.empty(c.tokens, c.N, dtype=torch.float32, device=dev)
+        wsm = torch.empty(tig.tig_moe_workspace_bytes(c.tokens, c.N, c.K, c.experts, c.topk),
+                          dtype=torch.uint8, device=dev)
+        ms, _ = timed(lambda: tig.tig_moe_tree_gemm_combine(Hm, We, tid, tw, out, c.leaves, wsm), 20, 3)
+        moe = {"ms": ms, "shape": f"T={c.tokens} E={c.experts} top{c.topk} K={c.K} N={c.N} leaves={c.leaves}",
+               "roofline": mfma_line(2.0 * c.tokens * c.topk * c.K * c.N, ms)}
+        log(f"moe: {ms * 1e3:.1f} us, {moe['roofline']['achieved']:.0f} TFLOP/s")
+        del Hm, We, out, wsm
+
+        c = wl.CONFIGS["large"]
+        sg = wl.streams(c.seed)
+        Mg = c.n_seq * c.n_pos
+        Hg = to_dev(wl.normal_bf16(sg["H"], (Mg, c.K), 1.0))
+        Wg = to_dev(wl.normal_bf16(sg["W"], (c.N, c.K), 0.02))
+        ig = torch.from_numpy(wl.uniform_ids(sg["ids"], Mg, c.N)).to(dev)
+        large = {}
+        for name, Mr, steps in (("prefill", Mg, 3), ("decode", c.n_seq, 20)):
+            Hr, ir = Hg[:Mr].contiguous(), ig[:Mr].contiguous()
+            wsg = torch.empty(tig.tig_logprob_workspace_bytes(Mr, c.K, c.N, c.leaves), dtype=torch.uint8,
+                              device=dev)
+            lpg = torch.empty(Mr, dtype=torch.float32, device=dev)
+            ms, _ = timed(lambda: tig.tig_logprob_gather(Hr, Wg, ir, lpg, None, c.leaves, wsg), steps, 1)
+            line = {"tokens": Mr, "ms": ms, "tokens_per_s": Mr / (ms / 1e3),
+                    "roofline": mfma_line(2.0 * Mr * c.K * c.N, ms),
+                    "hbm": hbm_line(2.0 * c.K * c.N + 2.0 * Mr * c.K + 12.0 * Mr, ms)}
+            large[name] = line
+            log(f"large {name} M={Mr}: {ms:.3f} ms, {line['roofline']['achieved']:.0f} TFLOP/s, "
+                f"{line['hbm']['achieved']:.0f} GB/s")
+            del wsg
+        del Hg, Wg
 
     out = {
         "metric": "logprob tokens/s (LM head 4096x151936 bf16) + tree-GEMM TFLOP/s, % MFMA peak",
@@ -214,6 +272,9 @@ def main():
             "tflops": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
             "shape": f"M={M} K={K} N={V} leaves={L}"},
         "decode": decode,
+        "linear": linear,
+        "moe": moe,
+        "large": large,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
