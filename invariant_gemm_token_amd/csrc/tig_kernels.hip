@@ -188,12 +188,19 @@ struct Geo {
 constexpr int GROUP_N = 8;
 
 struct TileSched {
-  int n_mt, n_nt, slots, first, end, nb, nn;
+  int n_mt, n_nt, slots, first, end, nb, nn, lmask;
   __device__ __forceinline__ void init(int n_mt_, int n_nt_) {
     n_mt = n_mt_;
     n_nt = n_nt_;
     slots = int(gridDim.x) >> 3;
     const int x = blockIdx.x & 7;
+    // With a single row of tiles no two workgroups share an operand tile,
+    // and the ~32 workgroups of an XCD would otherwise read the same k-slice
+    // of their W tiles at the same moment (rows one leading dimension apart,
+    // which the L2 serves through few of its channels).  Staggering their
+    // leaf order by up to 4 positions spreads them.  With several m-tiles
+    // the workgroups of an XCD share operands and run in step.
+    lmask = n_mt == 1 ? int(blockIdx.x >> 3) & 3 : 0;
     if (n_nt >= 4 * GROUP_N) {
       nb = int(int64_t(n_nt) * x / 8);
       nn = int(int64_t(n_nt) * (x + 1) / 8) - nb;
@@ -240,7 +247,9 @@ struct DenseOperands {
 // offset is off[g & 1] + 16 g ld: two VGPRs per operand and a scalar stride.
 // Rows past the tile's last row have offsets past the resource's size and
 // read as zero.
-template <int MI>
+// WAUX: cache policy of the W loads (0, or 2 = non-temporal when every W
+// tile is read by one workgroup only).
+template <int MI, int WAUX = 0>
 struct Loader {
   using G = Geo<MI>;
   DenseOperands op;
@@ -265,34 +274,33 @@ struct Loader {
     sw = uint32_t(op.ldw * 16);
   }
 
-  // Part P of the DMA of k-tile kt of the current tile into the ring buffer
-  // `stage`: 0 and 1 = the two halves of this wave's A segments, 2 = its W
-  // segments (so the issue can be spread between MFMA steps).
-  template <int P>
-  __device__ __forceinline__ void issue(char* stage, int kt) const {
+  // DMA instruction J (0 <= J < VM_PER_STAGE) of k-tile kt of the current
+  // tile into the ring buffer `stage`: J < A_SEG = this wave's A segment J,
+  // else its W segment J - A_SEG.  One instruction at a time, so that the
+  // issue can be spread evenly between the MFMAs of a stage.
+  template <int J>
+  __device__ __forceinline__ void seg(char* stage, int kt) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // scalar: M0 arithmetic
     const int so = kt * (BK * 2);
-    if constexpr (P < 2) {
-      constexpr int H = G::A_SEG / 2;
-#pragma unroll
-      for (int j = P * H; j < (P + 1) * H; ++j) {
-        const int g = wave * G::A_SEG + j;   // A_SEG is even: g & 1 == j & 1
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LDS_AS void*)(stage + g * 1024), 16,
-                                                 oa[j & 1] + uint32_t(g) * sa, so, 0, 0);
-      }
+    if constexpr (J < G::A_SEG) {
+      const int g = wave * G::A_SEG + J;   // A_SEG is even: g & 1 == J & 1
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LDS_AS void*)(stage + g * 1024), 16,
+                                               oa[J & 1] + uint32_t(g) * sa, so, 0, 0);
     } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int g = wave * 4 + j;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (LDS_AS void*)(stage + G::A_BYTES + g * 1024),
-                                                 16, ow[j & 1] + uint32_t(g) * sw, so, 0, 0);
-      }
+      const int g = wave * 4 + (J - G::A_SEG);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (LDS_AS void*)(stage + G::A_BYTES + g * 1024), 16,
+                                               ow[J & 1] + uint32_t(g) * sw, so, 0, WAUX);
+    }
+  }
+  template <int J0, int D>
+  __device__ __forceinline__ void segs(char* stage, int kt) const {
+    if constexpr (D > 0) {
+      seg<J0>(stage, kt);
+      segs<J0 + 1, D - 1>(stage, kt);
     }
   }
   __device__ __forceinline__ void issue_all(char* stage, int kt) const {
-    issue<0>(stage, kt);
-    issue<1>(stage, kt);
-    issue<2>(stage, kt);
+    segs<0, G::VM_PER_STAGE>(stage, kt);
   }
 };
 
@@ -325,23 +333,15 @@ __device__ __forceinline__ void mfma_step(AccT<MI>& c, const Frags<MI>& f) {
   }
 }
 
-// Scheduling hint for one step: the MI + 2 fragment reads of the next step
-// interleaved with the 2 MI MFMAs of this one.
-template <int MI>
+// Scheduling hint for one step: the 2 MI MFMAs of this step, with the MI + 2
+// fragment reads of a later step and D DMA instructions spread between them.
+template <int MI, int D>
 __device__ __forceinline__ void sched_step() {
-  if constexpr (MI == 2) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-  } else {
 #pragma unroll
-    for (int t = 0; t < MI + 2; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * MI - (MI + 2), 0);
+  for (int t = 0; t < 2 * MI; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (t < MI + 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (((t + 1) * D) / (2 * MI) > (t * D) / (2 * MI)) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
   }
 }
 
@@ -380,13 +380,17 @@ __device__ __forceinline__ void leaf_tree_persistent(Ld& ld, int ktiles, const T
   const int kpl = ktiles >> LG;
   const int total = n_my * ktiles;
 
-  // DMA cursor: tile l_tile, leaf position l_pos, k-tile kt.  Odd tiles of
-  // this workgroup visit their leaves last to first, so that a new round of
-  // tiles starts on the k-slices the previous round used last (still in L2).
-  // The pending-stack fold then meets every pair of subtrees in swapped
-  // operand order, which FP32 addition does not see (a + b == b + a bit for
-  // bit), so the tree value is the same.
-  int l_tile = 0, l_pos = 0, l_j = 0, kt = 0, issued = 0;
+  // DMA cursor: tile l_tile, leaf position l_pos, k-tile kt.  Position p of
+  // a tile visits leaf p ^ m with m = m0 (the schedule's stagger) on even
+  // tiles and m0 ^ (L - 1) on odd ones, so that a new round of tiles starts
+  // on the k-slice the previous round used last (still in L2).  XOR with a
+  // constant maps every aligned block of 2^k positions onto an aligned block
+  // of 2^k leaves, so the pending-stack fold, which combines positions, still
+  // combines exactly the sibling subtrees of the balanced adjacent-pair tree;
+  // it meets some pairs in swapped operand order, which FP32 addition does
+  // not see (a + b == b + a bit for bit), so the tree value is the same.
+  const int m0 = __builtin_amdgcn_readfirstlane(ts.lmask & (L - 1));
+  int l_tile = 0, l_pos = 0, l_j = 0, kt = m0 * kpl, issued = 0;
   {
     int mt, nt;
     ts.coords(0, mt, nt);
@@ -404,7 +408,7 @@ __device__ __forceinline__ void leaf_tree_persistent(Ld& ld, int ktiles, const T
         ts.coords(l_tile, mt, nt);
         ld.setup(mt, nt);
       }
-      kt = ((l_tile & 1) ? (L - 1 - l_pos) : l_pos) * kpl;
+      kt = (l_pos ^ m0 ^ ((l_tile & 1) ? (L - 1) : 0)) * kpl;
     }
   };
 #pragma unroll
@@ -422,30 +426,35 @@ __device__ __forceinline__ void leaf_tree_persistent(Ld& ld, int ktiles, const T
   fa.read(F0, smem, 0);
   fa.read(F1, smem, 1);
 
+  // DMA instructions per k-step: the stage's VM_PER_STAGE spread over its 4 steps.
+  constexpr int VM = G::VM_PER_STAGE;
+  constexpr int D0 = VM / 4, D1 = VM / 2 - VM / 4, D2 = (3 * VM) / 4 - VM / 2, D3 = VM - (3 * VM) / 4;
   // vmcnt once stage q+1 has landed, at the mid-stage wait of stage q: the
-  // later stages q+2 .. q+STAGES-2 and the A part of stage q+STAGES-1.
-  constexpr int MID_WAIT = G::VM_PER_STAGE * (STAGES - 3) + G::A_SEG;
+  // later stages q+2 .. q+STAGES-2 and this stage's first D0 + D1 instructions.
+  constexpr int MID_WAIT = VM * (STAGES - 3) + D0 + D1;
   auto stage = [&](AccT<MI>& cur, auto first) {
     const char* st = smem + off_q;
     char* pb = smem + off_pf;
     const uint32_t off_n = off_q + G::STAGE == RING ? 0u : off_q + uint32_t(G::STAGE);
     fa.read(F2, st, 2);
     mfma_step<decltype(first)::value>(cur, F0);
-    ld.template issue<0>(pb, kt);
-    sched_step<MI>();
+    ld.template segs<0, D0>(pb, kt);
+    sched_step<MI, D0>();
     fa.read(F3, st, 3);
     mfma_step<false>(cur, F1);
-    ld.template issue<1>(pb, kt);
-    sched_step<MI>();
+    ld.template segs<D0, D1>(pb, kt);
+    sched_step<MI, D1>();
     wait_vmcnt_lgkm0<MID_WAIT>();   // stage q+1 landed; this wave's reads of stage q returned
     bar();                          // every wave is done with stage q's buffer
     fa.read(F0, smem + off_n, 0);
     mfma_step<false>(cur, F2);
-    ld.template issue<2>(pb, kt);
-    advance();
-    sched_step<MI>();
+    ld.template segs<D0 + D1, D2>(pb, kt);
+    sched_step<MI, D2>();
     fa.read(F1, smem + off_n, 1);
     mfma_step<false>(cur, F3);
+    ld.template segs<D0 + D1 + D2, D3>(pb, kt);
+    sched_step<MI, D3>();
+    advance();
     off_pf = off_q;
     off_q = off_n;
   };
@@ -580,13 +589,25 @@ __device__ __forceinline__ void LogprobEpi<MI>::operator()(const AccT<MI>& acc, 
 #pragma unroll
       for (int v = 0; v < 16; ++v)
         P[tr_index((v >> 2) * 8 + h * 4 + (v & 3), j * 32 + r)] = acc.c[i][j][v];
-    asm volatile("" ::: "memory");
+    {
+      uint32_t ad[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float4 t4 = *reinterpret_cast<const float4*>(P + r * 64 + (((8 * h + k) ^ (r & 15)) << 2));
-      x[i][4 * k + 0] = t4.x; x[i][4 * k + 1] = t4.y; x[i][4 * k + 2] = t4.z; x[i][4 * k + 3] = t4.w;
+      for (int k = 0; k < 8; ++k)
+        ad[k] = uint32_t(reinterpret_cast<uintptr_t>(P + r * 64 + (((8 * h + k) ^ (r & 15)) << 2)));
+      float4 t0, t1, t2, t3, t4, t5, t6, t7;
+      asm volatile(
+          "ds_read_b128 %0, %8\n ds_read_b128 %1, %9\n ds_read_b128 %2, %10\n ds_read_b128 %3, %11\n"
+          "ds_read_b128 %4, %12\n ds_read_b128 %5, %13\n ds_read_b128 %6, %14\n ds_read_b128 %7, %15\n"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
+          : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
+          : "memory");
+      const float4 tt[8] = {t0, t1, t2, t3, t4, t5, t6, t7};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        x[i][4 * k + 0] = tt[k].x; x[i][4 * k + 1] = tt[k].y; x[i][4 * k + 2] = tt[k].z; x[i][4 * k + 3] = tt[k].w;
+      }
     }
-    asm volatile("" ::: "memory");
     float mx = -__builtin_inff();
     if (full) {
 #pragma unroll
@@ -641,14 +662,14 @@ __device__ __forceinline__ void LogprobEpi<MI>::operator()(const AccT<MI>& acc, 
   lds_sync();   // the partner's slots are read before the buffer is refilled
 }
 
-template <int LG, int MI>
+template <int LG, int MI, int WAUX>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void logprob_tile_kernel(DenseOperands op, int ktiles, int n_mt, int n_nt, float2* __restrict__ part) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   TileSched ts;
   ts.init(n_mt, n_nt);
   LogprobEpi<MI> epi{part, op.M, op.N, n_nt};
-  Loader<MI> ld{op};
+  Loader<MI, WAUX> ld{op};
   leaf_tree_persistent<LG, MI>(ld, ktiles, ts, epi, smem);
 }
 
@@ -957,31 +978,29 @@ struct MoeLoader {
     }
   }
 
-  template <int P>
-  __device__ __forceinline__ void issue(char* stage, int kt) const {
+  template <int J>
+  __device__ __forceinline__ void seg(char* stage, int kt) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int so = kt * (BK * 2);
-    if constexpr (P < 2) {
-      constexpr int H = G::A_SEG / 2;
-#pragma unroll
-      for (int j = P * H; j < (P + 1) * H; ++j) {
-        const int g = wave * G::A_SEG + j;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LDS_AS void*)(stage + g * 1024), 16,
-                                                 uint32_t(oa[j]), so, 0, 0);
-      }
+    if constexpr (J < G::A_SEG) {
+      const int g = wave * G::A_SEG + J;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LDS_AS void*)(stage + g * 1024), 16,
+                                               uint32_t(oa[J]), so, 0, 0);
     } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int g = wave * 4 + j;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (LDS_AS void*)(stage + G::A_BYTES + g * 1024),
-                                                 16, ow[j & 1] + uint32_t(g) * sw, so, 0, 0);
-      }
+      const int g = wave * 4 + (J - G::A_SEG);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (LDS_AS void*)(stage + G::A_BYTES + g * 1024), 16,
+                                               ow[J & 1] + uint32_t(g) * sw, so, 0, 0);
+    }
+  }
+  template <int J0, int D>
+  __device__ __forceinline__ void segs(char* stage, int kt) const {
+    if constexpr (D > 0) {
+      seg<J0>(stage, kt);
+      segs<J0 + 1, D - 1>(stage, kt);
     }
   }
   __device__ __forceinline__ void issue_all(char* stage, int kt) const {
-    issue<0>(stage, kt);
-    issue<1>(stage, kt);
-    issue<2>(stage, kt);
+    segs<0, G::VM_PER_STAGE>(stage, kt);
   }
 };
 
@@ -1120,8 +1139,14 @@ hipError_t launch_logprob_mi(const LogprobLaunch& p, hipStream_t s) {
                      p.xleaf, p.M, p.K, p.V);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((logprob_tile_kernel<LG, MI>), dim3(persistent_grid(int64_t(n_mt) * n_vt)),
-                     dim3(NTHREADS), 0, s, op, int(p.K / BK), n_mt, n_vt, part);
+  // One row of tiles (decode-sized batches): each W tile is read once, so its
+  // loads bypass the caches' retention (non-temporal).
+  if (n_mt == 1)
+    hipLaunchKernelGGL((logprob_tile_kernel<LG, MI, 2>), dim3(persistent_grid(int64_t(n_mt) * n_vt)),
+                       dim3(NTHREADS), 0, s, op, int(p.K / BK), n_mt, n_vt, part);
+  else
+    hipLaunchKernelGGL((logprob_tile_kernel<LG, MI, 0>), dim3(persistent_grid(int64_t(n_mt) * n_vt)),
+                       dim3(NTHREADS), 0, s, op, int(p.K / BK), n_mt, n_vt, part);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   int q = 0;
