@@ -839,73 +839,105 @@ __global__ __launch_bounds__(256) void moe_hist_kernel(const int32_t* __restrict
   for (int e = threadIdx.x; e < n_experts; e += 256) hist[int64_t(blockIdx.x) * n_experts + e] = h[e];
 }
 
-// One workgroup: first[c][e] = first row of chunk c inside expert e's list
-// (exclusive scan of hist over chunks; four threads per expert, each owning a
-// quarter of the chunks); counts, first row of each expert in Y, and the work
-// items (expert, m-tile of bm rows, rows of the expert, first row).
-__global__ __launch_bounds__(256) void moe_plan_kernel(const int32_t* __restrict__ hist,
-                                                       int32_t* __restrict__ first, int n_chunks,
-                                                       int n_experts, int bm,
-                                                       int32_t* __restrict__ counts,
-                                                       int32_t* __restrict__ prefix,
-                                                       int4* __restrict__ items,
-                                                       int32_t* __restrict__ n_items) {
-  __shared__ int part[256];
+// One workgroup of 1024: first[c][e] = first row of chunk c inside expert
+// e's list (exclusive scan of hist over chunks), counts, the first row of
+// each expert in Y (exclusive scan over experts) and the work items (expert,
+// m-tile of bm rows, rows of the expert, first row), numbered in ascending
+// expert order.  G = PLAN_THREADS / 64 threads share an expert (fewer when
+// there are more than 64 experts), each owning a contiguous run of chunks
+// whose counts it keeps in registers (the first PLAN_U; the rest of a longer
+// run is read twice).
+constexpr int PLAN_THREADS = 1024, PLAN_U = 8;
+
+// Exclusive prefix sum over the workgroup's threads in thread order: a scan
+// inside each wave, then over the wave totals.  buf holds >= 16 ints.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* buf) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) {
+    const int o = __shfl_up(x, d);
+    if (lane >= d) x += o;
+  }
+  if (lane == 63) buf[wave] = x;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += buf[w];
+  __syncthreads();
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(PLAN_THREADS) void moe_plan_kernel(const int32_t* __restrict__ hist,
+                                                                int32_t* __restrict__ first, int n_chunks,
+                                                                int n_experts, int bm,
+                                                                int32_t* __restrict__ counts,
+                                                                int32_t* __restrict__ prefix,
+                                                                int4* __restrict__ items,
+                                                                int32_t* __restrict__ n_items) {
   __shared__ int cnt[kMaxExperts];
-  const int q = threadIdx.x & 3;
-  const int per = (n_chunks + 3) >> 2;
+  __shared__ int buf[PLAN_THREADS];
+  int G = PLAN_THREADS / 64;
+  while (G > 1 && G * n_experts > PLAN_THREADS) G >>= 1;
+  const int per_pass = PLAN_THREADS / G;   // experts per pass
+  // Thread t: expert e0 + t % per_pass (consecutive lanes, consecutive
+  // experts: coalesced), chunk run q = t / per_pass.
+  const int q = int(threadIdx.x) / per_pass, el = int(threadIdx.x) % per_pass;
+  const int per = (n_chunks + G - 1) / G;
   const int c0 = q * per, c1 = min(n_chunks, c0 + per);
-  for (int e0 = 0; e0 < n_experts; e0 += 64) {
-    const int e = e0 + (threadIdx.x >> 2);
+  for (int e0 = 0; e0 < n_experts; e0 += per_pass) {
+    const int e = e0 + el;
+    int v[PLAN_U];
     int sum = 0;
     if (e < n_experts) {
-      int c = c0;
-      for (; c + 8 <= c1; c += 8) {   // eight loads in flight
-        int v[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = hist[int64_t(c + k) * n_experts + e];
+      for (int k = 0; k < PLAN_U; ++k) v[k] = c0 + k < c1 ? hist[int64_t(c0 + k) * n_experts + e] : 0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) sum += v[k];
-      }
-      for (; c < c1; ++c) sum += hist[int64_t(c) * n_experts + e];
+      for (int k = 0; k < PLAN_U; ++k) sum += v[k];
+      for (int c = c0 + PLAN_U; c < c1; ++c) sum += hist[int64_t(c) * n_experts + e];
     }
-    part[threadIdx.x] = sum;
+    buf[threadIdx.x] = sum;
     __syncthreads();
     if (e < n_experts) {
       int acc = 0;
-      for (int k = 0; k < q; ++k) acc += part[(threadIdx.x & ~3) + k];
-      int c = c0;
-      for (; c + 8 <= c1; c += 8) {
-        int v[8];
+      for (int k = 0; k < q; ++k) acc += buf[k * per_pass + el];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = hist[int64_t(c + k) * n_experts + e];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          first[int64_t(c + k) * n_experts + e] = acc;
+      for (int k = 0; k < PLAN_U; ++k)
+        if (c0 + k < c1) {
+          first[int64_t(c0 + k) * n_experts + e] = acc;
           acc += v[k];
         }
-      }
-      for (; c < c1; ++c) {
+      for (int c = c0 + PLAN_U; c < c1; ++c) {
         first[int64_t(c) * n_experts + e] = acc;
         acc += hist[int64_t(c) * n_experts + e];
       }
-      if (q == 3) {
+      if (q == G - 1) {
         cnt[e] = acc;
         counts[e] = acc;
       }
     }
     __syncthreads();
   }
-  if (threadIdx.x != 0) return;
-  int acc = 0, k = 0;
-  for (int e = 0; e < n_experts; ++e) {
-    const int c = cnt[e];
-    prefix[e] = acc;
-    for (int mt = 0; mt * bm < c; ++mt) items[k++] = make_int4(e, mt, c, acc);
-    acc += c;
+  // Exclusive scans over experts of rows and of work items; thread t owns
+  // experts [t k, (t + 1) k).
+  const int k = (n_experts + PLAN_THREADS - 1) / PLAN_THREADS;
+  const int ea = min(n_experts, int(threadIdx.x) * k), eb = min(n_experts, ea + k);
+  int rows = 0, nit = 0;
+  for (int e = ea; e < eb; ++e) {
+    rows += cnt[e];
+    nit += (cnt[e] + bm - 1) / bm;
   }
-  prefix[n_experts] = acc;
-  *n_items = k;
+  int row0 = block_exclusive_scan(rows, buf);
+  int it0 = block_exclusive_scan(nit, buf);
+  for (int e = ea; e < eb; ++e) {
+    const int c = cnt[e];
+    prefix[e] = row0;
+    for (int mt = 0; mt * bm < c; ++mt) items[it0++] = make_int4(e, mt, c, row0);
+    row0 += c;
+  }
+  if (threadIdx.x == PLAN_THREADS - 1) {
+    prefix[n_experts] = row0;
+    *n_items = it0;
+  }
 }
 
 // Chunk c: each pair's row = first row of (c, e) + pairs of the chunk before
@@ -1054,36 +1086,58 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* __restr
                                                           int topk, int n_experts) {
   __shared__ int64_t rows[kMaxTopk];
   __shared__ float wts[kMaxTopk];
+  __shared__ int ex[kMaxTopk];
   __shared__ int bad;
   const int64_t t = blockIdx.x;
-  if (threadIdx.x == 0) {
-    int order[kMaxTopk];
-    int b = 0;
-    for (int s = 0; s < topk; ++s) {
-      const int e = topk_ids[t * topk + s];
-      b |= e < 0 || e >= n_experts;
-      int j = s;
-      while (j > 0 && topk_ids[t * topk + order[j - 1]] > e) {   // stable insertion
-        order[j] = order[j - 1];
-        --j;
-      }
-      order[j] = s;
-    }
-    bad = b;
+  const int s = threadIdx.x;
+  // Thread s < topk owns slot s: its expert, weight and Y row are loaded in
+  // parallel; its rank in (expert id, slot) order places it.
+  int e = 0;
+  float w = 0.0f;
+  if (s < topk) {
+    e = topk_ids[t * topk + s];
+    w = topk_w[t * topk + s];
+    ex[s] = e;
+  }
+  if (s == 0) bad = 0;
+  __syncthreads();
+  if (s < topk) {
+    const bool ok = e >= 0 && e < n_experts;
+    if (!ok) bad = 1;
+    int rank = 0;
     for (int k = 0; k < topk; ++k) {
-      const int64_t p = t * topk + order[k];
-      rows[k] = b ? 0 : (int64_t(prefix[topk_ids[p]]) + pos[p]) * N;
-      wts[k] = topk_w[p];
+      const int ek = ex[k];
+      rank += ek < e || (ek == e && k < s);
     }
+    rows[rank] = ok ? (int64_t(prefix[e]) + pos[t * topk + s]) * N : 0;
+    wts[rank] = w;
   }
   __syncthreads();
-  for (int64_t n = threadIdx.x; n < N; n += 256) {
-    float acc = 0.0f;
-    for (int k = 0; k < topk; ++k) {
-      const float term = wts[k] * Y[rows[k] + n];
-      acc = acc + term;
+  const float nan = __builtin_nanf("");
+  // Rows of Y (the workspace) and of out 16-byte aligned: four columns per thread.
+  if ((N & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+    const int64_t N4 = N >> 2;
+    for (int64_t n = s; n < N4; n += 256) {
+      float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      for (int k = 0; k < topk; ++k) {
+        const float wk = wts[k];
+        const float4 y = reinterpret_cast<const float4*>(Y + rows[k])[n];
+        acc.x = acc.x + wk * y.x;
+        acc.y = acc.y + wk * y.y;
+        acc.z = acc.z + wk * y.z;
+        acc.w = acc.w + wk * y.w;
+      }
+      reinterpret_cast<float4*>(out + t * N)[n] = bad ? make_float4(nan, nan, nan, nan) : acc;
     }
-    out[t * N + n] = bad ? __builtin_nanf("") : acc;
+  } else {
+    for (int64_t n = s; n < N; n += 256) {
+      float acc = 0.0f;
+      for (int k = 0; k < topk; ++k) {
+        const float term = wts[k] * Y[rows[k] + n];
+        acc = acc + term;
+      }
+      out[t * N + n] = bad ? nan : acc;
+    }
   }
 }
 
@@ -1172,7 +1226,7 @@ hipError_t launch_moe_mi(const MoeLaunch& p, hipStream_t s) {
                      n_pairs, p.n_experts, p.hist);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(256), 0, s, p.hist, p.first, n_chunks, p.n_experts,
+  hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, s, p.hist, p.first, n_chunks, p.n_experts,
                      64 * MI, p.counts, p.prefix, reinterpret_cast<int4*>(p.items), p.n_items);
   err = hipGetLastError();
   if (err != hipSuccess) return err;

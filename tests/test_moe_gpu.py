@@ -104,6 +104,28 @@ def test_moe_combine_order_matches_emulator(gpu_lib):
     assert np.any(slot != ref), "slot order should differ somewhere (power of the check)"
 
 
+@pytest.mark.parametrize("N", [132, 130])
+def test_moe_repeated_expert_keeps_slot_order(gpu_lib, N):
+    """A token may route two slots to one expert: equal ids combine in slot order.
+
+    Exact expert outputs and float32 gates make the combine the only rounding;
+    N = 132 takes the four-column path of the combine, N = 130 the scalar one.
+    """
+    rng = np.random.default_rng(60 + N)
+    T, E, K, topk = 97, 6, 512, 8
+    H = wl.integer_bf16(rng, (T, K), -2, 2)
+    We = wl.integer_bf16(rng, (E, N, K), -2, 2)
+    ids = rng.integers(0, E, size=(T, topk)).astype(np.int32)   # repeats within a token
+    assert any(len(set(r)) < topk for r in ids.tolist())
+    w = rng.random((T, topk)).astype(np.float32)
+    say(f"moe repeated experts N={N}")
+    out = _run(gpu_lib, H, We, ids, w, 8)
+    Y = np.stack([oracle.contraction_ref(H, We[e]) for e in range(E)])
+    Yp = Y[ids, np.arange(T)[:, None]].astype(np.float32)
+    ref = oracle.moe_combine_f32(Yp, ids, w)
+    assert_bitwise(out, torch.from_numpy(ref), f"repeated experts, N={N}")
+
+
 def test_moe_invalid_expert_gives_nan_for_that_token(gpu_lib):
     rng = np.random.default_rng(7)
     T, E, N, K, topk = 10, 4, 64, 512, 2
