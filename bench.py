@@ -160,13 +160,26 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    copy_gbs = None
+    if args.phase == "all":
+        # Attainable HBM rate on this machine: a 1 GiB device-to-device copy (bytes read + written).
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        copy_ms, _ = timed(lambda: dst.copy_(src), 10, 2)
+        copy_gbs = 2.0 * (1 << 30) / (copy_ms / 1e3) / 1e9
+        log(f"device copy: {copy_gbs:.0f} GB/s (read + write)")
+        del src, dst
+
     tok_s = ms_step = tflops = None
+    spread = None
     flops = 2.0 * M * K * V
     if args.phase in ("all", "prefill"):
         ms_step, per_call = timed(lambda: tig.tig_logprob_gather(Hd, Wd, idd, lp, lse, L, ws),
                                   args.steps, args.warmup)
         tok_s = M / (ms_step / 1e3)
         tflops = flops / (float(np.mean(per_call)) / 1e3) / 1e12
+        spread = {"min_ms": float(np.min(per_call)), "median_ms": float(np.median(per_call)),
+                  "max_ms": float(np.max(per_call))}
         log(f"prefill: {ms_step:.3f} ms/step, {tok_s:.4g} tok/s, {tflops:.1f} TFLOP/s "
             f"(min {min(per_call):.3f} ms, max {max(per_call):.3f} ms)")
 
@@ -183,7 +196,8 @@ def main():
         log(f"decode M={Md}: {dec_ms * 1e3:.1f} us/step, {r['achieved']:.0f} GB/s")
         decode = {"tokens": Md, "us_per_step": dec_ms * 1e3, "tokens_per_s": Md / (dec_ms / 1e3),
                   "achieved_GBs": r["achieved"], "peak_GBs": PEAK_HBM_GBS, "hbm_frac": r["frac"],
-                  "algorithmic_bytes": dec_bytes, "roofline": r}
+                  "algorithmic_bytes": dec_bytes, "roofline": r,
+                  "frac_of_device_copy": None if copy_gbs is None else r["achieved"] / copy_gbs}
 
     cpu = None
     if not args.no_cpu_baseline and args.phase == "all":
@@ -270,7 +284,8 @@ def main():
             "frac": tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic("lmhead_prefill")},
         "tree_gemm": None if tflops is None else {
             "tflops": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
-            "shape": f"M={M} K={K} N={V} leaves={L}"},
+            "shape": f"M={M} K={K} N={V} leaves={L}", "spread": spread},
+        "device_copy_GBs": copy_gbs,
         "decode": decode,
         "linear": linear,
         "moe": moe,
