@@ -107,7 +107,12 @@ tig_status tig_logprob_gather(const void* H, const void* W, const int64_t* ids,
                               void* workspace, size_t workspace_bytes,
                               hipStream_t stream);
 
-/* Workspace bytes tig_logprob_gather needs for these sizes (written to *bytes). */
+/*
+ * Workspace bytes tig_logprob_gather needs for these sizes (written to *bytes):
+ * 8 bytes per row per 128-column vocabulary tile, 4 per row per leaf, and at
+ * 16 leaves with 192-row tiles (M above 128 where that needs fewer tiles) a
+ * further 24 MiB where each tile parks the root of its first 8 leaves.
+ */
 tig_status tig_logprob_workspace_bytes(int64_t M, int64_t K, int64_t n_vocab,
                                        int32_t leaves, size_t* bytes);
 

@@ -242,13 +242,16 @@ tig_status tig_logprob_gather(const void* H, const void* W, const int64_t* ids, 
     return fail(TIG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : size_t(0));
   if (!aligned(workspace, 256)) return fail(TIG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  const int bm = tig::block_m_for(M, log2i(leaves));
+  const int bm = tig::logprob_block_m_for(M, log2i(leaves));
   if ((s = check_span("H tile", bm, K)) != TIG_OK) return s;
   if (tig::cdiv(M, bm) * tig::cdiv(n_vocab, tig::kBlockN) >= (int64_t(1) << 31) - 8)
     return fail(TIG_ERR_UNSUPPORTED, "too many output tiles");
   char* ws = static_cast<char*>(workspace);
+  const size_t xoff = tig::logprob_partials_bytes(M, n_vocab);
+  const size_t soff = xoff + tig::logprob_xleaf_bytes(M, leaves);
   tig::LogprobLaunch p{H, W, ids, logprob_out, lse_out, M, K, n_vocab, log2i(leaves), ws,
-                       reinterpret_cast<float*>(ws + tig::logprob_partials_bytes(M, n_vocab))};
+                       reinterpret_cast<float*>(ws + xoff),
+                       tig::logprob_spill_bytes(M, leaves) ? reinterpret_cast<float*>(ws + soff) : nullptr};
   const hipError_t e = tig::launch_logprob(p, stream);
   if (e != hipSuccess) return fail(TIG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();

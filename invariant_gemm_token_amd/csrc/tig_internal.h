@@ -23,6 +23,17 @@ inline int block_m_for(int64_t M, int leaves_log2) {
   if (block_m_for_log2(leaves_log2) == 192 && (M + 191) / 192 < (M + 127) / 128) return 192;
   return 128;
 }
+// The logprob path also takes 192-row tiles at 16 leaves: it keeps the left
+// half of the leaf tree (the root of leaves 0..7) in global scratch instead
+// of registers while the right half streams (see kSpillGrid).
+inline int logprob_block_m_for(int64_t M, int leaves_log2) {
+  (void)leaves_log2;
+  return (M + 191) / 192 < (M + 127) / 128 ? 192 : 128;
+}
+// Scratch for that left half: one 192 x 128 FP32 tile per workgroup of a
+// grid of at most kSpillGrid workgroups.
+constexpr int kSpillGrid = 256;
+constexpr size_t kSpillBytesPerGroup = 256 * 96 * 4;
 constexpr int kBlockN = 128;   // also the vocabulary tile of the log-softmax
 constexpr int kBlockK = 64;
 constexpr int kMfmaM = 32, kMfmaN = 32, kMfmaK = 16;
@@ -50,6 +61,7 @@ struct LogprobLaunch {
   int leaves_log2;
   void* partials;   // float2 [M][n_vtiles]
   float* xleaf;     // float [M][leaves]
+  float* spill;     // leaves == 16 with 192-row tiles: kSpillGrid * kSpillBytesPerGroup bytes
 };
 
 struct MoeLaunch {
@@ -77,9 +89,14 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t logprob_partials_bytes(int64_t M, int64_t V) {
   return align256(size_t(M) * size_t(cdiv(V, kBlockN)) * 8);
 }
-// partials float2 [M][vocabulary tiles], then the picked logit's leaf values float [M][leaves]
+inline size_t logprob_xleaf_bytes(int64_t M, int leaves) { return align256(size_t(M) * size_t(leaves) * 4); }
+inline size_t logprob_spill_bytes(int64_t M, int leaves) {
+  return leaves == 16 && logprob_block_m_for(M, 4) == 192 ? size_t(kSpillGrid) * kSpillBytesPerGroup : 0;
+}
+// partials float2 [M][vocabulary tiles], then the picked logit's leaf values float [M][leaves],
+// then the spill scratch of 16-leaf launches with 192-row tiles
 inline size_t logprob_ws_bytes(int64_t M, int64_t V, int leaves) {
-  return logprob_partials_bytes(M, V) + align256(size_t(M) * size_t(leaves) * 4);
+  return logprob_partials_bytes(M, V) + logprob_xleaf_bytes(M, leaves) + logprob_spill_bytes(M, leaves);
 }
 // MoE workspace, in this order (each part 256-byte aligned).
 inline int64_t moe_max_items(int64_t T, int topk, int n_experts) {

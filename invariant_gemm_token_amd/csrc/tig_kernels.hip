@@ -459,14 +459,25 @@ __device__ __forceinline__ void leaf_tree_persistent(Ld& ld, int ktiles, const T
     off_q = off_n;
   };
 
+  // With Epi::kSplitTop the top level of the tree is not held in registers:
+  // each half of the positions is folded on its own, the first half's root
+  // goes to the epilogue's scratch (epi.spill) and the epilogue adds it to
+  // the second half's root, the same last addition of the same tree.
+  constexpr bool SPLIT = Epi::kSplitTop && LG > 0;
+  constexpr int PLG = SPLIT ? LG - 1 : LG;   // tree levels held in registers
   for (int ti = 0; ti < n_my; ++ti) {
-    AccT<MI> pend[LG > 0 ? LG : 1];
+    AccT<MI> pend[PLG > 0 ? PLG : 1];
     AccT<MI> cur;
 #pragma unroll 1
-    for (int pos = 0; pos < L; ++pos) {   // leaf pos, or L-1-pos on odd tiles
+    for (int pos = 0; pos < L; ++pos) {   // sequence position; leaf pos ^ m
       stage(cur, std::true_type{});
       for (int j = 1; j < kpl; ++j) stage(cur, std::false_type{});
-      tree_fold<0, LG>(pend, cur, pos);
+      if constexpr (SPLIT) {
+        tree_fold<0, PLG>(pend, cur, pos & ((1 << PLG) - 1));
+        if (pos == (L >> 1) - 1) epi.spill(cur);
+      } else {
+        tree_fold<0, LG>(pend, cur, pos);
+      }
     }
     int mt, nt;
     ts.coords(ti, mt, nt);
@@ -478,7 +489,9 @@ __device__ __forceinline__ void leaf_tree_persistent(Ld& ld, int ktiles, const T
 // Epilogue: store the tile (FP32, or bf16 by RNE).
 template <int EPI, int MI>
 struct StoreEpi {
+  static constexpr bool kSplitTop = false;
   void* C; int64_t ldc; int64_t M, N;
+  __device__ __forceinline__ void spill(const AccT<MI>&) const {}
   __device__ __forceinline__ void operator()(const AccT<MI>& acc, int mt, int nt, char*) const;
 };
 
@@ -487,10 +500,68 @@ struct StoreEpi {
 // owns row t/4, columns 32 (t%4)..+31.  (The sampled token's logit is picked
 // by its own kernel: a global load here would have to wait for the whole DMA
 // ring, which returns in order.)
-template <int MI>
+template <int MI, bool SPLIT = false>
 struct LogprobEpi {
+  static constexpr bool kSplitTop = SPLIT;
   float2* part; int64_t M, V; int n_vt;
-  __device__ __forceinline__ void operator()(const AccT<MI>& acc, int mt, int nt, char* region) const;
+  float* scratch;   // SPLIT: this launch's spill area, kSpillBytesPerGroup bytes per workgroup
+  __device__ __forceinline__ void operator()(AccT<MI>& acc, int mt, int nt, char* region) const;
+  // The left half's root waits in the workgroup's area in the accumulator
+  // layout: 16-byte chunk q of block (i, j) of thread t at byte
+  // (((i 2 + j) 4 + q) 256 + t) 16.
+  __device__ __forceinline__ float* area() const {
+    return scratch + size_t(blockIdx.x) * (kSpillBytesPerGroup / 4);
+  }
+  // One VGPR of lane offset for all 24 stores, the chunk offset in soffset
+  // (always inside the area).
+  __device__ __forceinline__ void spill(const AccT<MI>& c) const {
+    if constexpr (SPLIT) {
+      const __amdgpu_buffer_rsrc_t r = make_rsrc(area(), uint32_t(kSpillBytesPerGroup));
+      const int voff = opaque_tid() * 16;
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            // Each element through a scalar first: __builtin_bit_cast applied to a
+            // vector-element expression directly reads element 0 with this compiler.
+            i32x4 d;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float f = c.c[i][j][4 * q + u];
+              d[u] = __builtin_bit_cast(int, f);
+            }
+            __builtin_amdgcn_raw_buffer_store_b128(d, r, voff, ((i * 2 + j) * 4 + q) * NTHREADS * 16, 0);
+          }
+    }
+  }
+  // Block (i, j) of the right half's root becomes left + right, the tree's
+  // last addition.  The loads are asm blocks of two, each ending in its own
+  // wait (device scope: read from L2), so that the compiler neither hoists
+  // them nor keeps more than 8 extra registers live.
+  __device__ __forceinline__ void join(int i, int j, f32x16& c) const {
+    const float* b = area() + ((i * 2 + j) * 4) * NTHREADS * 4;   // uniform: scalar base
+    const uint32_t voff = uint32_t(opaque_tid()) * 16;
+#pragma unroll
+    for (int q = 0; q < 4; q += 2) {
+      float4 l0, l1;
+      asm volatile(
+          "global_load_dwordx4 %0, %2, %3 sc1\n global_load_dwordx4 %1, %2, %4 sc1\n s_waitcnt vmcnt(0)"
+          : "=&v"(l0), "=&v"(l1)
+          : "v"(voff), "s"(b + q * NTHREADS * 4), "s"(b + (q + 1) * NTHREADS * 4)
+          : "memory");
+      c[4 * q + 0] = l0.x + c[4 * q + 0];
+      c[4 * q + 1] = l0.y + c[4 * q + 1];
+      c[4 * q + 2] = l0.z + c[4 * q + 2];
+      c[4 * q + 3] = l0.w + c[4 * q + 3];
+      c[4 * q + 4] = l1.x + c[4 * q + 4];
+      c[4 * q + 5] = l1.y + c[4 * q + 5];
+      c[4 * q + 6] = l1.z + c[4 * q + 6];
+      c[4 * q + 7] = l1.w + c[4 * q + 7];
+    }
+  }
+
 };
 
 // ---------------------------------------------------------------------------
@@ -570,9 +641,9 @@ __device__ __forceinline__ int tr_index(int r, int c) {
 // the wave's 64-column max and sum; the two waves of a row pair meet through
 // LDS.  Tree over the 128 columns: ((q0 + q1) + (q2 + q3)), q = 32-column
 // quarters, the same as every other placement of this epilogue.
-template <int MI>
-__device__ __forceinline__ void LogprobEpi<MI>::operator()(const AccT<MI>& acc, int mt, int nt,
-                                                           char* region) const {
+template <int MI, bool SPLIT>
+__device__ __forceinline__ void LogprobEpi<MI, SPLIT>::operator()(AccT<MI>& acc, int mt, int nt,
+                                                                  char* region) const {
   const int tid = opaque_tid(), lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   float* P = reinterpret_cast<float*>(region + wave * 8192);
   const float* Q = reinterpret_cast<const float*>(region + (wave ^ 1) * 8192);
@@ -584,6 +655,10 @@ __device__ __forceinline__ void LogprobEpi<MI>::operator()(const AccT<MI>& acc, 
   float mw[MI];
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
+    if constexpr (SPLIT) {
+      join(i, 0, acc.c[i][0]);
+      join(i, 1, acc.c[i][1]);
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -662,13 +737,16 @@ __device__ __forceinline__ void LogprobEpi<MI>::operator()(const AccT<MI>& acc, 
   lds_sync();   // the partner's slots are read before the buffer is refilled
 }
 
-template <int LG, int MI, int WAUX>
+// SPLIT (16 leaves with 192-row tiles): the left half of the tree waits in
+// `scratch` instead of registers.
+template <int LG, int MI, int WAUX, bool SPLIT>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void logprob_tile_kernel(DenseOperands op, int ktiles, int n_mt, int n_nt, float2* __restrict__ part) {
+void logprob_tile_kernel(DenseOperands op, int ktiles, int n_mt, int n_nt, float2* __restrict__ part,
+                         float* __restrict__ scratch) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   TileSched ts;
   ts.init(n_mt, n_nt);
-  LogprobEpi<MI> epi{part, op.M, op.N, n_nt};
+  LogprobEpi<MI, SPLIT> epi{part, op.M, op.N, n_nt, scratch};
   Loader<MI, WAUX> ld{op};
   leaf_tree_persistent<LG, MI>(ld, ktiles, ts, epi, smem);
 }
@@ -1039,7 +1117,9 @@ struct MoeLoader {
 // Epilogue: the item's rows go to Y rows prefix[e] + mt * BM + r (FP32).
 template <int MI>
 struct MoeStoreEpi {
+  static constexpr bool kSplitTop = false;
   MoeOperands op;
+  __device__ __forceinline__ void spill(const AccT<MI>&) const {}
   __device__ __forceinline__ void operator()(const AccT<MI>& acc, int item, int nt, char*) const {
     const int tid = opaque_tid();
     const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
@@ -1194,13 +1274,18 @@ hipError_t launch_logprob_mi(const LogprobLaunch& p, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // One row of tiles (decode-sized batches): each W tile is read once, so its
-  // loads bypass the caches' retention (non-temporal).
+  // loads bypass the caches' retention (non-temporal).  The split tree's
+  // scratch holds kSpillGrid workgroups.
+  constexpr bool SPLIT = LG == 4 && MI == 3;
+  int grid = persistent_grid(int64_t(n_mt) * n_vt);
+  if (SPLIT && grid > kSpillGrid) grid = kSpillGrid;
+  if (SPLIT && !p.spill) return hipErrorInvalidValue;
   if (n_mt == 1)
-    hipLaunchKernelGGL((logprob_tile_kernel<LG, MI, 2>), dim3(persistent_grid(int64_t(n_mt) * n_vt)),
-                       dim3(NTHREADS), 0, s, op, int(p.K / BK), n_mt, n_vt, part);
+    hipLaunchKernelGGL((logprob_tile_kernel<LG, MI, 2, SPLIT>), dim3(grid), dim3(NTHREADS), 0, s, op,
+                       int(p.K / BK), n_mt, n_vt, part, p.spill);
   else
-    hipLaunchKernelGGL((logprob_tile_kernel<LG, MI, 0>), dim3(persistent_grid(int64_t(n_mt) * n_vt)),
-                       dim3(NTHREADS), 0, s, op, int(p.K / BK), n_mt, n_vt, part);
+    hipLaunchKernelGGL((logprob_tile_kernel<LG, MI, 0, SPLIT>), dim3(grid), dim3(NTHREADS), 0, s, op,
+                       int(p.K / BK), n_mt, n_vt, part, p.spill);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   int q = 0;
@@ -1212,9 +1297,7 @@ hipError_t launch_logprob_mi(const LogprobLaunch& p, hipStream_t s) {
 
 template <int LG>
 hipError_t launch_logprob_lg(const LogprobLaunch& p, hipStream_t s) {
-  if constexpr (block_m_for_log2(LG) == 192) {
-    if (block_m_for(p.M, LG) == 192) return launch_logprob_mi<LG, 3>(p, s);
-  }
+  if (logprob_block_m_for(p.M, LG) == 192) return launch_logprob_mi<LG, 3>(p, s);
   return launch_logprob_mi<LG, 2>(p, s);
 }
 

@@ -90,7 +90,12 @@ def test_workspace_queries():
     # per-row partials of every 128-column vocabulary tile, then the picked logit's leaf values
     b = tig.tig_logprob_workspace_bytes(8192, 4096, 151936, 8)
     assert b == 8192 * 1187 * 8 + 8192 * 8 * 4
-    assert tig.tig_logprob_workspace_bytes(8192, 4096, 151936, 16) == 8192 * 1187 * 8 + 8192 * 16 * 4
+    # 16 leaves on 192-row tiles also keep the left half of each tile's leaf tree in
+    # scratch: one 192 x 128 FP32 tile for each of up to 256 workgroups
+    assert tig.tig_logprob_workspace_bytes(8192, 4096, 151936, 16) == (
+        8192 * 1187 * 8 + 8192 * 16 * 4 + 256 * 192 * 128 * 4)
+    # 128 rows fit one 128-row tile: no scratch
+    assert tig.tig_logprob_workspace_bytes(128, 7168, 129280, 16) == 128 * 1010 * 8 + 128 * 16 * 4
     assert tig.tig_logprob_workspace_bytes(0, 4096, 151936, 8) == 0
     assert tig.tig_logprob_workspace_bytes(3, 512, 1, 8) == 256 + 256
     m = tig.tig_moe_workspace_bytes(4096, 1408, 2048, 64, 8)

@@ -1,10 +1,12 @@
 """Schedule freedom on the GPU: tile height, leaf visiting order, sampled-logit pass.
 
 The dense kernels use 192-row tiles where that needs fewer tiles than 128-row
-ones (and 128 rows otherwise, and always at 16 leaves), and a workgroup that
-runs several tiles visits the leaves of every other tile last to first.  Only
-the schedule may depend on either choice: a row's bits must not [BitRL,
-section 2: one accumulation order for every M].  The sampled token's logit is
+ones (and 128 rows otherwise; tree_gemm always at 16 leaves, while the logprob
+path then keeps the left half of each tile's leaf tree in scratch and adds it
+to the right half's root at the end), and a workgroup that runs several tiles
+visits the leaves of every other tile last to first.  Only the schedule may
+depend on these choices: a row's bits must not [BitRL, section 2: one
+accumulation order for every M].  The sampled token's logit is
 computed by its own pass with the same MFMA k-steps and leaf tree, so logprob
 must equal the FP32 difference of the contraction's own element and the
 log-sum-exp, bit for bit.
@@ -24,8 +26,8 @@ from gpu_util import assert_bitwise, dev_bf16, say
 pytestmark = pytest.mark.gpu
 
 
-def _block_m(M, L):
-    tall = 192 if L <= 8 else 128
+def _block_m(M, L, logprob=False):
+    tall = 192 if L <= 8 or logprob else 128
     return 192 if tall == 192 and -(-M // 192) < -(-M // 128) else 128
 
 
@@ -44,12 +46,12 @@ def test_logprob_rows_identical_across_tile_heights(gpu_lib, L):
     full_lp, full_lse = gpu_lib.logprob_gather(H, W, ids, L)
     heights = set()
     for a, b in SLICES:
-        heights.add(_block_m(b - a, L))
-        say(f"logprob L={L} rows [{a}, {b}) tile rows {_block_m(b - a, L)}")
+        heights.add(_block_m(b - a, L, logprob=True))
+        say(f"logprob L={L} rows [{a}, {b}) tile rows {_block_m(b - a, L, logprob=True)}")
         lp, lse = gpu_lib.logprob_gather(H[a:b].contiguous(), W, ids[a:b].contiguous(), L)
         assert_bitwise(lp, full_lp[a:b], f"logprob rows [{a},{b}) L={L}")
         assert_bitwise(lse, full_lse[a:b], f"lse rows [{a},{b}) L={L}")
-    assert heights == ({128, 192} if L <= 8 else {128})
+    assert heights == {128, 192}
 
 
 @pytest.mark.parametrize("L", [2, 8, 16])
