@@ -115,18 +115,22 @@ def main():
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    def timed(fn, steps, warmup):
-        """Mean ms per call over `steps` calls (events on the launch stream) and per-call times."""
+    def timed(fn, steps, warmup, per_call=False):
+        """Mean ms per call over `steps` calls (events on the launch stream), and with
+        per_call the time of each call (an event between calls: fine for long calls, an
+        overhead of its own for short ones)."""
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_call else 2)]
         ev[0].record(stream)
         for i in range(steps):
             fn()
-            ev[i + 1].record(stream)
+            if per_call:
+                ev[i + 1].record(stream)
+        ev[-1].record(stream)
         torch.cuda.synchronize()
-        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+        per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)] if per_call else []
         return ev[0].elapsed_time(ev[-1]) / steps, per
 
     def mfma_line(flops, ms):
@@ -175,7 +179,7 @@ def main():
     flops = 2.0 * M * K * V
     if args.phase in ("all", "prefill"):
         ms_step, per_call = timed(lambda: tig.tig_logprob_gather(Hd, Wd, idd, lp, lse, L, ws),
-                                  args.steps, args.warmup)
+                                  args.steps, args.warmup, per_call=True)
         tok_s = M / (ms_step / 1e3)
         tflops = flops / (float(np.mean(per_call)) / 1e3) / 1e12
         spread = {"min_ms": float(np.min(per_call)), "median_ms": float(np.median(per_call)),
