@@ -29,12 +29,19 @@ Readings where the pages leave a step open:
 * R8 a sampled id outside ``[0, V)`` yields NaN for that row only.
 * R12 the MoE combine runs in ascending expert id, ``acc = acc + g*y`` with a
   float32 multiply then a float32 add, each rounded to nearest even.
+* R13 the router: logits are the FP32 leaf-tree contraction of the token with
+  the router weight, the same at every batch size ([Bit-consistent RL],
+  section 4.1: the router gate uses one FP32-output GEMM at every batch size);
+  the top-k experts are taken largest logit first, equal logits in ascending
+  expert id (the pages ask only that tie-breaking and output order be fixed,
+  section 1); the gates are the softmax over the selected logits.
 
 Parity status:
 
 * ``contraction_ref``, ``lse_ref``, ``log_softmax_ref``, ``logprob_ref``,
-  ``moe_ref``: plain definitions in fp64; pinned by brute force (exact rational
-  arithmetic), closed forms and invariants in ``tests/test_oracle_pins.py``.
+  ``moe_ref``, ``route_select``, ``route_gates_ref``, ``route_ref``: plain
+  definitions in fp64; pinned by brute force (exact rational arithmetic, rank
+  counting), closed forms and invariants in ``tests/test_oracle_pins.py``.
 * ``leaf_tree_f32``, ``leaf_tree_gemm_f32``, ``moe_combine_f32``: float32
   emulators of the fixed orders; pinned by hand-derived closed forms.  They are
   exact models of the GPU only where every leaf sum (or every expert output) is
@@ -60,6 +67,9 @@ __all__ = [
     "gumbel_max_ids",
     "moe_ref",
     "moe_combine_f32",
+    "route_select",
+    "route_gates_ref",
+    "route_ref",
     "k3_kl",
 ]
 
@@ -278,6 +288,39 @@ def moe_combine_f32(Y, topk_ids, topk_w) -> np.ndarray:
             term = np.multiply(w[rows, s][:, None], Y[rows, s], dtype=np.float32)
             out = np.add(out, term, dtype=np.float32)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Router of the MoE layer   [Bit-consistent RL, sections 1 and 4.1; reading R13]
+# ---------------------------------------------------------------------------
+
+def route_select(logits, topk: int) -> np.ndarray:
+    """Expert ids of the ``topk`` largest logits of each row, largest first.
+
+    Equal logits are taken in ascending expert id (reading R13); +0 and -0 are
+    equal; NaN logits come after every other value.  A plain stable sort by the
+    key (-logit, expert id).
+    """
+    X = np.asarray(logits, dtype=np.float64)
+    T, E = X.shape
+    ids = np.broadcast_to(np.arange(E), X.shape)
+    order = np.lexsort((ids, -X), axis=1)   # last key first: -logit, then id
+    return order[:, :topk].astype(np.int32)
+
+
+def route_gates_ref(logits, topk_ids) -> np.ndarray:
+    """Softmax over each row's selected logits (fp64): ``exp(l - m) / sum``."""
+    X = np.asarray(logits, dtype=np.float64)
+    sel = np.take_along_axis(X, np.asarray(topk_ids, dtype=np.int64), axis=1)
+    e = np.exp(sel - sel.max(axis=1, keepdims=True))
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def route_ref(H, Wr, topk: int):
+    """Router of the MoE layer: (fp64 logits, top-k ids, fp64 gates)."""
+    logits = contraction_ref(H, Wr)
+    ids = route_select(logits, topk)
+    return logits, ids, route_gates_ref(logits, ids)
 
 
 # ---------------------------------------------------------------------------

@@ -356,6 +356,82 @@ def test_routing_input_is_valid():
 
 
 # ---------------------------------------------------------------------------
+# The router   [Bit-consistent RL, sections 1 and 4.1; reading R13]
+# ---------------------------------------------------------------------------
+
+def _rank_select(row, k):
+    """Brute force: rank(e) = #{better e'}, better = larger value, or equal value
+    and lower id; NaN after every number, NaNs by id.  Slot r holds rank r."""
+    def better(a, b):   # is expert a ahead of expert b?
+        va, vb = row[a], row[b]
+        na, nb = math.isnan(va), math.isnan(vb)
+        if na or nb:
+            return (not na and nb) or (na and nb and a < b)
+        return va > vb or (va == vb and a < b)
+    E = len(row)
+    rank = [sum(better(o, e) for o in range(E) if o != e) for e in range(E)]
+    assert sorted(rank) == list(range(E))
+    return [rank.index(r) for r in range(k)]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_route_select_brute_force_ranks(seed):
+    rng = np.random.default_rng(700 + seed)
+    E, k = 12, 5
+    X = rng.integers(-2, 3, size=(40, E)).astype(np.float64)   # many ties
+    X[0, [1, 4, 7]] = [0.0, -0.0, 0.0]                            # signed zeros tie
+    X[1] = -0.0
+    X[2, 3] = np.nan
+    X[3, :] = np.nan
+    X[3, 9] = -5.0
+    got = oracle.route_select(X, k)
+    for t in range(X.shape[0]):
+        assert got[t].tolist() == _rank_select(X[t].tolist(), k), t
+
+
+def test_route_equal_logits_take_lowest_ids_with_equal_gates():
+    X = np.full((3, 64), 0.75)
+    ids = oracle.route_select(X, 8)
+    assert np.all(ids == np.arange(8))
+    assert np.all(oracle.route_gates_ref(X, ids) == 1.0 / 8)
+
+
+def test_route_gates_closed_form():
+    # logits 0, -ln 2, -2 ln 2, -3 ln 2 and far smaller ones: exp terms 1, 1/2,
+    # 1/4, 1/8 of sum 15/8, so the gates are 8/15, 4/15, 2/15, 1/15
+    ln2 = math.log(2.0)
+    row = np.array([-9.0, -ln2, -20.0, 0.0, -3 * ln2, -2 * ln2, -30.0, -11.0])
+    ids = oracle.route_select(row[None], 4)
+    assert ids[0].tolist() == [3, 1, 5, 4]
+    g = oracle.route_gates_ref(row[None], ids)[0]
+    assert np.allclose(g, [8 / 15, 4 / 15, 2 / 15, 1 / 15], rtol=0, atol=1e-15)
+
+
+def test_route_gates_invariants():
+    rng = np.random.default_rng(711)
+    X = rng.standard_normal((50, 64))
+    ids = oracle.route_select(X, 8)
+    g = oracle.route_gates_ref(X, ids)
+    assert np.allclose(g.sum(axis=1), 1.0, atol=1e-14)
+    assert np.all(np.diff(g, axis=1) <= 0)                      # largest logit first
+    assert np.allclose(oracle.route_gates_ref(X + 3.5, ids), g, atol=1e-14)
+    top1 = oracle.route_select(X, 1)[:, 0]
+    assert np.all(top1 == np.argmax(X, axis=1))                 # argmax takes the first maximum
+    assert np.all(oracle.route_gates_ref(X, top1[:, None]) == 1.0)
+
+
+def test_route_ref_is_the_contraction_then_the_rule():
+    rng = np.random.default_rng(712)
+    H = wl.integer_bf16(rng, (9, 64), -2, 2)
+    Wr = wl.integer_bf16(rng, (16, 64), -2, 2)
+    logits, ids, g = oracle.route_ref(H, Wr, 4)
+    exact = oracle.as_f64(H) @ oracle.as_f64(Wr).T                # small integers: exact
+    assert np.array_equal(logits, exact)
+    for t in range(9):
+        assert ids[t].tolist() == _rank_select(exact[t].tolist(), 4)
+
+
+# ---------------------------------------------------------------------------
 # Gumbel-max sampling and the k3 metric
 # ---------------------------------------------------------------------------
 
