@@ -252,7 +252,20 @@ def main():
         moe = {"ms": ms, "shape": f"T={c.tokens} E={c.experts} top{c.topk} K={c.K} N={c.N} leaves={c.leaves}",
                "roofline": mfma_line(2.0 * c.tokens * c.topk * c.K * c.N, ms)}
         log(f"moe: {ms * 1e3:.1f} us, {moe['roofline']['achieved']:.0f} TFLOP/s")
-        del Hm, We, out, wsm
+        del We, out, wsm
+
+        # The router of the same layer on the GPU: FP32 logits (4096 x 64, K = 2048,
+        # 8 leaves), top-8 and gates.  Bound by reading H once.
+        Wr = to_dev(wl.normal_bf16(sm["router"], (c.experts, c.K), 0.02))
+        lgt = torch.empty(c.tokens, c.experts, dtype=torch.float32, device=dev)
+        rid = torch.empty(c.tokens, c.topk, dtype=torch.int32, device=dev)
+        rw = torch.empty(c.tokens, c.topk, dtype=torch.float32, device=dev)
+        ms, _ = timed(lambda: tig.tig_moe_route(Hm, Wr, lgt, rid, rw, c.leaves), 50, 3)
+        rbytes = 2.0 * c.tokens * c.K + 2.0 * c.experts * c.K + 4.0 * c.tokens * c.experts + 8.0 * c.tokens * c.topk
+        moe["route"] = {"us": ms * 1e3, "shape": f"T={c.tokens} E={c.experts} top{c.topk} K={c.K} leaves={c.leaves}",
+                        "roofline": hbm_line(rbytes, ms)}
+        log(f"route: {ms * 1e3:.1f} us")
+        del Hm, Wr, lgt, rid, rw
 
         c = wl.CONFIGS["large"]
         sg = wl.streams(c.seed)

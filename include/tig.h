@@ -146,6 +146,30 @@ tig_status tig_moe_workspace_bytes(int64_t T, int64_t N, int64_t K, int32_t n_ex
                                    int32_t topk, size_t* bytes);
 
 /*
+ * MoE router on the GPU, batch-invariant: [BitRL, 4.1] the router gate is one
+ * GEMM with FP32 output at every batch size; [BitRL, 1] once the logits match,
+ * the top-k tie-breaking and output order must be fixed too.
+ *   logits = leaf-tree(H Wr^T) in FP32 (exactly tig_tree_gemm with FP32 out);
+ *   topk_ids[t] = the topk largest logits of token t, largest first; equal
+ *     logits in ascending expert id; +0 equals -0; NaN after every number;
+ *   topk_w[t] = softmax over those logits: m = the largest,
+ *     e_s = exp2((l_s - m) * log2 e) (hardware exp2), the sum of the e_s by
+ *     the balanced adjacent-pair tree over the slots zero-padded to a power
+ *     of two, topk_w = e_s / sum (IEEE FP32 division).
+ * The outputs are the routing inputs of tig_moe_tree_gemm_combine.
+ *   H         bf16 [T, K] contiguous (tokens)
+ *   Wr        bf16 [n_experts, K] contiguous (router weight)
+ *   logits    float [T, n_experts] out (caller-owned; also the kernel's scratch)
+ *   topk_ids  int32 [T, topk] out
+ *   topk_w    float [T, topk] out
+ * Implemented: n_experts <= 1024, topk <= 16, leaves <= 16, K/leaves a
+ * multiple of 64.  T == 0 is TIG_OK and launches nothing.
+ */
+tig_status tig_moe_route(const void* H, const void* Wr, float* logits, int32_t* topk_ids,
+                         float* topk_w, int64_t T, int64_t K, int32_t n_experts, int32_t topk,
+                         int32_t leaves, hipStream_t stream);
+
+/*
  * The pinned numerical policy for (K, leaves): the constants that decide the
  * bits, in the spirit of [IsoExec, Unified execution contract] (implementation
  * and constants pinned per region; identities are SHA-256 digests).

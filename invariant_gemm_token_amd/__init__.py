@@ -20,9 +20,9 @@ import os
 __all__ = [
     "TigError", "load", "lib_path",
     "tig_tree_gemm", "tig_logprob_gather", "tig_logprob_workspace_bytes",
-    "tig_moe_tree_gemm_combine", "tig_moe_workspace_bytes", "tig_plan_describe",
+    "tig_moe_tree_gemm_combine", "tig_moe_workspace_bytes", "tig_moe_route", "tig_plan_describe",
     "tig_status_string", "tig_last_error",
-    "tree_gemm", "logprob_gather", "moe_tree_gemm_combine",
+    "tree_gemm", "logprob_gather", "moe_tree_gemm_combine", "moe_route",
     "TIG_OK", "TIG_ERR_INVALID_ARG", "TIG_ERR_UNSUPPORTED", "TIG_ERR_WORKSPACE", "TIG_ERR_HIP",
     "TIG_OUT_F32", "TIG_OUT_BF16",
 ]
@@ -62,6 +62,7 @@ _SIGNATURES = {
     "tig_moe_tree_gemm_combine": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i64, _i64, _i64,
                                          _i32, _vp, _sz, _vp]),
     "tig_moe_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, _i32, ctypes.POINTER(_sz)]),
+    "tig_moe_route": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp]),
     "tig_plan_describe": (_i32, [_i64, _i32, ctypes.POINTER(_Plan)]),
     "tig_status_string": (ctypes.c_char_p, [_i32]),
     "tig_last_error": (ctypes.c_char_p, []),
@@ -236,6 +237,28 @@ def tig_moe_tree_gemm_combine(H, W_experts, topk_ids, topk_w, out, leaves: int, 
     _check(st, "tig_moe_tree_gemm_combine")
 
 
+def tig_moe_route(H, Wr, logits, topk_ids, topk_w, leaves: int, stream=None) -> None:
+    """MoE router: FP32 leaf-tree logits, top-k (ties to the lower id) and softmax gates."""
+    torch = _torch()
+    _need(H, "H", torch.bfloat16, 2)
+    _need(Wr, "Wr", torch.bfloat16, 2)
+    _need(logits, "logits", torch.float32, 2)
+    _need(topk_ids, "topk_ids", torch.int32, 2)
+    _need(topk_w, "topk_w", torch.float32, 2)
+    _same_device(H, Wr, logits, topk_ids, topk_w)
+    for t, n in ((H, "H"), (Wr, "Wr"), (logits, "logits"), (topk_ids, "topk_ids"), (topk_w, "topk_w")):
+        _contig(t, n)
+    T, K = H.shape
+    E, K2 = Wr.shape
+    topk = topk_ids.shape[1]
+    if K2 != K or tuple(logits.shape) != (T, E) or tuple(topk_ids.shape) != (T, topk) or tuple(
+            topk_w.shape) != (T, topk):
+        raise ValueError("shapes do not match")
+    st = load().tig_moe_route(H.data_ptr(), Wr.data_ptr(), logits.data_ptr(), topk_ids.data_ptr(),
+                              topk_w.data_ptr(), T, K, E, topk, int(leaves), _stream(stream))
+    _check(st, "tig_moe_route")
+
+
 def tig_plan_describe(K: int, leaves: int) -> dict:
     plan = _Plan()
     _check(load().tig_plan_describe(int(K), int(leaves), ctypes.byref(plan)), "tig_plan_describe")
@@ -266,6 +289,18 @@ def logprob_gather(H, W, ids, leaves: int, workspace=None, with_lse: bool = True
     lse = torch.empty(M, dtype=torch.float32, device=H.device) if with_lse else None
     tig_logprob_gather(H, W, ids, lp, lse, leaves, workspace, stream)
     return lp, lse
+
+
+def moe_route(H, Wr, topk: int, leaves: int, stream=None):
+    """Allocate and return (logits, topk_ids, topk_w) of tig_moe_route."""
+    torch = _torch()
+    T = H.shape[0]
+    E = Wr.shape[0]
+    logits = torch.empty((T, E), dtype=torch.float32, device=H.device)
+    ids = torch.empty((T, topk), dtype=torch.int32, device=H.device)
+    w = torch.empty((T, topk), dtype=torch.float32, device=H.device)
+    tig_moe_route(H, Wr, logits, ids, w, leaves, stream)
+    return logits, ids, w
 
 
 def moe_tree_gemm_combine(H, W_experts, topk_ids, topk_w, leaves: int, workspace=None, stream=None):

@@ -273,6 +273,32 @@ tig_status tig_moe_workspace_bytes(int64_t T, int64_t N, int64_t K, int32_t n_ex
   return ok();
 }
 
+tig_status tig_moe_route(const void* H, const void* Wr, float* logits, int32_t* topk_ids,
+                         float* topk_w, int64_t T, int64_t K, int32_t n_experts, int32_t topk,
+                         int32_t leaves, hipStream_t stream) {
+  if (T < 0) return fail(TIG_ERR_INVALID_ARG, "T must be >= 0");
+  if (n_experts < 1 || topk < 1 || topk > n_experts)
+    return fail(TIG_ERR_INVALID_ARG, "need 1 <= topk <= n_experts");
+  if (n_experts > tig::kMaxRouteExperts)
+    return fail(TIG_ERR_UNSUPPORTED, "n_experts > %d not implemented", tig::kMaxRouteExperts);
+  if (topk > tig::kMaxTopk) return fail(TIG_ERR_UNSUPPORTED, "topk > %d not implemented", tig::kMaxTopk);
+  tig_status s = check_k_leaves(K, leaves);
+  if (s != TIG_OK) return s;
+  if (T == 0) return ok();
+  if (!H || !Wr || !logits || !topk_ids || !topk_w)
+    return fail(TIG_ERR_INVALID_ARG, "H, Wr, logits, topk_ids and topk_w must not be NULL");
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4))
+    return fail(TIG_ERR_INVALID_ARG, "logits, topk_ids or topk_w misaligned");
+  if (T * int64_t(n_experts) >= (int64_t(1) << 40))
+    return fail(TIG_ERR_UNSUPPORTED, "T * n_experts too large");
+  // The logits: the leaf-tree contraction with FP32 output, as tig_tree_gemm.
+  s = tig_tree_gemm(H, K, Wr, K, logits, n_experts, TIG_OUT_F32, T, n_experts, K, leaves, stream);
+  if (s != TIG_OK) return s;
+  const hipError_t e = tig::launch_moe_route(logits, T, n_experts, topk, topk_ids, topk_w, stream);
+  if (e != hipSuccess) return fail(TIG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 tig_status tig_moe_tree_gemm_combine(const void* H, const void* W_experts, int32_t n_experts,
                                      const int32_t* topk_ids, const float* topk_w, int32_t topk,
                                      float* out, int64_t T, int64_t N, int64_t K, int32_t leaves,

@@ -129,5 +129,10 @@ inline size_t moe_ws_bytes(int64_t T, int64_t N, int n_experts, int topk) {
 hipError_t launch_tree_gemm(const TreeGemmLaunch& p, hipStream_t stream);
 hipError_t launch_logprob(const LogprobLaunch& p, hipStream_t stream);
 hipError_t launch_moe(const MoeLaunch& p, hipStream_t stream);
+// Router, after its logits are computed: per token the topk largest logits
+// and their softmax gates.
+constexpr int kMaxRouteExperts = 1024;
+hipError_t launch_moe_route(const float* logits, int64_t T, int n_experts, int topk, int32_t* topk_ids,
+                            float* topk_w, hipStream_t stream);
 
 }  // namespace tig

@@ -1367,6 +1367,96 @@ hipError_t launch_logprob(const LogprobLaunch& p, hipStream_t s) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// MoE router, after the logits (a tree_gemm with FP32 output, the same at
+// every batch size): per token the topk largest logits, largest first, equal
+// logits in ascending expert id, +0 equal to -0, NaN after every number; then
+// the softmax over them: m = the largest, e_s = exp2((l_s - m) log2 e), the
+// sum by the balanced adjacent-pair tree over the slots zero-padded to a power
+// of two, gate_s = e_s / sum (FP32 division).  One wave per token.
+// ---------------------------------------------------------------------------
+namespace {
+
+// Order key of a logit: larger key = ahead.  -0 becomes +0 (v + 0 under
+// round to nearest even); negative floats are mirrored so that the integer
+// order is the float order; NaN sorts below every number.
+__device__ __forceinline__ int route_key(float v) {
+  if (__builtin_isnan(v)) return INT_MIN;
+  const int b = __builtin_bit_cast(int, v + 0.0f);
+  return b >= 0 ? b : (b ^ 0x7FFFFFFF);
+}
+
+constexpr int ROUTE_PER_LANE = kMaxRouteExperts / 64;
+
+__global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict__ logits, int64_t T, int E,
+                                                        int topk, int32_t* __restrict__ ids,
+                                                        float* __restrict__ gates) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;   // the whole wave
+  const float* row = logits + t * E;
+  // Lane l holds experts l + 64 c; a candidate is (key << 32) | ~expert, so
+  // the largest candidate is the largest logit, then the lowest expert id.
+  float v[ROUTE_PER_LANE];
+  int64_t cand[ROUTE_PER_LANE];
+#pragma unroll
+  for (int c = 0; c < ROUTE_PER_LANE; ++c) {
+    const int e = c * 64 + lane;
+    v[c] = e < E ? row[e] : 0.0f;
+    cand[c] = e < E ? int64_t((uint64_t(uint32_t(route_key(v[c]))) << 32) | uint32_t(~e)) : INT64_MIN;
+  }
+  float my_v = 0.0f, vmax = 0.0f;
+  int my_e = 0;
+  for (int r = 0; r < topk; ++r) {
+    int64_t best = INT64_MIN;
+#pragma unroll
+    for (int c = 0; c < ROUTE_PER_LANE; ++c) best = cand[c] > best ? cand[c] : best;
+#pragma unroll
+    for (int d = 1; d < 64; d *= 2) {
+      const int64_t o = __shfl_xor(best, d);
+      best = o > best ? o : best;
+    }
+    const int e = int(~uint32_t(uint64_t(best)));   // every lane: the winner
+    float mine = 0.0f;
+#pragma unroll
+    for (int c = 0; c < ROUTE_PER_LANE; ++c)
+      if (c == (e >> 6)) mine = v[c];
+    const float ve = __shfl(mine, e & 63);
+    if (lane == (e & 63)) {
+#pragma unroll
+      for (int c = 0; c < ROUTE_PER_LANE; ++c)
+        if (c == (e >> 6)) cand[c] = INT64_MIN;
+    }
+    if (r == 0) vmax = ve;
+    if (lane == r) {
+      my_e = e;
+      my_v = ve;
+    }
+  }
+  float x = lane < topk ? __builtin_amdgcn_exp2f((my_v - vmax) * LOG2E) : 0.0f;
+  float S = x;
+  for (int d = 1; d < topk; d *= 2) {   // pair tree over lanes 0 .. 2^ceil(log2 topk) - 1
+    const float o = __shfl_xor(S, d);
+    S = (lane & d) ? o + S : S + o;
+  }
+  if (lane < topk) {
+    ids[t * topk + lane] = my_e;
+    gates[t * topk + lane] = x / S;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_moe_route(const float* logits, int64_t T, int n_experts, int topk, int32_t* topk_ids,
+                            float* topk_w, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (n_experts < 1 || n_experts > kMaxRouteExperts || topk < 1 || topk > n_experts || topk > 64)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(moe_route_kernel, dim3(unsigned((T + 3) / 4)), dim3(256), 0, s, logits, T, n_experts, topk,
+                     topk_ids, topk_w);
+  return hipGetLastError();
+}
+
 hipError_t launch_moe(const MoeLaunch& p, hipStream_t s) {
   switch (p.leaves_log2) {
     case 0: return launch_moe_lg<0>(p, s);

@@ -25,10 +25,12 @@ def dev_bf16(bits: np.ndarray) -> torch.Tensor:
 
 
 def host_bits(t: torch.Tensor) -> np.ndarray:
-    """Raw bits of a float32 / bf16 tensor as an unsigned numpy array."""
+    """Raw bits of a float32 / bf16 / int32 tensor as an unsigned numpy array."""
     t = t.detach().contiguous().cpu()
     if t.dtype == torch.float32:
         return t.view(torch.int32).numpy().view(np.uint32)
+    if t.dtype == torch.int32:
+        return t.numpy().view(np.uint32)
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     raise TypeError(t.dtype)

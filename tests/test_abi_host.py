@@ -122,6 +122,22 @@ def test_zero_rows_is_a_noop_even_with_null_pointers():
     assert lib.tig_logprob_gather(None, None, None, None, None, 0, 4096, 151936, 8, None, 0, None) == tig.TIG_OK
     assert lib.tig_moe_tree_gemm_combine(None, None, 64, None, None, 8, None, 0, 1408, 2048, 8,
                                          None, 0, None) == tig.TIG_OK
+    assert lib.tig_moe_route(None, None, None, None, None, 0, 2048, 64, 8, 8, None) == tig.TIG_OK
+
+
+def test_route_arguments_rejected_before_any_launch():
+    lib = _raw()
+    # topk outside [1, n_experts]
+    assert lib.tig_moe_route(None, None, None, None, None, 4, 512, 8, 9, 8, None) == tig.TIG_ERR_INVALID_ARG
+    assert lib.tig_moe_route(None, None, None, None, None, 4, 512, 8, 0, 8, None) == tig.TIG_ERR_INVALID_ARG
+    # limits of this implementation
+    assert lib.tig_moe_route(None, None, None, None, None, 4, 512, 1025, 8, 8, None) == tig.TIG_ERR_UNSUPPORTED
+    assert lib.tig_moe_route(None, None, None, None, None, 4, 512, 64, 17, 8, None) == tig.TIG_ERR_UNSUPPORTED
+    # leaves that do not split K into 64-multiples; negative T; NULL outputs
+    assert lib.tig_moe_route(None, None, None, None, None, 4, 512, 64, 8, 16, None) == tig.TIG_ERR_UNSUPPORTED
+    assert lib.tig_moe_route(None, None, None, None, None, -1, 512, 64, 8, 8, None) == tig.TIG_ERR_INVALID_ARG
+    assert lib.tig_moe_route(None, None, None, None, None, 4, 512, 64, 8, 8, None) == tig.TIG_ERR_INVALID_ARG
+    assert "NULL" in tig.tig_last_error()
 
 
 def test_null_pointers_rejected():

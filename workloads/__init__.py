@@ -131,7 +131,8 @@ CONFIGS = {
                     M=(16384,), n_seq=256, n_pos=64),
 }
 
-_STREAMS = ("H", "W", "ids", "perm", "route", "gumbel", "extra")
+# Appending keeps every existing stream (child i of the seed sequence is fixed by i).
+_STREAMS = ("H", "W", "ids", "perm", "route", "gumbel", "extra", "router")
 
 
 def streams(seed: int) -> dict:
