@@ -39,7 +39,8 @@ Readings where the pages leave a step open:
 Parity status:
 
 * ``contraction_ref``, ``lse_ref``, ``log_softmax_ref``, ``logprob_ref``,
-  ``moe_ref``, ``route_select``, ``route_gates_ref``, ``route_ref``: plain
+  ``moe_ref``, ``route_select``, ``route_gates_ref``, ``route_ref``,
+  ``topk_positions``: plain
   definitions in fp64; pinned by brute force (exact rational arithmetic, rank
   counting), closed forms and invariants in ``tests/test_oracle_pins.py``.
 * ``leaf_tree_f32``, ``leaf_tree_gemm_f32``, ``moe_combine_f32``: float32
@@ -70,6 +71,7 @@ __all__ = [
     "route_select",
     "route_gates_ref",
     "route_ref",
+    "topk_positions",
     "k3_kl",
 ]
 
@@ -321,6 +323,35 @@ def route_ref(H, Wr, topk: int):
     logits = contraction_ref(H, Wr)
     ids = route_select(logits, topk)
     return logits, ids, route_gates_ref(logits, ids)
+
+
+# ---------------------------------------------------------------------------
+# Deterministic Top-K of positions   [Bit-consistent RL, section 4.3]
+# ---------------------------------------------------------------------------
+
+def topk_positions(scores, lengths, k: int) -> np.ndarray:
+    """Top-``k`` positions of each row by score; ties to the larger position.
+
+    Row r's candidates are its positions ``0 .. lengths[r]-1``.  A position is
+    ahead of another when its score is larger, or the scores are equal and its
+    position is larger (the 64-bit key of score and in-request position of
+    section 4.3); +0 equals -0 and NaN scores come after every number.  The
+    ``min(k, lengths[r])`` selected positions are then listed by descending
+    position, followed by -1 (invalid) entries up to ``k``.
+    """
+    S = np.asarray(scores, dtype=np.float64)
+    R = S.shape[0]
+    out = np.full((R, k), -1, dtype=np.int64)
+    for r in range(R):
+        n = int(lengths[r])
+        s = S[r, :n]
+        pos = np.arange(n)
+        nan = np.isnan(s)
+        key = np.where(nan, 0.0, -s)          # ascending key = descending score
+        order = np.lexsort((-pos, key, nan))  # not NaN first, then score, then position
+        sel = np.sort(order[:min(k, n)])[::-1]
+        out[r, :sel.size] = sel
+    return out
 
 
 # ---------------------------------------------------------------------------

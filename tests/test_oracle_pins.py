@@ -432,6 +432,71 @@ def test_route_ref_is_the_contraction_then_the_rule():
 
 
 # ---------------------------------------------------------------------------
+# Deterministic Top-K of positions   [Bit-consistent RL, section 4.3]
+# ---------------------------------------------------------------------------
+
+def _topk_brute(row, n, k):
+    """Rank counting: p is ahead of q when score(p) > score(q), or equal scores
+    and p > q; NaN after every number (NaNs: larger position first)."""
+    def ahead(p, q):
+        a, b = row[p], row[q]
+        na, nb = math.isnan(a), math.isnan(b)
+        if na or nb:
+            return (not na and nb) or (na and nb and p > q)
+        return a > b or (a == b and p > q)
+    sel = [p for p in range(n) if sum(ahead(q, p) for q in range(n) if q != p) < k]
+    sel = sorted(sel, reverse=True)
+    return sel + [-1] * (k - len(sel))
+
+
+def test_topk_golden_examples():
+    for name, k, n, pairs, expect in load_golden("topk_figure_example.txt"):
+        k, n = int(k), int(n)
+        row = np.full((1, max(n, 64)), -1.0)
+        for item in [x for x in pairs.split(",") if x.strip()]:
+            p, v = item.split("=")
+            row[0, int(p)] = float(Fraction(v.strip()))
+        if not pairs.strip():
+            row[0, :] = 0.5
+        got = oracle.topk_positions(row, [n], k)[0].tolist()
+        assert got == [int(x) for x in expect.split(",")], name
+        assert got == _topk_brute(row[0].tolist(), n, k), name
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_topk_positions_brute_force(seed):
+    rng = np.random.default_rng(800 + seed)
+    R, N, k = 12, 40, 7
+    S = rng.integers(-3, 4, size=(R, N)).astype(np.float64)        # many ties
+    S[0, 5:9] = [0.0, -0.0, 0.0, -0.0]
+    S[1, :] = np.nan
+    S[1, [3, 30]] = [-7.0, 2.0]
+    S[2, ::3] = np.nan
+    lengths = rng.integers(0, N + 1, size=R)
+    lengths[:3] = N
+    lengths[3] = 0
+    lengths[4] = 5                                                   # fewer than k
+    got = oracle.topk_positions(S, lengths, k)
+    for r in range(R):
+        assert got[r].tolist() == _topk_brute(S[r].tolist(), int(lengths[r]), k), r
+
+
+def test_topk_positions_properties():
+    rng = np.random.default_rng(810)
+    S = rng.standard_normal((5, 3000))
+    lengths = np.array([3000, 2999, 2048, 100, 1])
+    out = oracle.topk_positions(S, lengths, 2048)
+    for r in range(5):
+        n = int(lengths[r])
+        sel = out[r][out[r] >= 0]
+        assert sel.size == min(2048, n) and np.all(out[r][sel.size:] == -1)
+        assert np.all(np.diff(sel) < 0)                                   # descending positions
+        if sel.size < n:
+            rest = np.setdiff1d(np.arange(n), sel)
+            assert S[r, sel].min() >= S[r, rest].max()                    # the largest scores
+
+
+# ---------------------------------------------------------------------------
 # Gumbel-max sampling and the k3 metric
 # ---------------------------------------------------------------------------
 
