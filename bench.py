@@ -224,7 +224,7 @@ def main():
     del Hd, Wd, idd, ws
 
     # ---------------- the other workloads of the path ----------------
-    linear = moe = large = None
+    linear = moe = large = topk = None
     if not args.no_extra and args.phase == "all":
         c = wl.CONFIGS["linear"]
         sl = wl.streams(c.seed)
@@ -267,6 +267,23 @@ def main():
         log(f"route: {ms * 1e3:.1f} us")
         del Hm, Wr, lgt, rid, rw
 
+        # Sparse-attention indexer Top-K: 128 rows of pitch 65536, k = 2048, lengths
+        # mixed (uniform in [1, 65536]) and all full.  Bound by reading the scores.
+        c = wl.CONFIGS["indexer"]
+        si = wl.streams(c.seed)
+        sc = torch.from_numpy(wl.indexer_scores(si["scores"], c.tokens, c.N)).to(dev)
+        mixed = wl.request_lengths(si["lengths"], c.tokens, 1, c.N)
+        tko = torch.empty(c.tokens, c.topk, dtype=torch.int32, device=dev)
+        topk = {}
+        for name, lens in (("mixed", mixed), ("full", np.full(c.tokens, c.N, dtype=np.int32))):
+            ln = torch.from_numpy(lens).to(dev)
+            ms, _ = timed(lambda: tig.tig_topk_positions(sc, ln, tko), 50, 3)
+            tbytes = 4.0 * float(lens.sum()) + 4.0 * c.tokens * (c.topk + 1)
+            topk[name] = {"us": ms * 1e3, "shape": f"R={c.tokens} ld={c.N} k={c.topk} lengths={name}",
+                                 "roofline": hbm_line(tbytes, ms)}
+            log(f"topk {name}: {ms * 1e3:.1f} us")
+        del sc, tko
+
         c = wl.CONFIGS["large"]
         sg = wl.streams(c.seed)
         Mg = c.n_seq * c.n_pos
@@ -306,6 +323,7 @@ def main():
         "decode": decode,
         "linear": linear,
         "moe": moe,
+        "topk": topk,
         "large": large,
         "cpu_baseline": cpu,
     }

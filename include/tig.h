@@ -11,7 +11,8 @@
  *   [BitRL]    "Termina el entrenamiento RL mas rapido: Consistente a nivel de
  *              bits, de alto rendimiento y dirigido por agentes", section 2
  *              (diff = 0 per sampled token; batch independence; prefill/decode
- *              consistency), 4.1 (one accumulation order for every M), 4.4 and
+ *              consistency), 4.1 (one accumulation order for every M), 4.3
+ *              (deterministic Top-K of positions: key, ties, order), 4.4 and
  *              4.5 (expert outputs combined in FP32 in a fixed order), 4.6
  *              (no host sync, workspaces sized from static bounds).
  *   [RZero]    "REINFORCE Zero: ..." section 6 (MI355X): libraries that pick
@@ -168,6 +169,27 @@ tig_status tig_moe_workspace_bytes(int64_t T, int64_t N, int64_t K, int32_t n_ex
 tig_status tig_moe_route(const void* H, const void* Wr, float* logits, int32_t* topk_ids,
                          float* topk_w, int64_t T, int64_t K, int32_t n_experts, int32_t topk,
                          int32_t leaves, hipStream_t stream);
+
+/*
+ * Deterministic Top-K of positions, [BitRL, 4.3] (the sparse-attention
+ * indexer's selection and the figure of its 64-bit key): row r's candidates
+ * are its positions 0 .. lengths[r]-1; a position is ahead of another when
+ * its score is larger, or the scores are equal and its position is larger
+ * (the key is score, then in-request position, so a request's result does not
+ * depend on where it sits in the batch).  +0 equals -0; NaN scores come after
+ * every number.  The min(k, lengths[r]) selected positions are written by
+ * descending position, then -1 up to k.
+ *   scores   float [R, ld] (row r at scores + r*ld; only the first
+ *            lengths[r] entries are read)
+ *   lengths  int32 [R] on the device; values below 0 count as 0, above ld
+ *            as ld
+ *   out      int32 [R, k] out
+ * One workgroup per row.  Implemented: ld <= 65536 (TIG_ERR_UNSUPPORTED
+ * above), k >= 1 (any k; entries past the row's length are -1).  R == 0 is
+ * TIG_OK and launches nothing.
+ */
+tig_status tig_topk_positions(const float* scores, int64_t ld, const int32_t* lengths, int64_t R,
+                              int32_t k, int32_t* out, hipStream_t stream);
 
 /*
  * The pinned numerical policy for (K, leaves): the constants that decide the

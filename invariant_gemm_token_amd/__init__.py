@@ -20,9 +20,10 @@ import os
 __all__ = [
     "TigError", "load", "lib_path",
     "tig_tree_gemm", "tig_logprob_gather", "tig_logprob_workspace_bytes",
-    "tig_moe_tree_gemm_combine", "tig_moe_workspace_bytes", "tig_moe_route", "tig_plan_describe",
+    "tig_moe_tree_gemm_combine", "tig_moe_workspace_bytes", "tig_moe_route", "tig_topk_positions",
+    "tig_plan_describe",
     "tig_status_string", "tig_last_error",
-    "tree_gemm", "logprob_gather", "moe_tree_gemm_combine", "moe_route",
+    "tree_gemm", "logprob_gather", "moe_tree_gemm_combine", "moe_route", "topk_positions",
     "TIG_OK", "TIG_ERR_INVALID_ARG", "TIG_ERR_UNSUPPORTED", "TIG_ERR_WORKSPACE", "TIG_ERR_HIP",
     "TIG_OUT_F32", "TIG_OUT_BF16",
 ]
@@ -63,6 +64,7 @@ _SIGNATURES = {
                                          _i32, _vp, _sz, _vp]),
     "tig_moe_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, _i32, ctypes.POINTER(_sz)]),
     "tig_moe_route": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp]),
+    "tig_topk_positions": (_i32, [_vp, _i64, _vp, _i64, _i32, _vp, _vp]),
     "tig_plan_describe": (_i32, [_i64, _i32, ctypes.POINTER(_Plan)]),
     "tig_status_string": (ctypes.c_char_p, [_i32]),
     "tig_last_error": (ctypes.c_char_p, []),
@@ -259,6 +261,24 @@ def tig_moe_route(H, Wr, logits, topk_ids, topk_w, leaves: int, stream=None) -> 
     _check(st, "tig_moe_route")
 
 
+def tig_topk_positions(scores, lengths, out, stream=None) -> None:
+    """Top-k positions per row by (score, position), listed by descending position, -1 padded."""
+    torch = _torch()
+    _need(scores, "scores", torch.float32, 2)
+    _need(lengths, "lengths", torch.int32, 1)
+    _need(out, "out", torch.int32, 2)
+    _same_device(scores, lengths, out)
+    _contig(scores, "scores")
+    _contig(lengths, "lengths")
+    _contig(out, "out")
+    R, ld = scores.shape
+    if lengths.shape[0] != R or out.shape[0] != R:
+        raise ValueError("scores, lengths and out must have the same number of rows")
+    st = load().tig_topk_positions(scores.data_ptr(), ld, lengths.data_ptr(), R, out.shape[1], out.data_ptr(),
+                                   _stream(stream))
+    _check(st, "tig_topk_positions")
+
+
 def tig_plan_describe(K: int, leaves: int) -> dict:
     plan = _Plan()
     _check(load().tig_plan_describe(int(K), int(leaves), ctypes.byref(plan)), "tig_plan_describe")
@@ -312,4 +332,12 @@ def moe_tree_gemm_combine(H, W_experts, topk_ids, topk_w, leaves: int, workspace
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=H.device)
     out = torch.empty((T, N), dtype=torch.float32, device=H.device)
     tig_moe_tree_gemm_combine(H, W_experts, topk_ids, topk_w, out, leaves, workspace, stream)
+    return out
+
+
+def topk_positions(scores, lengths, k: int, stream=None):
+    """Allocate and return the ``[R, k]`` int32 output of tig_topk_positions."""
+    torch = _torch()
+    out = torch.empty((scores.shape[0], int(k)), dtype=torch.int32, device=scores.device)
+    tig_topk_positions(scores, lengths, out, stream)
     return out

@@ -299,6 +299,22 @@ tig_status tig_moe_route(const void* H, const void* Wr, float* logits, int32_t* 
   return ok();
 }
 
+tig_status tig_topk_positions(const float* scores, int64_t ld, const int32_t* lengths, int64_t R,
+                              int32_t k, int32_t* out, hipStream_t stream) {
+  if (R < 0 || ld < 0) return fail(TIG_ERR_INVALID_ARG, "R and ld must be >= 0");
+  if (k < 1) return fail(TIG_ERR_INVALID_ARG, "k must be >= 1");
+  if (ld > tig::kTopkMaxLen)
+    return fail(TIG_ERR_UNSUPPORTED, "rows longer than %lld not implemented", (long long)tig::kTopkMaxLen);
+  if (R == 0) return ok();
+  if (R > 0x7FFFFFFF) return fail(TIG_ERR_UNSUPPORTED, "R too large");
+  if (!scores || !lengths || !out) return fail(TIG_ERR_INVALID_ARG, "scores, lengths and out must not be NULL");
+  if (!aligned(scores, 4) || !aligned(lengths, 4) || !aligned(out, 4))
+    return fail(TIG_ERR_INVALID_ARG, "scores, lengths or out misaligned");
+  const hipError_t e = tig::launch_topk_positions(scores, ld, lengths, R, k, out, stream);
+  if (e != hipSuccess) return fail(TIG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 tig_status tig_moe_tree_gemm_combine(const void* H, const void* W_experts, int32_t n_experts,
                                      const int32_t* topk_ids, const float* topk_w, int32_t topk,
                                      float* out, int64_t T, int64_t N, int64_t K, int32_t leaves,

@@ -129,6 +129,12 @@ inline size_t moe_ws_bytes(int64_t T, int64_t N, int n_experts, int topk) {
 hipError_t launch_tree_gemm(const TreeGemmLaunch& p, hipStream_t stream);
 hipError_t launch_logprob(const LogprobLaunch& p, hipStream_t stream);
 hipError_t launch_moe(const MoeLaunch& p, hipStream_t stream);
+// Deterministic Top-K of positions: one workgroup of kTopkThreads per row,
+// kTopkPerThread scores per thread in registers.
+constexpr int kTopkThreads = 512, kTopkPerThread = 128;
+constexpr int64_t kTopkMaxLen = int64_t(kTopkThreads) * kTopkPerThread;
+hipError_t launch_topk_positions(const float* scores, int64_t ld, const int32_t* lengths, int64_t R, int k,
+                                 int32_t* out, hipStream_t stream);
 // Router, after its logits are computed: per token the topk largest logits
 // and their softmax gates.
 constexpr int kMaxRouteExperts = 1024;

@@ -1457,6 +1457,358 @@ hipError_t launch_moe_route(const float* logits, int64_t T, int n_experts, int t
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Deterministic Top-K of positions: per row, the k positions of largest key,
+// key = (order key of the score, position) as one 64-bit value, so equal
+// scores go to the larger position; +0 equals -0, NaN below every number.
+// The selected positions are written by descending position, then -1.
+//
+// One workgroup of 512 threads per row.  Slot j of thread t holds position
+// n-1-(512j+t): each load instruction of a wave reads 64 consecutive scores,
+// and (slot, wave, lane) order is descending position order.  The threshold
+// T, the take-th largest 32-bit score key, is found by a radix select over
+// LDS histograms of 11, 11 and 10 bits: each pass counts the keys that share
+// the digits found so far and picks the digit at which the count from the
+// top reaches the number still wanted.  Keys above T are selected, and of the
+// keys equal to T the `need` at the largest positions.  The wave ballots of
+// "key > T" and "key == T" per slot are, in that order, a bitmap of the row
+// by descending position; one scan over their popcounts gives each 64-position
+// block its output offset and tie rank, and the blocks' 16-position quarters,
+// dealt round-robin to the threads, write the selected positions.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kTopkGroup = 16;                       // slots loaded and tested together
+constexpr int kTopkCopies = 8;                       // histogram copies, by lane % 8
+constexpr int kTopkHistStride = 2048 + 4;            // words from one copy to the next (4 banks on)
+constexpr int kTopkBlocks = kTopkPerThread * kTopkWaves;   // 64-position blocks of the longest row
+
+// f(integral_constant<I>), f(integral_constant<I+1>), ..., below N.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// The eight words w0..w7 (uniform) into lanes L..L+7 of `acc`.  The
+// compiler does not insert the wait states between a vector instruction that
+// writes an SGPR (as a ballot's compare does) and a lane write that reads it
+// when the read is in inline asm, so the s_nop gives them.
+template <int L>
+__device__ __forceinline__ uint32_t write_lanes8(uint32_t acc, uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                                 uint32_t w4, uint32_t w5, uint32_t w6, uint32_t w7) {
+  asm("s_nop 4\n\t"
+      "v_writelane_b32 %0, %1, %9\n\t"
+      "v_writelane_b32 %0, %2, %9+1\n\t"
+      "v_writelane_b32 %0, %3, %9+2\n\t"
+      "v_writelane_b32 %0, %4, %9+3\n\t"
+      "v_writelane_b32 %0, %5, %9+4\n\t"
+      "v_writelane_b32 %0, %6, %9+5\n\t"
+      "v_writelane_b32 %0, %7, %9+6\n\t"
+      "v_writelane_b32 %0, %8, %9+7"
+      : "=v"(acc)
+      : "s"(w0), "s"(w1), "s"(w2), "s"(w3), "s"(w4), "s"(w5), "s"(w6), "s"(w7), "n"(L), "0"(acc));
+  return acc;
+}
+
+// Unsigned order key of a score, larger = ahead: -0 becomes +0; numbers map
+// to keys >= 0x007FFFFF, NaN to 1, below every number.  Key 0 marks a slot
+// past the row's end, below everything and never selected.
+__device__ __forceinline__ uint32_t topk_key(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v + 0.0f);
+  const uint32_t kk = b ^ (uint32_t(int32_t(b) >> 31) | 0x80000000u);
+  return __builtin_isnan(v) ? 1u : kk;
+}
+
+// Inclusive prefix sum over the wave's lanes: within each row of 16 lanes by
+// row shifts, then across rows by the row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
+  return x;
+}
+
+// Inclusive prefix sums of a and b over the workgroup's threads in thread
+// order (ia, ib) and their totals (ta, tb, the same for every thread).  One
+// barrier; `red` (2 * waves ints) must not be written again before the
+// workgroup has passed another barrier.
+__device__ __forceinline__ void block_scan2_topk(int a, int b, int* red, int& ia, int& ib, int& ta, int& tb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int xa = wave_incl_scan(a), xb = wave_incl_scan(b);
+  if (lane == 63) {
+    red[wave] = xa;
+    red[kTopkWaves + wave] = xb;
+  }
+  __syncthreads();
+  int ba = 0, bb = 0, sa = 0, sb = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const int ca = red[w], cb = red[kTopkWaves + w];
+    ba += w < wave ? ca : 0;
+    bb += w < wave ? cb : 0;
+    sa += ca;
+    sb += cb;
+  }
+  ia = ba + xa;
+  ib = bb + xb;
+  ta = sa;
+  tb = sb;
+}
+
+// The same for one value.
+__device__ __forceinline__ int block_scan1_topk(int v, int* red, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int x = wave_incl_scan(v);
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkWaves; ++w) {
+    const int c = red[w];
+    before += w < wave ? c : 0;
+    all += c;
+  }
+  total = all;
+  return before + x;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const float* __restrict__ scores, int64_t ld,
+                                                                     const int32_t* __restrict__ lengths, int k,
+                                                                     int32_t* __restrict__ out) {
+  // The histograms, later the blocks' output offsets and tie ranks.
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kTopkCopies * kTopkHistStride];
+  __shared__ __attribute__((aligned(16))) uint32_t masks[kTopkBlocks * 4];   // per block: gt lo, hi, eq lo, hi
+  __shared__ __attribute__((aligned(16))) int red[4 * kTopkWaves];   // two halves, alternated by pass; scans
+  __shared__ int found[2][2];
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int n = lengths[r];
+  n = n < 0 ? 0 : (int64_t(n) > ld ? int(ld) : n);
+  const int take = n < k ? n : k;
+  int32_t* o = out + r * int64_t(k);
+  const int groups = (n + kTopkThreads * kTopkGroup - 1) / (kTopkThreads * kTopkGroup);
+  uint32_t key[kTopkPerThread];
+  if (take > 0) {
+    // Loads of all groups that reach into the row first, then the keys, so
+    // that every load is in flight at once.  A slot before position 0 (only in
+    // the last group) has a byte offset that wraps to 2^32 - 4|p| in 32 bits,
+    // past the buffer's range of 4n <= 2^18 bytes: it returns 0 with no
+    // branch, and the slot gets key 0.
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(scores + r * ld, uint32_t(n) * 4u);
+    const uint32_t off0 = uint32_t(n - 1 - tid) * 4u;
+#pragma unroll
+    for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g) {
+      if (g < groups) {
+#pragma unroll
+        for (int i = 0; i < kTopkGroup; ++i) {
+          const uint32_t off = off0 - uint32_t(kTopkThreads * 4 * (kTopkGroup * g + i));
+          key[kTopkGroup * g + i] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g) {
+      if (g < groups) {
+#pragma unroll
+        for (int i = 0; i < kTopkGroup; ++i) {
+          const int j = kTopkGroup * g + i;
+          key[j] = topk_key(__builtin_bit_cast(float, key[j]));
+        }
+        if (g == groups - 1) {
+#pragma unroll
+          for (int i = 0; i < kTopkGroup; ++i) {
+            const int j = kTopkGroup * g + i;
+            key[j] = n - 1 - (kTopkThreads * j + tid) >= 0 ? key[j] : 0u;
+          }
+        }
+      }
+    }
+    // Radix select of T.  `rem` = how many of the keys sharing the digits
+    // found so far are still wanted.  Lane l counts into histogram copy l % 8
+    // (equal digits in one wave then mostly land in different banks).
+    uint32_t* const hcopy = hist + (lane & (kTopkCopies - 1)) * kTopkHistStride;
+    // The histograms start at zero; each pass's scan clears the words it
+    // reads, ready for the next pass.
+    for (int i = tid; i < kTopkCopies * kTopkHistStride / 4; i += kTopkThreads)
+      reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    uint32_t prefix = 0;
+    int rem = take;
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+      const int pshift = pass == 1 ? 21 : 10;        // bits below the digits already found
+#pragma unroll
+      for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g) {
+        if (g < groups) {
+          if (pass == 0 && g != groups - 1) {        // full groups: every slot counts
+#pragma unroll
+            for (int i = 0; i < kTopkGroup; ++i) atomicAdd(&hcopy[key[kTopkGroup * g + i] >> 21], 1u);
+          } else if (pass == 0) {                   // the last group: slots past the row have key 0
+#pragma unroll
+            for (int i = 0; i < kTopkGroup; ++i) {
+              const uint32_t kv = key[kTopkGroup * g + i];
+              if (kv != 0u) atomicAdd(&hcopy[kv >> 21], 1u);
+            }
+          } else {
+            // Four slots per test: a wave with no match in any of them skips
+            // the four (the common case in the last pass).
+#pragma unroll
+            for (int i0 = 0; i0 < kTopkGroup; i0 += 4) {
+              bool m[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) m[q] = (key[kTopkGroup * g + i0 + q] >> pshift) == prefix;
+              if (m[0] || m[1] || m[2] || m[3]) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                  if (m[q]) atomicAdd(&hcopy[(key[kTopkGroup * g + i0 + q] >> shift) & dmask], 1u);
+              }
+            }
+          }
+        }
+      }
+      __syncthreads();
+      // Thread t owns bins 4t..4t+3; `above` counts the bins of the threads
+      // after it, i.e. the larger digits.
+      int h[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int c = 0; c < kTopkCopies; ++c) {
+        uint4* const w = reinterpret_cast<uint4*>(&hist[c * kTopkHistStride + 4 * tid]);
+        const uint4 q = *w;
+        *w = make_uint4(0u, 0u, 0u, 0u);
+        h[0] += int(q.x);
+        h[1] += int(q.y);
+        h[2] += int(q.z);
+        h[3] += int(q.w);
+      }
+      const int mine = h[0] + h[1] + h[2] + h[3];
+      int total;
+      const int incl = block_scan1_topk(mine, red + (pass & 1) * kTopkWaves, total);
+      int above = total - incl;
+      if (above < rem && above + mine >= rem) {
+#pragma unroll
+        for (int b = 3; b >= 0; --b) {
+          if (above < rem && above + h[b] >= rem) {
+            found[pass & 1][0] = 4 * tid + b;
+            found[pass & 1][1] = rem - above;
+          }
+          above += h[b];
+        }
+      }
+      __syncthreads();
+      prefix = (prefix << (pass == 2 ? 10 : 11)) | uint32_t(found[pass & 1][0]);
+      rem = found[pass & 1][1];
+    }
+    const uint32_t T = prefix;
+    const int need = rem;                            // keys equal to T to take, largest positions first
+    // Ballots per slot, gathered 16 slots to a register (lane 4s+q holds word
+    // q of slot s of the group) and stored with one write per group.
+#pragma unroll
+    for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g) {
+      if (g < groups) {
+        uint32_t acc = 0;
+        static_for<0, kTopkGroup / 2>([&](auto ic) {
+          constexpr int i = 2 * decltype(ic)::value;
+          const uint32_t ka = key[kTopkGroup * g + i], kb = key[kTopkGroup * g + i + 1];
+          const uint64_t ga = __ballot(ka > T), ea = __ballot(ka == T);
+          const uint64_t gb = __ballot(kb > T), eb = __ballot(kb == T);
+          acc = write_lanes8<4 * i>(acc, uint32_t(ga), uint32_t(ga >> 32), uint32_t(ea), uint32_t(ea >> 32),
+                                    uint32_t(gb), uint32_t(gb >> 32), uint32_t(eb), uint32_t(eb >> 32));
+        });
+        masks[((kTopkGroup * g + (lane >> 2)) * kTopkWaves + wave) * 4 + (lane & 3)] = acc;
+      }
+    }
+    __syncthreads();
+    // Blocks e = slot * 8 + wave (64 positions each, descending) in order;
+    // thread t scans blocks 2t and 2t+1.  Blocks of groups past the row are 0.
+    const int used = groups * kTopkGroup * kTopkWaves;
+    int pg[2], pq[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = 2 * tid + u;
+      pg[u] = pq[u] = 0;
+      if (e < used) {
+        const uint4 m = *reinterpret_cast<const uint4*>(&masks[4 * e]);
+        pg[u] = __builtin_popcount(m.x) + __builtin_popcount(m.y);
+        pq[u] = __builtin_popcount(m.z) + __builtin_popcount(m.w);
+      }
+    }
+    int ig, iq, tg, tq;
+    block_scan2_topk(pg[0] + pg[1], pq[0] + pq[1], red + 2 * kTopkWaves, ig, iq, tg, tq);
+    const int gb = ig - pg[0] - pg[1], qb = iq - pq[0] - pq[1];
+    // Per block: keys > T and keys == T in the blocks before it.
+    int2* const before = reinterpret_cast<int2*>(hist);
+    before[2 * tid] = make_int2(gb, qb);
+    before[2 * tid + 1] = make_int2(gb + pg[0], qb + pq[0]);
+    __syncthreads();
+    // Output: a selected position's offset is the number of selected positions
+    // above it, = (keys > T above it) + min(need, ties above it).  Quarter
+    // u = 4e + c holds positions 16c .. 16c+15 of block e; thread t writes the
+    // quarters t, t + 512, ...  The stores go through a buffer over the row's
+    // k outputs, so even an offset out of range could not write outside them.
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(o, uint32_t(k) * 4u);
+    uint4 mu[kTopkPerThread / 16];
+    int2 bu[kTopkPerThread / 16];
+#pragma unroll
+    for (int i = 0; i < kTopkPerThread / 16; ++i) {   // every read first, then the writes
+      const int e = (tid + kTopkThreads * i) >> 2;
+      mu[i] = *reinterpret_cast<const uint4*>(&masks[4 * e]);
+      bu[i] = before[e];
+    }
+#pragma unroll
+    for (int i = 0; i < kTopkPerThread / 16; ++i) {
+      const int u = tid + kTopkThreads * i;
+      if (u >= 4 * used) break;
+      const int e = u >> 2, c = u & 3;
+      const uint4 m = mu[i];
+      const uint64_t gm = uint64_t(m.x) | (uint64_t(m.y) << 32), em = uint64_t(m.z) | (uint64_t(m.w) << 32);
+      const uint64_t below = (uint64_t(1) << (16 * c)) - 1;
+      uint32_t gq = uint32_t(gm >> (16 * c)) & 0xFFFFu, eq = uint32_t(em >> (16 * c)) & 0xFFFFu;
+      if ((gq | eq) == 0u) continue;
+      const int2 b = bu[i];
+      const int at_g = b.x + __popcll(gm & below), at_q = b.y + __popcll(em & below);
+      // The quarter's selected positions go to consecutive offsets from the
+      // number selected above it; of its ties, the first need - at_q.
+      const int allow = need - at_q;
+      uint32_t keep = 0u;
+      if (allow > 0) {                               // then keep has more than `drop` bits set
+        keep = eq;
+        for (int drop = __builtin_popcount(eq) - allow; drop > 0; --drop)
+          keep &= ~(0x80000000u >> __builtin_clz(keep));
+      }
+      uint32_t sel = gq | keep;
+      int at = at_g + (at_q < need ? at_q : need);
+      const int top = n - 1 - ((e / kTopkWaves) * kTopkThreads + (e % kTopkWaves) * 64 + 16 * c);
+      while (sel) {
+        const int bit = __builtin_ctz(sel);
+        sel &= sel - 1;
+        __builtin_amdgcn_raw_buffer_store_b32(top - bit, ro, uint32_t(at) * 4u, 0, 0);
+        ++at;
+      }
+    }
+  }
+  for (int i = take + tid; i < k; i += kTopkThreads) o[i] = -1;
+}
+
+}  // namespace
+
+hipError_t launch_topk_positions(const float* scores, int64_t ld, const int32_t* lengths, int64_t R, int k,
+                                 int32_t* out, hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  if (ld < 0 || ld > kTopkMaxLen || k < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(topk_positions_kernel, dim3(unsigned(R)), dim3(kTopkThreads), 0, s, scores, ld, lengths, k,
+                     out);
+  return hipGetLastError();
+}
+
 hipError_t launch_moe(const MoeLaunch& p, hipStream_t s) {
   switch (p.leaves_log2) {
     case 0: return launch_moe_lg<0>(p, s);

@@ -123,6 +123,7 @@ def test_zero_rows_is_a_noop_even_with_null_pointers():
     assert lib.tig_moe_tree_gemm_combine(None, None, 64, None, None, 8, None, 0, 1408, 2048, 8,
                                          None, 0, None) == tig.TIG_OK
     assert lib.tig_moe_route(None, None, None, None, None, 0, 2048, 64, 8, 8, None) == tig.TIG_OK
+    assert lib.tig_topk_positions(None, 65536, None, 0, 2048, None, None) == tig.TIG_OK
 
 
 def test_route_arguments_rejected_before_any_launch():
@@ -137,6 +138,17 @@ def test_route_arguments_rejected_before_any_launch():
     assert lib.tig_moe_route(None, None, None, None, None, 4, 512, 64, 8, 16, None) == tig.TIG_ERR_UNSUPPORTED
     assert lib.tig_moe_route(None, None, None, None, None, -1, 512, 64, 8, 8, None) == tig.TIG_ERR_INVALID_ARG
     assert lib.tig_moe_route(None, None, None, None, None, 4, 512, 64, 8, 8, None) == tig.TIG_ERR_INVALID_ARG
+    assert "NULL" in tig.tig_last_error()
+
+
+def test_topk_arguments_rejected_before_any_launch():
+    lib = _raw()
+    # k < 1; negative R or ld; rows longer than one workgroup holds; NULL pointers
+    assert lib.tig_topk_positions(None, 1024, None, 4, 0, None, None) == tig.TIG_ERR_INVALID_ARG
+    assert lib.tig_topk_positions(None, 1024, None, -1, 8, None, None) == tig.TIG_ERR_INVALID_ARG
+    assert lib.tig_topk_positions(None, -1, None, 4, 8, None, None) == tig.TIG_ERR_INVALID_ARG
+    assert lib.tig_topk_positions(None, 65537, None, 4, 8, None, None) == tig.TIG_ERR_UNSUPPORTED
+    assert lib.tig_topk_positions(None, 65536, None, 4, 2048, None, None) == tig.TIG_ERR_INVALID_ARG
     assert "NULL" in tig.tig_last_error()
 
 

@@ -1,0 +1,128 @@
+"""GPU parity and batch invariance of tig_topk_positions (deterministic Top-K).
+
+[BitRL, section 4.3]: the sparse-attention indexer keeps at most 2048
+positions per query; the selection key is the score together with the
+in-request position, so equal scores go to the larger position, and the
+selected positions are listed by descending position with invalid entries
+last.  The result is integer: every case must match the oracle exactly.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _run(gpu_lib, scores: np.ndarray, lengths: np.ndarray, k: int) -> np.ndarray:
+    s = torch.from_numpy(np.ascontiguousarray(scores, dtype=np.float32)).to(DEV)
+    n = torch.from_numpy(np.ascontiguousarray(lengths, dtype=np.int32)).to(DEV)
+    out = gpu_lib.topk_positions(s, n, k)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.int64)
+
+
+def _check(gpu_lib, scores, lengths, k, what):
+    say(f"topk {what}: R={scores.shape[0]} ld={scores.shape[1]} k={k}")
+    got = _run(gpu_lib, scores, lengths, k)
+    ref = oracle.topk_positions(scores, lengths, k)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, (what, bad[:4].tolist(), got[tuple(bad[0])], ref[tuple(bad[0])])
+    return got
+
+
+@pytest.mark.parametrize("grid,ld,k", [
+    ("bf16", 1000, 7),        # one partial group of slots
+    ("int", 8193, 2048),      # ties everywhere, one position past a full group
+    ("bf16", 513, 2048),      # k above every length: all positions, then -1
+    ("int", 65536, 1),        # k = 1 over the longest rows
+    ("bf16", 4096, 4096),     # k equal to the row length
+    ("f32", 20000, 2048),     # (almost) no ties
+    ("int", 2048, 2047),
+])
+def test_topk_matches_oracle(gpu_lib, grid, ld, k):
+    rng = np.random.default_rng(7000 + ld + k)
+    R = 24
+    scores = wl.indexer_scores(rng, R, ld, grid)
+    edges = [0, 1, 2, k - 1, k, k + 1, ld - 1, ld, 511, 512, 513, 8191, 8192, 8193]
+    lengths = np.array([e for e in edges if 0 <= e <= ld] + list(rng.integers(0, ld + 1, size=R)),
+                       dtype=np.int32)[:R]
+    _check(gpu_lib, scores, lengths, k, f"{grid}")
+
+
+def test_topk_special_values(gpu_lib):
+    """NaN after every number, +0 equal to -0, infinities and the extremes in place."""
+    rng = np.random.default_rng(7100)
+    R, ld, k = 16, 3000, 64
+    scores = wl.indexer_scores(rng, R, ld, "int")
+    specials = np.array([np.nan, 0.0, -0.0, np.inf, -np.inf, np.finfo(np.float32).max,
+                         -np.finfo(np.float32).max, np.finfo(np.float32).tiny, 1e-45, -1e-45], dtype=np.float32)
+    for r in range(R):
+        idx = rng.choice(ld, size=ld // (r + 2), replace=False)
+        scores[r, idx] = rng.choice(specials, size=idx.size)
+    scores[0] = np.nan                              # only NaN: every position ties
+    scores[1] = -0.0
+    scores[1, ::3] = 0.0                            # +0 and -0 tie
+    scores[2, :] = -np.inf
+    scores[2, 100:110] = np.nan                     # NaN below -inf
+    lengths = np.full(R, ld, dtype=np.int32)
+    lengths[3] = 40                                 # fewer than k
+    got = _check(gpu_lib, scores, lengths, k, "special values")
+    assert np.array_equal(got[0], np.arange(ld - 1, ld - 1 - k, -1))
+    assert got[2, -1] == ld - 1 - (k - 1) and 100 not in got[2]
+
+
+def test_topk_lengths_clamped(gpu_lib):
+    """Lengths below 0 count as 0 (all -1), above the row pitch as the pitch."""
+    rng = np.random.default_rng(7200)
+    ld, k = 700, 16
+    scores = wl.indexer_scores(rng, 4, ld)
+    lengths = np.array([-5, 0, ld + 9, 2 ** 31 - 1], dtype=np.int32)
+    got = _run(gpu_lib, scores, lengths, k)
+    assert np.all(got[:2] == -1)
+    clamp = np.clip(lengths, 0, ld)
+    assert np.array_equal(got, oracle.topk_positions(scores, clamp, k))
+
+
+def test_topk_row_position_invariance(gpu_lib):
+    """A request's result depends on its own scores only: not on its row in the
+    batch, its neighbours, the batch size, the row pitch or what lies past its
+    length."""
+    rng = np.random.default_rng(7300)
+    k = 2048
+    reqs = [wl.indexer_scores(rng, 1, n, g)[0] for n, g in
+            ((5000, "bf16"), (65536, "int"), (1234, "bf16"), (30000, "f32"), (2048, "int"))]
+    alone = [_run(gpu_lib, q[None, :], np.array([q.size], np.int32), k)[0] for q in reqs]
+    ld = 65536
+    for trial in range(3):
+        R = 9 + 4 * trial
+        batch = wl.indexer_scores(rng, R, ld, "bf16")   # other requests around them
+        lengths = wl.request_lengths(rng, R, 0, ld)
+        slots = rng.choice(R, size=len(reqs), replace=False)
+        for q, sl in zip(reqs, slots):
+            batch[sl, :q.size] = q
+            batch[sl, q.size:] = rng.standard_normal(ld - q.size)   # garbage past the length
+            lengths[sl] = q.size
+        say(f"topk invariance trial {trial}: R={R} ld={ld}")
+        got = _run(gpu_lib, batch, lengths, k)
+        for q, sl, a in zip(reqs, slots, alone):
+            assert np.array_equal(got[sl], a), (trial, q.size, int(sl))
+        assert np.array_equal(got, oracle.topk_positions(batch, lengths, k))
+
+
+@pytest.mark.slow
+def test_topk_indexer_config(gpu_lib):
+    """The indexer workload the bench times (128 rows, pitch 65536, k = 2048,
+    lengths mixed), every row against the oracle."""
+    c = wl.CONFIGS["indexer"]
+    s = wl.streams(c.seed)
+    scores = wl.indexer_scores(s["scores"], c.tokens, c.N)
+    lengths = wl.request_lengths(s["lengths"], c.tokens, 1, c.N)
+    lengths[:4] = (c.N, c.topk, c.topk - 1, 1)
+    _check(gpu_lib, scores, lengths, c.topk, "indexer config")

@@ -21,7 +21,10 @@ the separate streams, so changing one stream never shifts another):
   sequence origins);
 * MoE routing: router logits N(0, 1) in float64, the top-k experts by logit
   (ties go to the lower expert id), gate weights are the softmax over the k
-  selected logits, stored as float32.
+  selected logits, stored as float32;
+* indexer scores for the Top-K of positions: float32 N(0, 1) draws, by default
+  rounded to bf16 values so that equal scores are common; request lengths
+  uniform in a stated range.
 """
 
 from __future__ import annotations
@@ -41,6 +44,8 @@ __all__ = [
     "route_topk",
     "prefill_decode_rows",
     "integer_bf16",
+    "indexer_scores",
+    "request_lengths",
 ]
 
 
@@ -129,10 +134,14 @@ CONFIGS = {
     # Large: hidden 7168, vocab 129280, 16 leaves; 16384 = 256 sequences x 64.
     "large": Config("large", K=7168, N=129280, leaves=16, seed=1004,
                     M=(16384,), n_seq=256, n_pos=64),
+    # Sparse-attention indexer Top-K: 128 query rows over histories of up to
+    # 65536 positions (N = row pitch), k = 2048 selected per row.
+    "indexer": Config("indexer", K=0, N=65536, leaves=0, seed=1005,
+                      topk=2048, tokens=128),
 }
 
 # Appending keeps every existing stream (child i of the seed sequence is fixed by i).
-_STREAMS = ("H", "W", "ids", "perm", "route", "gumbel", "extra", "router")
+_STREAMS = ("H", "W", "ids", "perm", "route", "gumbel", "extra", "router", "scores", "lengths")
 
 
 def streams(seed: int) -> dict:
@@ -183,3 +192,25 @@ def prefill_decode_rows(n_seq: int, n_pos: int, rng: np.random.Generator | None 
         seqs = np.arange(n_seq) if rng is None else rng.permutation(n_seq)
         steps[t] = seqs * n_pos + t
     return prefill, steps
+
+
+def indexer_scores(rng: np.random.Generator, R: int, n: int, grid: str = "bf16") -> np.ndarray:
+    """Indexer scores, float32 ``[R, n]``, from N(0, 1) draws.
+
+    ``grid="bf16"``: rounded to bf16 values (a few thousand distinct values per
+    row, so equal scores are common); ``"int"``: integers in ``[-4, 4]`` (ties
+    everywhere); ``"f32"``: the float32 draws as they are.
+    """
+    if grid == "int":
+        return rng.integers(-4, 5, size=(R, n)).astype(np.float32)
+    v = rng.standard_normal((R, n), dtype=np.float32)
+    if grid == "f32":
+        return v
+    if grid != "bf16":
+        raise ValueError(grid)
+    return (f32_to_bf16_bits(v).astype(np.uint32) << 16).view(np.float32)
+
+
+def request_lengths(rng: np.random.Generator, R: int, lo: int, hi: int) -> np.ndarray:
+    """Per-row history lengths, int32, uniform in ``[lo, hi]``."""
+    return rng.integers(lo, hi + 1, size=R).astype(np.int32)
