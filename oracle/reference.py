@@ -29,6 +29,16 @@ Readings where the pages leave a step open:
 * R8 a sampled id outside ``[0, V)`` yields NaN for that row only.
 * R12 the MoE combine runs in ascending expert id, ``acc = acc + g*y`` with a
   float32 multiply then a float32 add, each rounded to nearest even.
+* R19 the two expert layouts of section 4.4: masked = a block of ``cap`` rows
+  per expert, expert e's rows at ``e*cap .. e*cap+count_e-1`` (counts above
+  ``cap`` keep their first ``cap`` rows); contiguous = the experts' rows packed
+  in expert order, each expert's segment starting at a multiple of ``align``
+  (the alignment padding of the section's figure; ``align = 1`` packs them).
+  The output of a row sits at the same row index as its input.
+* R20 the activation between the two expert GEMMs (section 4.4, condition 3):
+  ``SiLU(g) * u`` with ``SiLU(g) = g / (1 + exp(-g))``, computed exactly here
+  and rounded to bf16 once, to nearest even; FP8 quantisation after it is not
+  modelled (out of scope).
 * R13 the router: logits are the FP32 leaf-tree contraction of the token with
   the router weight, the same at every batch size ([Bit-consistent RL],
   section 4.1: the router gate uses one FP32-output GEMM at every batch size);
@@ -40,7 +50,8 @@ Parity status:
 
 * ``contraction_ref``, ``lse_ref``, ``log_softmax_ref``, ``logprob_ref``,
   ``moe_ref``, ``route_select``, ``route_gates_ref``, ``route_ref``,
-  ``topk_positions``: plain
+  ``topk_positions``, ``expert_row_starts``, ``expert_gemm_ref``,
+  ``silu_mul_ref``, ``f64_to_bf16_rne``: plain
   definitions in fp64; pinned by brute force (exact rational arithmetic, rank
   counting), closed forms and invariants in ``tests/test_oracle_pins.py``.
 * ``leaf_tree_f32``, ``leaf_tree_gemm_f32``, ``moe_combine_f32``: float32
@@ -72,6 +83,10 @@ __all__ = [
     "route_gates_ref",
     "route_ref",
     "topk_positions",
+    "f64_to_bf16_rne",
+    "expert_row_starts",
+    "expert_gemm_ref",
+    "silu_mul_ref",
     "k3_kl",
 ]
 
@@ -290,6 +305,86 @@ def moe_combine_f32(Y, topk_ids, topk_w) -> np.ndarray:
             term = np.multiply(w[rows, s][:, None], Y[rows, s], dtype=np.float32)
             out = np.add(out, term, dtype=np.float32)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Expert GEMM on two layouts, and the activation between the expert GEMMs
+#   [Bit-consistent RL, section 4.4; readings R19, R20]
+# ---------------------------------------------------------------------------
+
+def f64_to_bf16_rne(x) -> np.ndarray:
+    """Round float64 values to bf16 once, to nearest even; return the uint16 bits.
+
+    bf16 keeps 8 significant bits (exponent range of float32): a normal value
+    ``m * 2**e`` with ``m`` in [0.5, 1) rounds to ``rint(m * 2**8) * 2**(e-8)``,
+    ``rint`` taking halves to even; below the smallest normal, 2**-126, the
+    step is 2**-133.  Values at or past the largest finite bf16 plus half a step
+    become infinities.  The rounding is done on the float64 value itself, not
+    through float32 (which would round twice).
+    """
+    v = np.asarray(x, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.float64)
+    a = np.abs(v)
+    nan = np.isnan(v)
+    small = a < 2.0 ** -126
+    m, e = np.frexp(np.where(small | nan, 1.0, a))
+    normal = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)
+    sub = np.rint(np.where(nan, 0.0, a) * 2.0 ** 133) * 2.0 ** -133
+    out = np.where(small, sub, normal)
+    top = float(np.ldexp(255.0, 120))          # largest finite bf16: (2 - 2**-7) * 2**127
+    out = np.where(out > top, np.inf, out)
+    out = np.copysign(out, v)
+    bits = (out.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    return np.where(nan, np.uint16(0x7FC0), bits).astype(np.uint16)
+
+
+def expert_row_starts(counts, layout: str, cap: int = 0, align: int = 1):
+    """First row of each expert's block (masked) or segment (contiguous).
+
+    Returns ``(starts, rows)``: ``rows[e]`` is the number of expert e's rows the
+    layout holds (``min(count, cap)`` when masked).  Contiguous: expert e starts
+    at the sum over e' < e of ``count_e'`` rounded up to a multiple of ``align``.
+    """
+    c = np.maximum(np.asarray(counts, dtype=np.int64), 0)
+    if layout == "masked":
+        rows = np.minimum(c, cap)
+        starts = np.arange(c.size, dtype=np.int64) * cap
+    elif layout == "contiguous":
+        rows = c
+        padded = -(-c // align) * align
+        starts = np.concatenate([[0], np.cumsum(padded)[:-1]]).astype(np.int64)
+    else:
+        raise ValueError(layout)
+    return starts, rows
+
+
+def expert_gemm_ref(X, counts, W_experts, layout: str, cap: int = 0, align: int = 1):
+    """Expert GEMM on a layout, fp64: ``Y[r] = X[r] . W_e^T`` for every row r
+    the layout gives to expert e; other rows are NaN (not defined)."""
+    X64 = as_f64(X)
+    starts, rows = expert_row_starts(counts, layout, cap, align)
+    E, N, K = np.asarray(W_experts).shape
+    Y = np.full((X64.shape[0], N), np.nan)
+    for e in range(E):
+        if rows[e] == 0:
+            continue
+        sl = slice(int(starts[e]), int(starts[e] + rows[e]))
+        Y[sl] = X64[sl] @ as_f64(W_experts[e]).T
+    return Y
+
+
+def silu_mul_ref(G, U) -> np.ndarray:
+    """``bf16(SiLU(g) * u)`` with one rounding (reading R20); uint16 bits.
+
+    ``SiLU(g) = g / (1 + exp(-g))`` in float64 (for g below -700, where
+    exp(-g) overflows, g * exp(g), which differs from it by less than float64
+    resolves), times u, then ``f64_to_bf16_rne``.
+    """
+    g = np.asarray(G, dtype=np.float64)
+    u = np.asarray(U, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        silu = np.where(g < -700.0, g * np.exp(np.maximum(g, -745.0)), g / (1.0 + np.exp(-g)))
+    return f64_to_bf16_rne(silu * u)
 
 
 # ---------------------------------------------------------------------------

@@ -500,6 +500,158 @@ def test_topk_positions_properties():
 # Gumbel-max sampling and the k3 metric
 # ---------------------------------------------------------------------------
 
+# ---------------------------------------------------------------------------
+# Expert layouts and the activation between the expert GEMMs
+#   [Bit-consistent RL, section 4.4]
+# ---------------------------------------------------------------------------
+
+def _bf16_value(bits: int) -> Fraction:
+    """Exact value of a finite bf16 bit pattern from its fields."""
+    sign = -1 if bits & 0x8000 else 1
+    ex, man = (bits >> 7) & 0xFF, bits & 0x7F
+    if ex == 0:
+        return sign * Fraction(man, 1 << 7) * Fraction(1, 1 << 126)
+    return sign * (1 + Fraction(man, 1 << 7)) * (Fraction(2) ** (ex - 127))
+
+
+def _bf16_round_exact(x: Fraction) -> int:
+    """Nearest bf16 to the rational x (halves to the even pattern), by looking
+    at the patterns around it: independent of any floating-point rounding."""
+    if x == 0:
+        return 0
+    neg = x < 0
+    a = -x if neg else x
+    # the largest non-negative pattern not above a (patterns of one sign are ordered)
+    lo, hi = 0, 0x7F7F
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        if _bf16_value(mid) <= a:
+            lo = mid
+        else:
+            hi = mid - 1
+    if lo == 0x7F7F:
+        half = (_bf16_value(0x7F7F) - _bf16_value(0x7F7E)) / 2
+        b = 0x7F80 if a >= _bf16_value(0x7F7F) + half else 0x7F7F
+    else:
+        d0, d1 = a - _bf16_value(lo), _bf16_value(lo + 1) - a
+        b = lo if d0 < d1 else (lo + 1 if d1 < d0 else (lo if lo % 2 == 0 else lo + 1))
+    return b | (0x8000 if neg else 0)
+
+
+def test_f64_to_bf16_fixed_points():
+    x = np.array([1.0, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -30, -2.5, 0.0, -0.0,
+                  1e-40, np.inf, -np.inf, 3.39e38, 3.4e38])
+    want = [0x3F80, 0x3F80, 0x3F82, 0x3F81, 0xC020, 0x0000, 0x8000, 0x0001, 0x7F80, 0xFF80, 0x7F7F, 0x7F80]
+    assert oracle.f64_to_bf16_rne(x).tolist() == want
+    # one rounding: through float32 first, 1 + 2^-8 + 2^-30 would become the tie 1 + 2^-8 and then 1.0
+    assert np.float32(1 + 2.0 ** -8 + 2.0 ** -30) == np.float32(1 + 2.0 ** -8)
+    assert oracle.f64_to_bf16_rne(np.array([np.nan]))[0] & 0x7FFF > 0x7F80
+
+
+def test_f64_to_bf16_matches_exact_rounding():
+    rng = np.random.default_rng(1900)
+    x = np.concatenate([rng.standard_normal(300) * 10.0 ** rng.integers(-40, 38, 300),
+                        rng.standard_normal(50) * 1e-39])
+    got = oracle.f64_to_bf16_rne(x)
+    for v, b in zip(x.tolist(), got.tolist()):
+        assert b == _bf16_round_exact(Fraction(v)), v
+
+
+def _silu_mul_decimal(g: float, u: float) -> Fraction:
+    import decimal
+    with decimal.localcontext() as ctx:
+        ctx.prec = 60
+        dg = decimal.Decimal(g)
+        val = dg / (1 + (-dg).exp()) * decimal.Decimal(u)
+    return Fraction(val)
+
+
+def test_silu_mul_against_high_precision():
+    """SiLU(g)*u from 60-digit decimal arithmetic, rounded exactly: the oracle
+    agrees except where the value lies within 1e-12 (relative) of a rounding
+    midpoint, which no case here does."""
+    rng = np.random.default_rng(1901)
+    g = np.concatenate([rng.standard_normal(400) * 3, [0.0, 30.0, -30.0, 80.0, -80.0, 1e-3]])
+    u = np.concatenate([rng.standard_normal(400) * 2, [1.5, -1.0, 1.0, 0.5, 2.0, -7.0]])
+    got = oracle.silu_mul_ref(g, u)
+    checked = 0
+    for gi, ui, b in zip(g.tolist(), u.tolist(), got.tolist()):
+        exact = _silu_mul_decimal(gi, ui)
+        r = _bf16_round_exact(exact)
+        if r & 0x7FFF not in (0, 0x7F80):
+            nb = r + 1 if (exact > 0) == (r < 0x8000) else r - 1
+            mid = (_bf16_value(r) + _bf16_value(nb)) / 2
+            if abs(exact - mid) <= abs(exact) * Fraction(1, 10 ** 12):
+                continue
+        assert b == r, (gi, ui, hex(b), hex(r))
+        checked += 1
+    assert checked >= 400
+
+
+def test_silu_mul_closed_forms():
+    ln3 = math.log(3.0)
+    # sigma(ln 3) = 3/4: SiLU(ln 3) = 0.75 ln 3 = 0.82396...; bf16 step on [0.5, 1) is 2^-8: 211/256
+    b = oracle.silu_mul_ref(np.array([ln3]), np.array([1.0]))[0]
+    assert _bf16_value(int(b)) == Fraction(211, 256)
+    z = oracle.silu_mul_ref(np.array([0.0, 0.0]), np.array([5.0, -5.0]))
+    assert z.tolist() == [0x0000, 0x8000]                    # 0 * u keeps the sign of u
+    big = oracle.silu_mul_ref(np.array([100.0, -100.0]), np.array([1.0, 1.0]))
+    assert big[0] == 0x42C8                                  # SiLU(100) = 100 to far below a bf16 step
+    # SiLU(-100) = -100 e^-100 = -3.7e-42, below half the smallest bf16 subnormal (2^-134): -0
+    assert big[1] == 0x8000
+    # SiLU(-95) = -95 e^-95 = -5.5e-40 = -6.0 steps of 2^-133: the subnormal pattern 6
+    assert oracle.silu_mul_ref(np.array([-95.0]), np.array([1.0]))[0] == 0x8006
+
+
+def test_silu_mul_rounds_once_not_twice():
+    """Rounding SiLU to bf16 before the multiply changes some results by one
+    step (the section's point); the oracle follows the one rounding."""
+    rng = np.random.default_rng(1902)
+    g = rng.standard_normal(2000) * 2
+    u = np.full(2000, 3.0)
+    once = oracle.silu_mul_ref(g, u)
+    silu = g / (1.0 + np.exp(-g))
+    twice = oracle.f64_to_bf16_rne(oracle.bf16_bits_to_f64(oracle.f64_to_bf16_rne(silu)) * 3.0)
+    diff = np.flatnonzero(once != twice)
+    assert diff.size > 20
+    for i in diff[:20]:
+        assert once[i] == _bf16_round_exact(_silu_mul_decimal(float(g[i]), 3.0))
+
+
+def test_expert_row_starts_closed_forms():
+    s, r = oracle.expert_row_starts([3, 0, 130, 1], "contiguous", align=128)
+    assert s.tolist() == [0, 128, 128, 384] and r.tolist() == [3, 0, 130, 1]
+    s, r = oracle.expert_row_starts([3, 0, 130, 1], "contiguous", align=1)
+    assert s.tolist() == [0, 3, 3, 133]
+    s, r = oracle.expert_row_starts([3, 0, 130, 1, -2], "masked", cap=100)
+    assert s.tolist() == [0, 100, 200, 300, 400] and r.tolist() == [3, 0, 100, 1, 0]
+
+
+def test_expert_gemm_ref_brute_force():
+    rng = np.random.default_rng(1903)
+    E, N, K = 3, 5, 6
+    W = wl.integer_bf16(rng, (E, N, K), -3, 3)
+    for layout, cap, align in (("masked", 4, 1), ("contiguous", 0, 4), ("contiguous", 0, 1)):
+        counts = [2, 0, 4]
+        starts, rows = oracle.expert_row_starts(counts, layout, cap, align)
+        M = int(max(starts + np.maximum(rows, 1)))
+        X = wl.integer_bf16(rng, (M, K), -4, 4)
+        Y = oracle.expert_gemm_ref(X, counts, W, layout, cap, align)
+        owner = {}
+        for e in range(E):
+            for i in range(int(rows[e])):
+                owner[int(starts[e]) + i] = e
+        Xv = oracle.bf16_bits_to_f64(X)
+        Wv = oracle.bf16_bits_to_f64(W)
+        for m in range(M):
+            if m not in owner:
+                assert np.all(np.isnan(Y[m]))
+                continue
+            for n in range(N):
+                exact = sum(Fraction(Xv[m, k]) * Fraction(Wv[owner[m], n, k]) for k in range(K))
+                assert Y[m, n] == exact
+
+
 def test_gumbel_max_samples_the_softmax():
     rng = np.random.default_rng(14)
     n = 200_000
