@@ -252,7 +252,44 @@ def main():
         moe = {"ms": ms, "shape": f"T={c.tokens} E={c.experts} top{c.topk} K={c.K} N={c.N} leaves={c.leaves}",
                "roofline": mfma_line(2.0 * c.tokens * c.topk * c.K * c.N, ms)}
         log(f"moe: {ms * 1e3:.1f} us, {moe['roofline']['achieved']:.0f} TFLOP/s")
-        del We, out, wsm
+        del out, wsm
+
+        # The same routed rows (32768 = 4096 tokens x top-8) as an expert GEMM on the
+        # masked layout (cap = the largest count rounded up to 64) and the contiguous
+        # one (segments aligned to 128), then SiLU * up on a [32768, 2 x 1408] FP32
+        # gate/up output.
+        order = np.argsort(tid.cpu().numpy().reshape(-1), kind="stable")
+        cnt = np.bincount(tid.cpu().numpy().reshape(-1), minlength=c.experts).astype(np.int32)
+        tok = torch.from_numpy(order // c.topk).to(dev)
+        cap = int(-(-cnt.max() // 64) * 64)
+        starts = np.concatenate([[0], np.cumsum(-(-cnt // 128) * 128)[:-1]])
+        Mc = int(starts[-1] + cnt[-1])
+        Xc = torch.zeros(Mc, c.K, dtype=torch.bfloat16, device=dev)
+        Xm = torch.zeros(c.experts, cap, c.K, dtype=torch.bfloat16, device=dev)
+        first = np.concatenate([[0], np.cumsum(cnt)[:-1]])
+        for e in range(c.experts):
+            rows = Hm[tok[first[e]:first[e] + cnt[e]]]
+            Xc[starts[e]:starts[e] + cnt[e]] = rows
+            Xm[e, :cnt[e]] = rows
+        cntd = torch.from_numpy(cnt).to(dev)
+        flops = 2.0 * float(cnt.sum()) * c.K * c.N
+        Ym = torch.empty(c.experts, cap, c.N, dtype=torch.float32, device=dev)
+        Yc = torch.empty(Mc, c.N, dtype=torch.float32, device=dev)
+        wse = torch.empty(tig.tig_expert_workspace_bytes(max(Mc, c.experts * cap), c.experts), dtype=torch.uint8,
+                          device=dev)
+        expert = {"shape": f"rows={int(cnt.sum())} E={c.experts} K={c.K} N={c.N} leaves={c.leaves} cap={cap}"}
+        ms, _ = timed(lambda: tig.tig_expert_gemm_masked(Xm, cntd, We, Ym, c.leaves, wse), 20, 3)
+        expert["masked"] = {"ms": ms, "roofline": mfma_line(flops, ms)}
+        ms, _ = timed(lambda: tig.tig_expert_gemm_contiguous(Xc, cntd, We, Yc, 128, c.leaves, wse), 20, 3)
+        expert["contiguous"] = {"ms": ms, "roofline": mfma_line(flops, ms)}
+        GU = torch.randn(int(cnt.sum()), 2 * c.N, device=dev)
+        act = torch.empty(int(cnt.sum()), c.N, dtype=torch.bfloat16, device=dev)
+        ms, _ = timed(lambda: tig.tig_silu_mul(GU, act), 50, 3)
+        expert["silu_mul"] = {"us": ms * 1e3, "roofline": hbm_line(10.0 * act.numel(), ms)}
+        moe["expert"] = expert
+        log(f"expert gemm masked {expert['masked']['ms'] * 1e3:.1f} us, contiguous "
+            f"{expert['contiguous']['ms'] * 1e3:.1f} us; silu_mul {expert['silu_mul']['us']:.1f} us")
+        del We, Xc, Xm, Ym, Yc, GU, act, wse
 
         # The router of the same layer on the GPU: FP32 logits (4096 x 64, K = 2048,
         # 8 leaves), top-8 and gates.  Bound by reading H once.

@@ -171,6 +171,53 @@ tig_status tig_moe_route(const void* H, const void* Wr, float* logits, int32_t* 
                          int32_t leaves, hipStream_t stream);
 
 /*
+ * Expert GEMM on two layouts with the same per-row result, [BitRL, 4.4]: the
+ * rollout side feeds the experts a masked layout (a fixed-capacity block per
+ * expert), the training side a contiguous one (experts packed in order, with
+ * alignment padding); a row's result must not depend on which, nor on the
+ * other rows.  Here every expert's rows are cut into m-tiles that run the
+ * leaf-tree contraction of tig_tree_gemm against that expert's W slice:
+ *   Y[r] = leaf-tree(X[r] W[e]^T) for every row r the layout gives to expert e,
+ * bit for bit the row tig_tree_gemm gives for X[r] alone against W[e].
+ *   X       bf16 [rows, K] contiguous; W bf16 [n_experts, N, K] contiguous
+ *   counts  int32 [n_experts] on the device: rows of each expert (below 0
+ *           counts as 0)
+ *   Y       [rows, N] contiguous, FP32 or bf16 (RNE of the FP32 value); rows
+ *           no expert owns are not written
+ *   workspace >= tig_expert_workspace_bytes(rows, n_experts), 256-byte
+ *           aligned (the work items, built on the device: nothing is read back)
+ * Masked: rows = n_experts * cap; expert e owns rows e*cap .. e*cap +
+ * min(count, cap) - 1.  Contiguous: expert e owns count_e rows from the sum
+ * over e' < e of count_e' rounded up to a multiple of `align`; rows that would
+ * lie at or past M are not computed.  Implemented: n_experts <= 1024,
+ * leaves <= 16, K/leaves a multiple of 64, K a multiple of 8.
+ */
+tig_status tig_expert_gemm_masked(const void* X, const int32_t* counts, const void* W, void* Y,
+                                  tig_out_dtype out_dtype, int32_t n_experts, int64_t cap, int64_t N,
+                                  int64_t K, int32_t leaves, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+tig_status tig_expert_gemm_contiguous(const void* X, const int32_t* counts, int64_t align, const void* W,
+                                      void* Y, tig_out_dtype out_dtype, int32_t n_experts, int64_t M,
+                                      int64_t N, int64_t K, int32_t leaves, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of the expert GEMMs over `rows` rows (written to *bytes). */
+tig_status tig_expert_workspace_bytes(int64_t rows, int32_t n_experts, size_t* bytes);
+
+/*
+ * The activation between the two expert GEMMs, [BitRL, 4.4] condition 3:
+ * SiLU(gate) * up computed in FP32 and rounded to bf16 once (rounding SiLU
+ * first can move the product by one bf16 step).
+ *   GU   float [rows, ldgu]: gate in columns 0 .. I-1, up in I .. 2I-1
+ *   out  bf16 [rows, ldo]: out[r, i] = RNE_bf16(SiLU(g) * u), SiLU(g) =
+ *        g * sigmoid(g), sigmoid(g) = 1/(1+t) for g >= 0 and t/(1+t) below,
+ *        t = 2^(-|g| log2 e) (hardware exp2), each step an FP32 operation
+ * Needs ldgu >= 2I, ldo >= I.  rows == 0 or I == 0 is TIG_OK.
+ */
+tig_status tig_silu_mul(const float* GU, int64_t ldgu, void* out, int64_t ldo, int64_t rows, int64_t I,
+                        hipStream_t stream);
+
+/*
  * Deterministic Top-K of positions, [BitRL, 4.3] (the sparse-attention
  * indexer's selection and the figure of its 64-bit key): row r's candidates
  * are its positions 0 .. lengths[r]-1; a position is ahead of another when

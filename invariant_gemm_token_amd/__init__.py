@@ -21,9 +21,11 @@ __all__ = [
     "TigError", "load", "lib_path",
     "tig_tree_gemm", "tig_logprob_gather", "tig_logprob_workspace_bytes",
     "tig_moe_tree_gemm_combine", "tig_moe_workspace_bytes", "tig_moe_route", "tig_topk_positions",
+    "tig_expert_gemm_masked", "tig_expert_gemm_contiguous", "tig_expert_workspace_bytes", "tig_silu_mul",
     "tig_plan_describe",
     "tig_status_string", "tig_last_error",
     "tree_gemm", "logprob_gather", "moe_tree_gemm_combine", "moe_route", "topk_positions",
+    "expert_gemm_masked", "expert_gemm_contiguous", "silu_mul",
     "TIG_OK", "TIG_ERR_INVALID_ARG", "TIG_ERR_UNSUPPORTED", "TIG_ERR_WORKSPACE", "TIG_ERR_HIP",
     "TIG_OUT_F32", "TIG_OUT_BF16",
 ]
@@ -65,6 +67,11 @@ _SIGNATURES = {
     "tig_moe_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, _i32, ctypes.POINTER(_sz)]),
     "tig_moe_route": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _i32, _vp]),
     "tig_topk_positions": (_i32, [_vp, _i64, _vp, _i64, _i32, _vp, _vp]),
+    "tig_expert_gemm_masked": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
+    "tig_expert_gemm_contiguous": (_i32, [_vp, _vp, _i64, _vp, _vp, _i32, _i32, _i64, _i64, _i64, _i32, _vp, _sz,
+                                          _vp]),
+    "tig_expert_workspace_bytes": (_i32, [_i64, _i32, ctypes.POINTER(_sz)]),
+    "tig_silu_mul": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64, _vp]),
     "tig_plan_describe": (_i32, [_i64, _i32, ctypes.POINTER(_Plan)]),
     "tig_status_string": (ctypes.c_char_p, [_i32]),
     "tig_last_error": (ctypes.c_char_p, []),
@@ -261,6 +268,72 @@ def tig_moe_route(H, Wr, logits, topk_ids, topk_w, leaves: int, stream=None) -> 
     _check(st, "tig_moe_route")
 
 
+def tig_expert_workspace_bytes(rows: int, n_experts: int) -> int:
+    out = _sz(0)
+    _check(load().tig_expert_workspace_bytes(int(rows), int(n_experts), ctypes.byref(out)),
+           "tig_expert_workspace_bytes")
+    return int(out.value)
+
+
+def _expert_args(X, counts, W, Y):
+    torch = _torch()
+    _need(X, "X", torch.bfloat16, X.dim())
+    _need(W, "W", torch.bfloat16, 3)
+    _need(counts, "counts", torch.int32, 1)
+    if Y.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("Y must be float32 or bfloat16")
+    _same_device(X, W, counts, Y)
+    for t, n in ((X, "X"), (W, "W"), (counts, "counts"), (Y, "Y")):
+        _contig(t, n)
+    E, N, K = W.shape
+    if counts.shape[0] != E:
+        raise ValueError("counts must have one entry per expert")
+    if X.shape[-1] != K or Y.shape[-1] != N or X.shape[:-1] != Y.shape[:-1]:
+        raise ValueError(f"shapes do not match: X {tuple(X.shape)}, W {tuple(W.shape)}, Y {tuple(Y.shape)}")
+    return E, N, K, (TIG_OUT_F32 if Y.dtype == torch.float32 else TIG_OUT_BF16)
+
+
+def tig_expert_gemm_masked(X, counts, W, Y, leaves: int, workspace, stream=None) -> None:
+    """Masked layout: X ``[E, cap, K]``, Y ``[E, cap, N]``; expert e's first counts[e] rows of its block."""
+    if X.dim() != 3:
+        raise ValueError("X must be [n_experts, cap, K]")
+    E, N, K, od = _expert_args(X, counts, W, Y)
+    if X.shape[0] != E:
+        raise ValueError("X must have one block per expert")
+    st = load().tig_expert_gemm_masked(X.data_ptr(), counts.data_ptr(), W.data_ptr(), Y.data_ptr(), od, E,
+                                       X.shape[1], N, K, int(leaves), workspace.data_ptr(), workspace.numel(),
+                                       _stream(stream))
+    _check(st, "tig_expert_gemm_masked")
+
+
+def tig_expert_gemm_contiguous(X, counts, W, Y, align: int, leaves: int, workspace, stream=None) -> None:
+    """Contiguous layout: X ``[M, K]``, Y ``[M, N]``; experts packed in order, segments aligned to ``align``."""
+    if X.dim() != 2:
+        raise ValueError("X must be [M, K]")
+    E, N, K, od = _expert_args(X, counts, W, Y)
+    st = load().tig_expert_gemm_contiguous(X.data_ptr(), counts.data_ptr(), int(align), W.data_ptr(),
+                                           Y.data_ptr(), od, E, X.shape[0], N, K, int(leaves),
+                                           workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _check(st, "tig_expert_gemm_contiguous")
+
+
+def tig_silu_mul(GU, out, stream=None) -> None:
+    """``out[r, i] = bf16(SiLU(GU[r, i]) * GU[r, I + i])`` computed in FP32, one rounding."""
+    torch = _torch()
+    _need(GU, "GU", torch.float32, 2)
+    _need(out, "out", torch.bfloat16, 2)
+    _same_device(GU, out)
+    _rowmajor(GU, "GU")
+    _rowmajor(out, "out")
+    rows, I = out.shape
+    if GU.shape[0] != rows or GU.shape[1] != 2 * I:
+        raise ValueError("GU must be [rows, 2 I] for out [rows, I]")
+    ldgu = GU.stride(0) if rows > 1 else 2 * I
+    ldo = out.stride(0) if rows > 1 else I
+    st = load().tig_silu_mul(GU.data_ptr(), ldgu, out.data_ptr(), ldo, rows, I, _stream(stream))
+    _check(st, "tig_silu_mul")
+
+
 def tig_topk_positions(scores, lengths, out, stream=None) -> None:
     """Top-k positions per row by (score, position), listed by descending position, -1 padded."""
     torch = _torch()
@@ -340,4 +413,38 @@ def topk_positions(scores, lengths, k: int, stream=None):
     torch = _torch()
     out = torch.empty((scores.shape[0], int(k)), dtype=torch.int32, device=scores.device)
     tig_topk_positions(scores, lengths, out, stream)
+    return out
+
+
+def _expert_ws(rows, n_experts, device, workspace):
+    torch = _torch()
+    need = tig_expert_workspace_bytes(rows, n_experts)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def expert_gemm_masked(X, counts, W, leaves: int, out_dtype=None, workspace=None, stream=None):
+    """Allocate and return Y ``[E, cap, N]`` of tig_expert_gemm_masked."""
+    torch = _torch()
+    E, cap = X.shape[0], X.shape[1]
+    Y = torch.empty((E, cap, W.shape[1]), dtype=out_dtype or torch.float32, device=X.device)
+    tig_expert_gemm_masked(X, counts, W, Y, leaves, _expert_ws(E * cap, E, X.device, workspace), stream)
+    return Y
+
+
+def expert_gemm_contiguous(X, counts, W, align: int, leaves: int, out_dtype=None, workspace=None, stream=None):
+    """Allocate and return Y ``[M, N]`` of tig_expert_gemm_contiguous."""
+    torch = _torch()
+    Y = torch.empty((X.shape[0], W.shape[1]), dtype=out_dtype or torch.float32, device=X.device)
+    tig_expert_gemm_contiguous(X, counts, W, Y, align, leaves,
+                               _expert_ws(X.shape[0], W.shape[0], X.device, workspace), stream)
+    return Y
+
+
+def silu_mul(GU, stream=None):
+    """Allocate and return the bf16 ``[rows, I]`` output of tig_silu_mul."""
+    torch = _torch()
+    out = torch.empty((GU.shape[0], GU.shape[1] // 2), dtype=torch.bfloat16, device=GU.device)
+    tig_silu_mul(GU, out, stream)
     return out

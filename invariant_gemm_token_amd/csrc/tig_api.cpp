@@ -299,6 +299,83 @@ tig_status tig_moe_route(const void* H, const void* Wr, float* logits, int32_t* 
   return ok();
 }
 
+tig_status tig_expert_workspace_bytes(int64_t rows, int32_t n_experts, size_t* bytes) {
+  if (!bytes) return fail(TIG_ERR_INVALID_ARG, "bytes is NULL");
+  if (rows < 0) return fail(TIG_ERR_INVALID_ARG, "rows must be >= 0");
+  if (n_experts < 1) return fail(TIG_ERR_INVALID_ARG, "n_experts must be >= 1");
+  if (n_experts > tig::kMaxGroupExperts)
+    return fail(TIG_ERR_UNSUPPORTED, "n_experts > %d not implemented", tig::kMaxGroupExperts);
+  *bytes = tig::group_ws_bytes(rows, n_experts);
+  return ok();
+}
+
+// Shared checks and launch of the two expert-GEMM layouts.
+static tig_status expert_gemm(bool masked, const void* X, const int32_t* counts, const void* W, void* Y,
+                              tig_out_dtype out_dtype, int32_t n_experts, int64_t rows, int64_t cap,
+                              int64_t align, int64_t N, int64_t K, int32_t leaves, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  size_t need = 0;
+  tig_status s = tig_expert_workspace_bytes(rows < 0 ? 0 : rows, n_experts, &need);
+  if (s != TIG_OK) return s;
+  if (rows < 0 || N < 0) return fail(TIG_ERR_INVALID_ARG, "row count and N must be >= 0");
+  if ((s = check_k_leaves(K, leaves)) != TIG_OK) return s;
+  if (out_dtype != TIG_OUT_F32 && out_dtype != TIG_OUT_BF16)
+    return fail(TIG_ERR_INVALID_ARG, "unknown out_dtype %d", int(out_dtype));
+  if (rows >= (int64_t(1) << 31) - 256) return fail(TIG_ERR_UNSUPPORTED, "too many rows");
+  if (rows == 0 || N == 0) return ok();
+  if (!X || !counts || !W || !Y) return fail(TIG_ERR_INVALID_ARG, "X, counts, W and Y must not be NULL");
+  if (!aligned(X, 16) || !aligned(W, 16) || K % 8)
+    return fail(TIG_ERR_UNSUPPORTED, "X and W must be 16-byte aligned with K a multiple of 8");
+  if (!aligned(counts, 4) || !aligned(Y, out_dtype == TIG_OUT_F32 ? 4 : 2))
+    return fail(TIG_ERR_INVALID_ARG, "counts or Y misaligned");
+  if ((s = check_span("X tile", 192, K)) != TIG_OK) return s;
+  if ((s = check_span("W tile", tig::kBlockN, K)) != TIG_OK) return s;
+  if (tig::group_max_items(rows, n_experts) * tig::cdiv(N, tig::kBlockN) >= (int64_t(1) << 31) - 8)
+    return fail(TIG_ERR_UNSUPPORTED, "too many output tiles");
+  if (!workspace || workspace_bytes < need)
+    return fail(TIG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : size_t(0));
+  if (!aligned(workspace, 256)) return fail(TIG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  tig::GroupLaunch p{X, counts, W, Y, out_dtype == TIG_OUT_F32 ? tig::kEpiF32 : tig::kEpiBF16, masked, rows, cap,
+                     align, N, K, n_experts, log2i(leaves), reinterpret_cast<int32_t*>(ws),
+                     reinterpret_cast<int32_t*>(ws + 256)};
+  const hipError_t e = tig::launch_group_gemm(p, stream);
+  if (e != hipSuccess) return fail(TIG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+tig_status tig_expert_gemm_masked(const void* X, const int32_t* counts, const void* W, void* Y,
+                                  tig_out_dtype out_dtype, int32_t n_experts, int64_t cap, int64_t N, int64_t K,
+                                  int32_t leaves, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (cap < 0) return fail(TIG_ERR_INVALID_ARG, "cap must be >= 0");
+  if (n_experts >= 1 && cap > ((int64_t(1) << 31) - 256) / n_experts)
+    return fail(TIG_ERR_UNSUPPORTED, "n_experts * cap too large");
+  return expert_gemm(true, X, counts, W, Y, out_dtype, n_experts, int64_t(n_experts < 0 ? 0 : n_experts) * cap,
+                     cap, 1, N, K, leaves, workspace, workspace_bytes, stream);
+}
+
+tig_status tig_expert_gemm_contiguous(const void* X, const int32_t* counts, int64_t align, const void* W, void* Y,
+                                      tig_out_dtype out_dtype, int32_t n_experts, int64_t M, int64_t N, int64_t K,
+                                      int32_t leaves, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+  if (align < 1 || align > (int64_t(1) << 20)) return fail(TIG_ERR_INVALID_ARG, "align must be in [1, 2^20]");
+  return expert_gemm(false, X, counts, W, Y, out_dtype, n_experts, M, 0, align, N, K, leaves, workspace,
+                     workspace_bytes, stream);
+}
+
+tig_status tig_silu_mul(const float* GU, int64_t ldgu, void* out, int64_t ldo, int64_t rows, int64_t I,
+                        hipStream_t stream) {
+  if (rows < 0 || I < 0) return fail(TIG_ERR_INVALID_ARG, "rows and I must be >= 0");
+  if (ldgu < 2 * I || ldo < I) return fail(TIG_ERR_INVALID_ARG, "ldgu must be >= 2 I and ldo >= I");
+  if (rows == 0 || I == 0) return ok();
+  if (!GU || !out) return fail(TIG_ERR_INVALID_ARG, "GU and out must not be NULL");
+  if (!aligned(GU, 4) || !aligned(out, 2)) return fail(TIG_ERR_INVALID_ARG, "GU or out misaligned");
+  const hipError_t e = tig::launch_silu_mul(GU, ldgu, static_cast<uint16_t*>(out), ldo, rows, I, stream);
+  if (e != hipSuccess) return fail(TIG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 tig_status tig_topk_positions(const float* scores, int64_t ld, const int32_t* lengths, int64_t R,
                               int32_t k, int32_t* out, hipStream_t stream) {
   if (R < 0 || ld < 0) return fail(TIG_ERR_INVALID_ARG, "R and ld must be >= 0");

@@ -125,10 +125,35 @@ inline size_t moe_ws_bytes(int64_t T, int64_t N, int n_experts, int topk) {
   return moe_ws_layout(T, N, n_experts, topk).total;
 }
 
+// Expert GEMM on the masked or contiguous layout: per expert, its rows of X
+// times its W slice, output rows at the input rows' indices.
+constexpr int kMaxGroupExperts = 1024;
+struct GroupLaunch {
+  const void* X; const int32_t* counts; const void* W; void* Y;
+  int epi;                 // kEpiF32 or kEpiBF16
+  bool masked;
+  int64_t rows;            // rows of X and Y (masked: n_experts * cap)
+  int64_t cap, align;      // masked: rows per expert block; contiguous: segment alignment
+  int64_t N, K;
+  int n_experts, leaves_log2;
+  int32_t* n_items;        // workspace: [1] number of work items
+  int32_t* items;          // workspace: [max items][4]: expert, first row, rows, 0
+};
+inline int64_t group_max_items(int64_t rows, int n_experts) {
+  return cdiv(rows, kBlockM) + n_experts;   // m-tiles of 128 or more rows, one partial per expert
+}
+inline size_t group_ws_bytes(int64_t rows, int n_experts) {
+  return 256 + align256(size_t(group_max_items(rows, n_experts)) * 16);
+}
+
 // Launchers: enqueue on `stream`, return the first HIP error (hipSuccess if none).
 hipError_t launch_tree_gemm(const TreeGemmLaunch& p, hipStream_t stream);
 hipError_t launch_logprob(const LogprobLaunch& p, hipStream_t stream);
 hipError_t launch_moe(const MoeLaunch& p, hipStream_t stream);
+hipError_t launch_group_gemm(const GroupLaunch& p, hipStream_t stream);
+// out[r, i] = bf16(SiLU(g) * u) in FP32, g = GU[r, i], u = GU[r, I + i], one rounding.
+hipError_t launch_silu_mul(const float* GU, int64_t ldgu, uint16_t* out, int64_t ldo, int64_t rows, int64_t I,
+                           hipStream_t stream);
 // Deterministic Top-K of positions: one workgroup of kTopkThreads per row,
 // kTopkPerThread scores per thread in registers.
 constexpr int kTopkThreads = 512, kTopkPerThread = 128;

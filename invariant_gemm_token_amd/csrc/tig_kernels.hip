@@ -1226,6 +1226,145 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const int32_t* __restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Expert GEMM on two layouts [BitRL, 4.4]: the rows of expert e are a block
+// of `cap` rows at e * cap (masked) or a segment in expert order whose start
+// is a multiple of `align` (contiguous).  Each expert's rows are cut into
+// m-tiles (work items); every tile runs the dense leaf-tree pipeline on its
+// rows with the expert's W slice, so a row's result depends on its own values
+// and the expert only, never on the layout or on the other rows.
+// ---------------------------------------------------------------------------
+constexpr int GROUP_PLAN_THREADS = 1024;
+
+// Exclusive prefix sum over the workgroup's threads in thread order, and the total.
+__device__ __forceinline__ int64_t block_excl_i64(int64_t v, int64_t* red, int64_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) {
+    const int64_t o = __shfl_up(x, d);
+    if (lane >= d) x += o;
+  }
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  int64_t before = 0, all = 0;
+  for (int w = 0; w < int(blockDim.x >> 6); ++w) {
+    before += w < wave ? red[w] : 0;
+    all += red[w];
+  }
+  total = all;
+  return before + x - v;
+}
+
+// One workgroup: thread e places expert e's rows and writes its work items
+// (expert, first row, rows, 0), the experts' items in expert order.  Rows that
+// would lie past the buffer's `rows` rows are not computed.
+__global__ __launch_bounds__(GROUP_PLAN_THREADS) void group_plan_kernel(const int32_t* __restrict__ counts,
+                                                                        int n_experts, bool masked, int64_t cap,
+                                                                        int64_t align, int64_t rows, int bm,
+                                                                        int4* __restrict__ items,
+                                                                        int32_t* __restrict__ n_items) {
+  __shared__ int64_t red[GROUP_PLAN_THREADS / 64];
+  const int e = threadIdx.x;
+  int64_t c = e < n_experts ? counts[e] : 0;
+  c = c < 0 ? 0 : c;
+  int64_t start;
+  if (masked) {
+    c = c < cap ? c : cap;
+    start = int64_t(e) * cap;
+  } else {
+    int64_t total;
+    start = block_excl_i64((c + align - 1) / align * align, red, total);
+    __syncthreads();
+  }
+  const int64_t fit = rows - start;
+  c = c < fit ? c : (fit > 0 ? fit : 0);
+  const int64_t tiles = (c + bm - 1) / bm;
+  int64_t n_all;
+  const int64_t first = block_excl_i64(tiles, red, n_all);
+  for (int64_t t = 0; t < tiles; ++t) {
+    const int64_t r0 = t * bm;
+    items[first + t] = make_int4(e, int(start + r0), int(c - r0 < bm ? c - r0 : bm), 0);
+  }
+  if (threadIdx.x == 0) *n_items = int32_t(n_all);
+}
+
+// Work item i: rows X[row0 .. row0+rows) of expert e against W[e].
+struct GroupOperands {
+  const uint16_t* X; const uint16_t* W; void* Y; const int4* items;
+  int64_t N, K;
+};
+
+template <int MI>
+struct GroupLoader : Loader<MI> {
+  GroupOperands g;
+  __device__ __forceinline__ void setup(int item, int nt) {
+    const CONST_AS int32_t* it = (const CONST_AS int32_t*)g.items + 4 * item;
+    const int e = it[0], row0 = it[1], rows = it[2];
+    this->op = DenseOperands{g.X + int64_t(row0) * g.K, g.K, rows, g.W + int64_t(e) * g.N * g.K, g.K, g.N};
+    Loader<MI>::setup(0, nt);
+  }
+};
+
+template <int EPI, int MI>
+struct GroupStoreEpi {
+  static constexpr bool kSplitTop = false;
+  GroupOperands g;
+  __device__ __forceinline__ void spill(const AccT<MI>&) const {}
+  __device__ __forceinline__ void operator()(const AccT<MI>& acc, int item, int nt, char* region) const {
+    const CONST_AS int32_t* it = (const CONST_AS int32_t*)g.items + 4 * item;
+    const int row0 = it[1], rows = it[2];
+    char* const base = static_cast<char*>(g.Y) + int64_t(row0) * g.N * (EPI == kEpiF32 ? 4 : 2);
+    const StoreEpi<EPI, MI> st{base, g.N, rows, g.N};
+    st(acc, 0, nt, region);
+  }
+};
+
+template <int LG, int MI, int EPI>
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void group_tile_kernel(GroupOperands g, const int32_t* __restrict__ n_items, int ktiles, int n_nt) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  TileSched ts;
+  ts.init(*(const CONST_AS int32_t*)n_items, n_nt);
+  GroupLoader<MI> ld;
+  ld.g = g;
+  GroupStoreEpi<EPI, MI> epi{g};
+  leaf_tree_persistent<LG, MI>(ld, ktiles, ts, epi, smem);
+}
+
+// SiLU(g) * u between the expert GEMMs [BitRL, 4.4, condition 3]: in FP32,
+// sigmoid(g) = 1 / (1 + t) for g >= 0 and t / (1 + t) below, t = e^-|g| by
+// the hardware exp2 (so that very negative g keep their tiny values), times g,
+// times u, then one rounding to bf16.  Thread: four consecutive columns.
+__device__ __forceinline__ float silu_f32(float g) {
+  const float t = __builtin_amdgcn_exp2f(-__builtin_fabsf(g) * LOG2E);
+  const float d = 1.0f + t;
+  const float s = g >= 0.0f ? 1.0f / d : t / d;
+  return g * s;
+}
+
+__global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__ GU, int64_t ldgu,
+                                                       uint16_t* __restrict__ out, int64_t ldo, int64_t rows,
+                                                       int64_t I, bool vec) {
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+  const float* g = GU + r * ldgu;
+  const float* u = g + I;
+  uint16_t* o = out + r * ldo;
+  for (int64_t c = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4; c < I; c += int64_t(gridDim.x) * 1024) {
+    if (vec) {
+      const float4 gv = *reinterpret_cast<const float4*>(g + c), uv = *reinterpret_cast<const float4*>(u + c);
+      const uint32_t lo = uint32_t(f32_to_bf16_rne(silu_f32(gv.x) * uv.x)) |
+                          (uint32_t(f32_to_bf16_rne(silu_f32(gv.y) * uv.y)) << 16);
+      const uint32_t hi = uint32_t(f32_to_bf16_rne(silu_f32(gv.z) * uv.z)) |
+                          (uint32_t(f32_to_bf16_rne(silu_f32(gv.w) * uv.w)) << 16);
+      *reinterpret_cast<uint2*>(o + c) = make_uint2(lo, hi);
+    } else {
+      for (int64_t j = c; j < c + 4 && j < I; ++j) o[j] = f32_to_bf16_rne(silu_f32(g[j]) * u[j]);
+    }
+  }
+  }
+}
+
 // Persistent grid: one workgroup per CU (multiple of 8 for the XCD deal), or
 // one per tile when there are fewer tiles.  Only the schedule depends on it.
 int persistent_grid(int64_t n_tiles) {
@@ -1341,6 +1480,34 @@ template <int LG>
 hipError_t launch_moe_lg(const MoeLaunch& p, hipStream_t s) {
   if constexpr (block_m_for_log2(LG) == 192) return launch_moe_mi<LG, 3>(p, s);
   else return launch_moe_mi<LG, 2>(p, s);
+}
+
+template <int LG, int MI>
+hipError_t launch_group_mi(const GroupLaunch& p, hipStream_t s) {
+  constexpr int BMm = 64 * MI;
+  hipLaunchKernelGGL(group_plan_kernel, dim3(1), dim3(GROUP_PLAN_THREADS), 0, s, p.counts, p.n_experts, p.masked,
+                     p.cap, p.align, p.rows, BMm, reinterpret_cast<int4*>(p.items), p.n_items);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int n_nt = int(cdiv(p.N, BN));
+  const GroupOperands g{static_cast<const uint16_t*>(p.X), static_cast<const uint16_t*>(p.W), p.Y,
+                        reinterpret_cast<const int4*>(p.items), p.N, p.K};
+  // The grid is sized from the static bound on work items; workgroups without
+  // a tile exit at once.
+  const dim3 grid(persistent_grid(group_max_items(p.rows, p.n_experts) * n_nt));
+  if (p.epi == kEpiF32)
+    hipLaunchKernelGGL((group_tile_kernel<LG, MI, kEpiF32>), grid, dim3(NTHREADS), 0, s, g, p.n_items,
+                       int(p.K / BK), n_nt);
+  else
+    hipLaunchKernelGGL((group_tile_kernel<LG, MI, kEpiBF16>), grid, dim3(NTHREADS), 0, s, g, p.n_items,
+                       int(p.K / BK), n_nt);
+  return hipGetLastError();
+}
+
+template <int LG>
+hipError_t launch_group_lg(const GroupLaunch& p, hipStream_t s) {
+  if constexpr (block_m_for_log2(LG) == 192) return launch_group_mi<LG, 3>(p, s);
+  else return launch_group_mi<LG, 2>(p, s);
 }
 
 }  // namespace
@@ -1818,6 +1985,30 @@ hipError_t launch_moe(const MoeLaunch& p, hipStream_t s) {
     case 4: return launch_moe_lg<4>(p, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_group_gemm(const GroupLaunch& p, hipStream_t s) {
+  if (p.n_experts < 1 || p.n_experts > kMaxGroupExperts) return hipErrorInvalidValue;
+  switch (p.leaves_log2) {
+    case 0: return launch_group_lg<0>(p, s);
+    case 1: return launch_group_lg<1>(p, s);
+    case 2: return launch_group_lg<2>(p, s);
+    case 3: return launch_group_lg<3>(p, s);
+    case 4: return launch_group_lg<4>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_silu_mul(const float* GU, int64_t ldgu, uint16_t* out, int64_t ldo, int64_t rows, int64_t I,
+                           hipStream_t s) {
+  if (rows <= 0 || I <= 0) return hipSuccess;
+  const bool vec = I % 4 == 0 && ldgu % 4 == 0 && ldo % 4 == 0 && (reinterpret_cast<uintptr_t>(GU) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(out) & 7) == 0;
+  const int64_t cx = cdiv(I, 1024);
+  hipLaunchKernelGGL(silu_mul_kernel, dim3(unsigned(cx < 64 ? cx : 64), unsigned(rows < 65535 ? rows : 65535)),
+                     dim3(256), 0, s, GU, ldgu,
+                     out, ldo, rows, I, vec);
+  return hipGetLastError();
 }
 
 }  // namespace tig

@@ -152,6 +152,43 @@ def test_topk_arguments_rejected_before_any_launch():
     assert "NULL" in tig.tig_last_error()
 
 
+def test_expert_gemm_arguments_rejected_before_any_launch():
+    lib = _raw()
+    ws = None
+    # n_experts out of range; negative cap / align below 1; NULL pointers; too small a workspace
+    assert lib.tig_expert_gemm_masked(None, None, None, None, 0, 0, 4, 128, 512, 8, ws, 0, None) == \
+        tig.TIG_ERR_INVALID_ARG
+    assert lib.tig_expert_gemm_masked(None, None, None, None, 0, 1025, 4, 128, 512, 8, ws, 0, None) == \
+        tig.TIG_ERR_UNSUPPORTED
+    assert lib.tig_expert_gemm_masked(None, None, None, None, 0, 4, -1, 128, 512, 8, ws, 0, None) == \
+        tig.TIG_ERR_INVALID_ARG
+    assert lib.tig_expert_gemm_contiguous(None, None, 0, None, None, 0, 4, 64, 128, 512, 8, ws, 0, None) == \
+        tig.TIG_ERR_INVALID_ARG
+    assert lib.tig_expert_gemm_masked(None, None, None, None, 0, 4, 16, 128, 512, 8, ws, 0, None) == \
+        tig.TIG_ERR_INVALID_ARG
+    assert "NULL" in tig.tig_last_error()
+    # leaves that do not split K into 64-multiples; an unknown output dtype
+    assert lib.tig_expert_gemm_masked(None, None, None, None, 0, 4, 16, 128, 512, 16, ws, 0, None) == \
+        tig.TIG_ERR_UNSUPPORTED
+    assert lib.tig_expert_gemm_masked(None, None, None, None, 7, 4, 16, 128, 512, 8, ws, 0, None) == \
+        tig.TIG_ERR_INVALID_ARG
+    # nothing to do: no rows, or no columns
+    assert lib.tig_expert_gemm_masked(None, None, None, None, 0, 4, 0, 128, 512, 8, ws, 0, None) == tig.TIG_OK
+    assert lib.tig_expert_gemm_contiguous(None, None, 128, None, None, 0, 4, 64, 0, 512, 8, ws, 0, None) == \
+        tig.TIG_OK
+    assert tig.tig_expert_workspace_bytes(1000, 64) == 256 + 72 * 16 + 128   # 72 items, 256-byte aligned
+    with pytest.raises(tig.TigError):
+        tig.tig_expert_workspace_bytes(10, 0)
+
+
+def test_silu_mul_arguments_rejected():
+    lib = _raw()
+    assert lib.tig_silu_mul(None, 10, None, 8, 4, 8, None) == tig.TIG_ERR_INVALID_ARG      # ldgu < 2 I
+    assert lib.tig_silu_mul(None, 16, None, 7, 4, 8, None) == tig.TIG_ERR_INVALID_ARG      # ldo < I
+    assert lib.tig_silu_mul(None, 16, None, 8, 4, 8, None) == tig.TIG_ERR_INVALID_ARG      # NULL
+    assert lib.tig_silu_mul(None, 16, None, 8, 0, 8, None) == tig.TIG_OK
+
+
 def test_null_pointers_rejected():
     lib = _raw()
     assert lib.tig_tree_gemm(None, 512, None, 512, None, 64, 0, 4, 64, 512, 8, None) == tig.TIG_ERR_INVALID_ARG
