@@ -39,6 +39,15 @@ Readings where the pages leave a step open:
   ``SiLU(g) * u`` with ``SiLU(g) = g / (1 + exp(-g))``, computed exactly here
   and rounded to bf16 once, to nearest even; FP8 quantisation after it is not
   modelled (out of scope).
+* R21 block FP8 (section 4.1: BF16 master weights quantised to block FP8 by
+  the deployment rule, W8A8; section 4.4: per-element round to nearest): OCP
+  E4M3 values (largest 448); a power-of-two scale 2^e per block, e the
+  smallest integer with amax <= 448 * 2^e (e = 0 for an all-zero block);
+  each element is x * 2^-e rounded to E4M3 once, to nearest even.  Weight
+  blocks are 128 x 128 (rows x columns of W), activation blocks 1 x 128 (a
+  token's 128 consecutive columns); a block cut by the matrix edge takes the
+  elements it has.  The product of two dequantised values is exact in FP32,
+  so the W8A8 GEMM is the leaf-tree contraction of the dequantised values.
 * R13 the router: logits are the FP32 leaf-tree contraction of the token with
   the router weight, the same at every batch size ([Bit-consistent RL],
   section 4.1: the router gate uses one FP32-output GEMM at every batch size);
@@ -51,7 +60,8 @@ Parity status:
 * ``contraction_ref``, ``lse_ref``, ``log_softmax_ref``, ``logprob_ref``,
   ``moe_ref``, ``route_select``, ``route_gates_ref``, ``route_ref``,
   ``topk_positions``, ``expert_row_starts``, ``expert_gemm_ref``,
-  ``silu_mul_ref``, ``f64_to_bf16_rne``: plain
+  ``silu_mul_ref``, ``f64_to_bf16_rne``, ``e4m3_value``, ``f64_to_e4m3_rne``,
+  ``fp8_block_quant``, ``fp8_dequant``, ``fp8_gemm_ref``: plain
   definitions in fp64; pinned by brute force (exact rational arithmetic, rank
   counting), closed forms and invariants in ``tests/test_oracle_pins.py``.
 * ``leaf_tree_f32``, ``leaf_tree_gemm_f32``, ``moe_combine_f32``: float32
@@ -87,6 +97,11 @@ __all__ = [
     "expert_row_starts",
     "expert_gemm_ref",
     "silu_mul_ref",
+    "e4m3_value",
+    "f64_to_e4m3_rne",
+    "fp8_block_quant",
+    "fp8_dequant",
+    "fp8_gemm_ref",
     "k3_kl",
 ]
 
@@ -385,6 +400,103 @@ def silu_mul_ref(G, U) -> np.ndarray:
     with np.errstate(over="ignore"):
         silu = np.where(g < -700.0, g * np.exp(np.maximum(g, -745.0)), g / (1.0 + np.exp(-g)))
     return f64_to_bf16_rne(silu * u)
+
+
+# ---------------------------------------------------------------------------
+# Block FP8 (W8A8)   [Bit-consistent RL, sections 4.1 and 4.4; reading R21]
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(bits) -> np.ndarray:
+    """Value of OCP E4M3 bytes: sign, 4 exponent bits (bias 7), 3 mantissa
+    bits; exponent field 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN."""
+    b = np.asarray(bits, dtype=np.uint8).astype(np.int64)
+    sign = np.where(b & 0x80, -1.0, 1.0)
+    ex, man = (b >> 3) & 0xF, b & 0x7
+    mag = np.where(ex == 0, man / 8.0 * 2.0 ** -6, (1.0 + man / 8.0) * np.exp2(ex - 7.0))
+    return np.where((b & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def f64_to_e4m3_rne(x) -> np.ndarray:
+    """Round float64 values with |x| <= 448 to E4M3 once, to nearest even; bytes.
+
+    A normal value keeps 4 significant bits: ``rint(m * 2^4) * 2^(e-4)`` for
+    ``x = m * 2^e``, m in [0.5, 1); below the smallest normal, 2^-6, the step
+    is 2^-9.  (Values above 448 are outside the block rule and rejected.)
+    """
+    v = np.asarray(x, dtype=np.float64)
+    a = np.abs(v)
+    if np.any(a > E4M3_MAX) or np.any(np.isnan(v)):
+        raise ValueError("E4M3 rounding needs finite |x| <= 448")
+    m, e = np.frexp(np.where(a == 0, 1.0, a))
+    normal = np.ldexp(np.rint(np.ldexp(m, 4)), e - 4)
+    r = np.where(a < 2.0 ** -6, np.rint(a * 2.0 ** 9) * 2.0 ** -9, normal)
+    # encode: find the byte whose value is r (exact), by field arithmetic
+    sub = r < 2.0 ** -6
+    code_sub = np.rint(r * 2.0 ** 9).astype(np.int64)                 # 0..8 (8 = smallest normal)
+    m2, e2 = np.frexp(np.where(sub | (r == 0), 1.0, r))
+    code_norm = ((e2 - 1 + 7) << 3) | (np.rint(m2 * 16).astype(np.int64) - 8)
+    code = np.where(sub, code_sub, code_norm)
+    return (code | np.where(np.signbit(v), 0x80, 0)).astype(np.uint8)
+
+
+def _block_exponent(amax) -> np.ndarray:
+    """Smallest integer e with amax <= 448 * 2^e (0 where amax == 0)."""
+    a = np.asarray(amax, dtype=np.float64)
+    _, ex = np.frexp(np.where(a > 0, a, 1.0))
+    e = ex - 9                                                        # 448 * 2^(ex-9) < 2^ex
+    while True:
+        low = (a > 0) & (np.ldexp(E4M3_MAX, e) < a)
+        if not low.any():
+            break
+        e = e + low
+    while True:
+        high = (a > 0) & (np.ldexp(E4M3_MAX, e - 1) >= a)
+        if not high.any():
+            break
+        e = e - high
+    return np.where(a > 0, e, 0).astype(np.int64)
+
+
+def fp8_block_quant(X, block_rows: int, block_cols: int = 128):
+    """Block FP8 quantisation of ``X [R, C]`` (reading R21).
+
+    Returns ``(q uint8 [R, C], e int [ceil(R/br), ceil(C/bc)])``: ``e`` the
+    block's scale exponent, ``q`` each element times 2^-e rounded to E4M3 once.
+    """
+    X64 = as_f64(X)
+    R, C = X64.shape
+    nbr, nbc = -(-R // block_rows), -(-C // block_cols)
+    e = np.zeros((nbr, nbc), dtype=np.int64)
+    q = np.zeros((R, C), dtype=np.uint8)
+    for i in range(nbr):
+        for j in range(nbc):
+            blk = X64[i * block_rows:(i + 1) * block_rows, j * block_cols:(j + 1) * block_cols]
+            ex = int(_block_exponent(np.max(np.abs(blk)) if blk.size else 0.0))
+            e[i, j] = ex
+            q[i * block_rows:(i + 1) * block_rows, j * block_cols:(j + 1) * block_cols] = \
+                f64_to_e4m3_rne(np.ldexp(blk, -ex))
+    return q, e
+
+
+def fp8_dequant(q, e, block_rows: int, block_cols: int = 128) -> np.ndarray:
+    """``q * 2^e`` with each element's block exponent, float64 (exact)."""
+    v = e4m3_value(q)
+    ee = np.repeat(np.repeat(np.asarray(e, dtype=np.int64), block_rows, 0), block_cols, 1)
+    return np.ldexp(v, ee[:v.shape[0], :v.shape[1]])
+
+
+def fp8_gemm_ref(qa, ea, qw, ew, row_chunk: int = 256) -> np.ndarray:
+    """W8A8 block-FP8 GEMM in float64: ``dequant(A) dequant(W)^T`` with A in
+    1 x 128 blocks and W in 128 x 128 blocks."""
+    A = fp8_dequant(qa, ea, 1)
+    W = fp8_dequant(qw, ew, 128)
+    out = np.empty((A.shape[0], W.shape[0]))
+    for r0 in range(0, A.shape[0], row_chunk):
+        out[r0:r0 + row_chunk] = A[r0:r0 + row_chunk] @ W.T
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -652,6 +652,95 @@ def test_expert_gemm_ref_brute_force():
                 assert Y[m, n] == exact
 
 
+# ---------------------------------------------------------------------------
+# Block FP8 (W8A8)   [Bit-consistent RL, sections 4.1 and 4.4]
+# ---------------------------------------------------------------------------
+
+def _e4m3_exact(code: int) -> Fraction:
+    """Value of an E4M3 byte from its fields, as a rational."""
+    sign = -1 if code & 0x80 else 1
+    ex, man = (code >> 3) & 0xF, code & 0x7
+    if ex == 0:
+        return sign * Fraction(man, 8) * Fraction(1, 64)
+    return sign * (1 + Fraction(man, 8)) * Fraction(2) ** (ex - 7)
+
+
+def test_e4m3_codes_round_trip():
+    codes = [c for c in range(256) if c & 0x7F != 0x7F]          # every code but NaN
+    vals = oracle.e4m3_value(np.array(codes, dtype=np.uint8))
+    for c, v in zip(codes, vals.tolist()):
+        assert Fraction(v) == _e4m3_exact(c), c
+    back = oracle.f64_to_e4m3_rne(vals)
+    assert back.tolist() == codes                                  # -0 keeps its sign bit
+    assert oracle.e4m3_value(np.array([0x7E]))[0] == 448.0 and np.isnan(oracle.e4m3_value(np.array([0xFF]))[0])
+
+
+def test_e4m3_rounding_is_nearest_even():
+    """Against the exact nearest of all finite codes, halves to the even mantissa."""
+    rng = np.random.default_rng(2000)
+    x = np.concatenate([rng.uniform(-448, 448, 300), rng.uniform(-2.0 ** -5, 2.0 ** -5, 200),
+                        [232.0, 1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -11, 447.9, -0.0]])
+    finite = [c for c in range(128) if c != 0x7F]
+    got = oracle.f64_to_e4m3_rne(x)
+    for v, b in zip(x.tolist(), got.tolist()):
+        a = abs(Fraction(v))
+        best = min(finite, key=lambda c: (abs(_e4m3_exact(c) - a), c & 1))
+        assert b & 0x7F == best, (v, b, best)
+        assert (b >> 7) == (1 if math.copysign(1.0, v) < 0 else 0)
+    with pytest.raises(ValueError):
+        oracle.f64_to_e4m3_rne(np.array([449.0]))
+
+
+def test_fp8_block_exponent_closed_forms():
+    from oracle.reference import _block_exponent
+    amax = np.array([448.0, 449.0, 1.0, 0.0, 0.875, 896.0, 1.75, 1.7501, 3e-5])
+    # 448 2^e >= amax > 448 2^(e-1): hand-derived (448 = 1.75 * 2^8)
+    assert _block_exponent(amax).tolist() == [0, 1, -8, 0, -9, 1, -8, -7, -23]
+
+
+def test_fp8_block_quant_hand_example():
+    """Blocks of 1 x 2: [1, -3] has amax 3, e = -7 (448/128 = 3.5 >= 3 > 1.75): 128 and -384
+    = codes 0x70 and 0xFC; [500, 0] has e = 1: 250 rounds to 256 (6 away, not 10) = 0x78."""
+    q, e = oracle.fp8_block_quant(np.array([[1.0, -3.0, 500.0, 0.0]]), 1, 2)
+    assert q.tolist() == [[0x70, 0xFC, 0x78, 0x00]] and e.tolist() == [[-7, 1]]
+    assert oracle.fp8_dequant(q, e, 1, 2).tolist() == [[1.0, -3.0, 512.0, 0.0]]
+
+
+def test_fp8_blocks_are_independent_and_bounded():
+    rng = np.random.default_rng(2001)
+    W = wl.normal_bf16(rng, (300, 260), 0.02)                      # cut blocks at both edges
+    q, e = oracle.fp8_block_quant(W, 128, 128)
+    assert q.shape == (300, 260) and e.shape == (3, 3)
+    W2 = W.copy()
+    W2[130:140, 5:9] = wl.normal_bf16(rng, (10, 4), 3.0)           # only block (1, 0) changes
+    q2, e2 = oracle.fp8_block_quant(W2, 128, 128)
+    same = np.ones((300, 260), bool)
+    same[128:256, 0:128] = False
+    assert np.array_equal(q[same], q2[same]) and e2[1, 0] != e[1, 0]
+    assert np.array_equal(np.delete(e.ravel(), 3), np.delete(e2.ravel(), 3))
+    # each element within half an E4M3 step of x * 2^-e (relative 2^-4 above 2^-6)
+    x = oracle.bf16_bits_to_f64(W)
+    ee = np.repeat(np.repeat(e, 128, 0), 128, 1)[:300, :260]
+    t = np.ldexp(x, -ee)
+    err = np.abs(oracle.e4m3_value(q) - t)
+    assert np.all((err <= np.abs(t) * 2.0 ** -4) | (err <= 2.0 ** -10))
+    assert np.all(np.abs(t) <= 448.0)
+
+
+def test_fp8_gemm_ref_brute_force():
+    rng = np.random.default_rng(2002)
+    A = wl.normal_bf16(rng, (3, 256), 1.0)
+    W = wl.normal_bf16(rng, (5, 256), 0.02)
+    qa, ea = oracle.fp8_block_quant(A, 1)
+    qw, ew = oracle.fp8_block_quant(W, 128)
+    C = oracle.fp8_gemm_ref(qa, ea, qw, ew)
+    for m in range(3):
+        for n in range(5):
+            exact = sum(_e4m3_exact(int(qa[m, k])) * Fraction(2) ** int(ea[m, k // 128]) *
+                        _e4m3_exact(int(qw[n, k])) * Fraction(2) ** int(ew[0, k // 128]) for k in range(256))
+            assert abs(Fraction(C[m, n]) - exact) <= abs(exact) * Fraction(1, 2 ** 50) + Fraction(1, 2 ** 80)
+
+
 def test_gumbel_max_samples_the_softmax():
     rng = np.random.default_rng(14)
     n = 200_000
