@@ -237,7 +237,22 @@ def main():
             ms, _ = timed(lambda: tig.tig_tree_gemm(Ar, Wl, C, c.leaves), 20, 3)
             linear[f"M{Mr}"] = {"ms": ms, "roofline": mfma_line(2.0 * Mr * c.K * c.N, ms)}
             log(f"linear M={Mr}: {ms * 1e3:.1f} us, {linear[f'M{Mr}']['roofline']['achieved']:.0f} TFLOP/s")
-        del A, Wl, C
+        # The same layer in block FP8 (W8A8): per-token quantisation of the 4096 rows,
+        # then the leaf-tree GEMM of the dequantised operands (the weights were
+        # quantised once; their expansion to bf16 is inside the timed call).
+        QW, SW = tig.fp8_quantize(Wl, 128)
+        Ar = A[:4096]
+        QA = torch.empty(4096, c.K, dtype=torch.uint8, device=dev)
+        SA = torch.empty(4096, c.K // 128, dtype=torch.uint8, device=dev)
+        ms_q, _ = timed(lambda: tig.tig_fp8_quantize(Ar, QA, SA, 1), 50, 3)
+        tig.tig_fp8_quantize(Ar, QA, SA, 1)
+        C8 = torch.empty(4096, c.N, dtype=torch.float32, device=dev)
+        ws8 = torch.empty(tig.tig_fp8_gemm_workspace_bytes(4096, c.N, c.K), dtype=torch.uint8, device=dev)
+        ms_g, _ = timed(lambda: tig.tig_fp8_tree_gemm(QA, SA, QW, SW, C8, c.leaves, ws8), 20, 3)
+        linear["fp8"] = {"quantize_us": ms_q * 1e3, "quantize": hbm_line(3.0 * 4096 * c.K + 4096 * c.K / 128, ms_q),
+                         "gemm_ms": ms_g, "gemm": mfma_line(2.0 * 4096 * c.K * c.N, ms_g)}
+        log(f"linear fp8: quantize {ms_q * 1e3:.1f} us, gemm {ms_g * 1e3:.1f} us")
+        del A, Wl, C, QW, SW, QA, SA, C8, ws8
 
         c = wl.CONFIGS["moe"]
         sm = wl.streams(c.seed)

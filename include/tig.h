@@ -11,7 +11,8 @@
  *   [BitRL]    "Termina el entrenamiento RL mas rapido: Consistente a nivel de
  *              bits, de alto rendimiento y dirigido por agentes", section 2
  *              (diff = 0 per sampled token; batch independence; prefill/decode
- *              consistency), 4.1 (one accumulation order for every M), 4.3
+ *              consistency), 4.1 (one accumulation order for every M; block
+ *              FP8 W8A8), 4.3
  *              (deterministic Top-K of positions: key, ties, order), 4.4 and
  *              4.5 (expert outputs combined in FP32 in a fixed order), 4.6
  *              (no host sync, workspaces sized from static bounds).
@@ -216,6 +217,41 @@ tig_status tig_expert_workspace_bytes(int64_t rows, int32_t n_experts, size_t* b
  */
 tig_status tig_silu_mul(const float* GU, int64_t ldgu, void* out, int64_t ldo, int64_t rows, int64_t I,
                         hipStream_t stream);
+
+/*
+ * Block FP8 quantisation, [BitRL, 4.1] (BF16 master weights quantised to block
+ * FP8 by the deployment rule, W8A8) and [BitRL, 4.4] (per-element round to
+ * nearest): OCP E4M3 values (largest 448) with one power-of-two scale 2^e per
+ * block, e the smallest integer >= -127 with amax <= 448 * 2^e (0 for an
+ * all-zero block); each element x * 2^-e (exact) is rounded to E4M3 once, to
+ * nearest even.  Blocks are block_rows x 128: 1 x 128 for activations (one per
+ * token and 128 columns), 128 x 128 for weights; a block cut by the matrix
+ * edge takes the elements it has.
+ *   X       bf16 [R, ldx] (row r at X + r*ldx)
+ *   Q       uint8 [R, ldq] out: E4M3 bytes
+ *   scales  uint8 [ceil(R/block_rows), ceil(C/128)] out, row-major: E8M0 bytes
+ *           e + 127
+ * A row's quantisation depends only on its own block(s).
+ */
+tig_status tig_fp8_quantize(const void* X, int64_t ldx, uint8_t* Q, int64_t ldq, uint8_t* scales, int64_t R,
+                            int64_t C, int32_t block_rows, hipStream_t stream);
+
+/*
+ * W8A8 block-FP8 leaf-tree GEMM: C = leaf-tree(dequant(A) dequant(W)^T), with
+ * A quantised in 1 x 128 blocks and W in 128 x 128 blocks (tig_fp8_quantize).
+ * A dequantised value (an E4M3 value times 2^e) is exact in bf16 and a product
+ * of two is exact in FP32, so this is the tig_tree_gemm contract (same leaves,
+ * same tree) applied to the dequantised operands: the operands are expanded to
+ * bf16 in the workspace, then contracted by the bf16 matrix cores.
+ *   QA [M, K] and SA [M, ceil(K/128)]; QW [N, K] and SW [ceil(N/128),
+ *   ceil(K/128)], all contiguous; C [M, ldc] FP32 or bf16 (RNE).
+ *   workspace >= tig_fp8_gemm_workspace_bytes(M, N, K), 256-byte aligned.
+ * Limits as tig_tree_gemm (K/leaves a multiple of 64, leaves <= 16).
+ */
+tig_status tig_fp8_tree_gemm(const uint8_t* QA, const uint8_t* SA, const uint8_t* QW, const uint8_t* SW, void* C,
+                             int64_t ldc, tig_out_dtype out_dtype, int64_t M, int64_t N, int64_t K, int32_t leaves,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+tig_status tig_fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes);
 
 /*
  * Deterministic Top-K of positions, [BitRL, 4.3] (the sparse-attention

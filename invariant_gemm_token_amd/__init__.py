@@ -22,10 +22,11 @@ __all__ = [
     "tig_tree_gemm", "tig_logprob_gather", "tig_logprob_workspace_bytes",
     "tig_moe_tree_gemm_combine", "tig_moe_workspace_bytes", "tig_moe_route", "tig_topk_positions",
     "tig_expert_gemm_masked", "tig_expert_gemm_contiguous", "tig_expert_workspace_bytes", "tig_silu_mul",
+    "tig_fp8_quantize", "tig_fp8_tree_gemm", "tig_fp8_gemm_workspace_bytes",
     "tig_plan_describe",
     "tig_status_string", "tig_last_error",
     "tree_gemm", "logprob_gather", "moe_tree_gemm_combine", "moe_route", "topk_positions",
-    "expert_gemm_masked", "expert_gemm_contiguous", "silu_mul",
+    "expert_gemm_masked", "expert_gemm_contiguous", "silu_mul", "fp8_quantize", "fp8_tree_gemm",
     "TIG_OK", "TIG_ERR_INVALID_ARG", "TIG_ERR_UNSUPPORTED", "TIG_ERR_WORKSPACE", "TIG_ERR_HIP",
     "TIG_OUT_F32", "TIG_OUT_BF16",
 ]
@@ -72,6 +73,9 @@ _SIGNATURES = {
                                           _vp]),
     "tig_expert_workspace_bytes": (_i32, [_i64, _i32, ctypes.POINTER(_sz)]),
     "tig_silu_mul": (_i32, [_vp, _i64, _vp, _i64, _i64, _i64, _vp]),
+    "tig_fp8_quantize": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i32, _vp]),
+    "tig_fp8_tree_gemm": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
+    "tig_fp8_gemm_workspace_bytes": (_i32, [_i64, _i64, _i64, ctypes.POINTER(_sz)]),
     "tig_plan_describe": (_i32, [_i64, _i32, ctypes.POINTER(_Plan)]),
     "tig_status_string": (ctypes.c_char_p, [_i32]),
     "tig_last_error": (ctypes.c_char_p, []),
@@ -334,6 +338,58 @@ def tig_silu_mul(GU, out, stream=None) -> None:
     _check(st, "tig_silu_mul")
 
 
+def tig_fp8_quantize(X, Q, scales, block_rows: int, stream=None) -> None:
+    """Block FP8 (E4M3, power-of-two block scales as E8M0 bytes) of bf16 ``X [R, C]``."""
+    torch = _torch()
+    _need(X, "X", torch.bfloat16, 2)
+    _need(Q, "Q", torch.uint8, 2)
+    _need(scales, "scales", torch.uint8, 2)
+    _same_device(X, Q, scales)
+    _rowmajor(X, "X")
+    _rowmajor(Q, "Q")
+    _contig(scales, "scales")
+    R, C = X.shape
+    br = int(block_rows)
+    if tuple(Q.shape) != (R, C) or tuple(scales.shape) != (-(-R // br) if br > 0 else 0, -(-C // 128)):
+        raise ValueError("Q must be [R, C] and scales [ceil(R/block_rows), ceil(C/128)]")
+    ldx = X.stride(0) if R > 1 else C
+    ldq = Q.stride(0) if R > 1 else C
+    st = load().tig_fp8_quantize(X.data_ptr(), ldx, Q.data_ptr(), ldq, scales.data_ptr(), R, C, br,
+                                 _stream(stream))
+    _check(st, "tig_fp8_quantize")
+
+
+def tig_fp8_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    out = _sz(0)
+    _check(load().tig_fp8_gemm_workspace_bytes(int(M), int(N), int(K), ctypes.byref(out)),
+           "tig_fp8_gemm_workspace_bytes")
+    return int(out.value)
+
+
+def tig_fp8_tree_gemm(QA, SA, QW, SW, C, leaves: int, workspace, stream=None) -> None:
+    """``C = leaf-tree(dequant(A) dequant(W)^T)`` (W8A8 block FP8)."""
+    torch = _torch()
+    for t, n in ((QA, "QA"), (SA, "SA"), (QW, "QW"), (SW, "SW")):
+        _need(t, n, torch.uint8, 2)
+        _contig(t, n)
+    if C.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("C must be float32 or bfloat16")
+    _need(C, "C", C.dtype, 2)
+    _rowmajor(C, "C")
+    _same_device(QA, SA, QW, SW, C)
+    M, K = QA.shape
+    N = QW.shape[0]
+    if QW.shape[1] != K or tuple(C.shape) != (M, N) or tuple(SA.shape) != (M, -(-K // 128)) or \
+            tuple(SW.shape) != (-(-N // 128), -(-K // 128)):
+        raise ValueError("shapes do not match")
+    od = TIG_OUT_F32 if C.dtype == torch.float32 else TIG_OUT_BF16
+    ldc = C.stride(0) if M > 1 else N
+    st = load().tig_fp8_tree_gemm(QA.data_ptr(), SA.data_ptr(), QW.data_ptr(), SW.data_ptr(), C.data_ptr(), ldc,
+                                  od, M, N, K, int(leaves), workspace.data_ptr(), workspace.numel(),
+                                  _stream(stream))
+    _check(st, "tig_fp8_tree_gemm")
+
+
 def tig_topk_positions(scores, lengths, out, stream=None) -> None:
     """Top-k positions per row by (score, position), listed by descending position, -1 padded."""
     torch = _torch()
@@ -448,3 +504,26 @@ def silu_mul(GU, stream=None):
     out = torch.empty((GU.shape[0], GU.shape[1] // 2), dtype=torch.bfloat16, device=GU.device)
     tig_silu_mul(GU, out, stream)
     return out
+
+
+def fp8_quantize(X, block_rows: int, stream=None):
+    """Allocate and return ``(Q, scales)`` of tig_fp8_quantize."""
+    torch = _torch()
+    R, C = X.shape
+    Q = torch.empty((R, C), dtype=torch.uint8, device=X.device)
+    S = torch.empty((-(-R // int(block_rows)), -(-C // 128)), dtype=torch.uint8, device=X.device)
+    tig_fp8_quantize(X, Q, S, block_rows, stream)
+    return Q, S
+
+
+def fp8_tree_gemm(QA, SA, QW, SW, leaves: int, out_dtype=None, workspace=None, stream=None):
+    """Allocate and return C ``[M, N]`` of tig_fp8_tree_gemm."""
+    torch = _torch()
+    M, K = QA.shape
+    N = QW.shape[0]
+    need = tig_fp8_gemm_workspace_bytes(M, N, K)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=QA.device)
+    C = torch.empty((M, N), dtype=out_dtype or torch.float32, device=QA.device)
+    tig_fp8_tree_gemm(QA, SA, QW, SW, C, leaves, workspace, stream)
+    return C

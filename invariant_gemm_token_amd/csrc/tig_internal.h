@@ -151,6 +151,14 @@ hipError_t launch_tree_gemm(const TreeGemmLaunch& p, hipStream_t stream);
 hipError_t launch_logprob(const LogprobLaunch& p, hipStream_t stream);
 hipError_t launch_moe(const MoeLaunch& p, hipStream_t stream);
 hipError_t launch_group_gemm(const GroupLaunch& p, hipStream_t stream);
+// Block FP8: quantise bf16 X [R, C] (row stride ldx) into E4M3 bytes Q (row
+// stride ldq) and E8M0 scale bytes S [ceil(R/block_rows)][ceil(C/128)];
+// block_rows = 1 (activations) or 128 (weights).  Dequantise (Q with row
+// stride C) to bf16 [R, C], exact.
+hipError_t launch_fp8_quantize(const uint16_t* X, int64_t ldx, uint8_t* Q, int64_t ldq, uint8_t* S, int64_t R,
+                               int64_t C, int block_rows, hipStream_t stream);
+hipError_t launch_fp8_dequant(const uint8_t* Q, const uint8_t* S, int64_t R, int64_t C, int block_rows,
+                              uint16_t* out, hipStream_t stream);
 // out[r, i] = bf16(SiLU(g) * u) in FP32, g = GU[r, i], u = GU[r, I + i], one rounding.
 hipError_t launch_silu_mul(const float* GU, int64_t ldgu, uint16_t* out, int64_t ldo, int64_t rows, int64_t I,
                            hipStream_t stream);

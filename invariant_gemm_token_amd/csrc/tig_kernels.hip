@@ -1365,6 +1365,126 @@ __global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__
   }
 }
 
+// ---------------------------------------------------------------------------
+// Block FP8 (W8A8) [BitRL, 4.1 and 4.4]: OCP E4M3 values with one power-of-two
+// scale 2^e per block (128 x 128 for weights, 1 x 128 for activations), e the
+// smallest integer >= -127 with amax <= 448 * 2^e, every element x * 2^-e
+// rounded to E4M3 once, to nearest even.  Scales are stored as E8M0 bytes
+// (e + 127).  Everything here is exact integer / power-of-two arithmetic.
+// ---------------------------------------------------------------------------
+
+// Smallest e >= -127 with a <= 448 * 2^e, for a finite a > 0 (448 = 1.75 * 2^8):
+// with a = 1.f * 2^E, e = E - 8 when 1.f <= 1.75, else E - 7.
+__device__ __forceinline__ int fp8_block_exponent(float a) {
+  if (!(a > 0.0f)) return 0;
+  uint32_t b = __builtin_bit_cast(uint32_t, a);
+  int E = int(b >> 23) - 127;
+  if ((b >> 23) == 0) {                                // subnormal: normalise exactly
+    b = __builtin_bit_cast(uint32_t, a * 18446744073709551616.0f);   // * 2^64
+    E = int(b >> 23) - 127 - 64;
+  }
+  const int e = E - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  return e < -127 ? -127 : e;
+}
+
+// E4M3 byte nearest to v (|v| <= 448, finite), halves to the even mantissa.
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const uint32_t sign = (b >> 24) & 0x80u, a = b & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x3C800000u) {                              // |v| >= 2^-6: keep 3 mantissa bits
+    const uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;   // (exponent, mantissa) rounded
+    code = r - (120u << 3);                           // rebias 127 -> 7
+  } else {                                             // subnormal step 2^-9: an integer 0..8
+    code = uint32_t(__builtin_rintf(__builtin_bit_cast(float, a) * 512.0f));
+  }
+  return sign | code;
+}
+
+// Value of an E4M3 byte times 2^e, as a float (exact).
+__device__ __forceinline__ float e4m3_scaled(uint32_t q, int e) {
+  const uint32_t ex = (q >> 3) & 0xFu, man = q & 7u;
+  const float mag = ex == 0 ? float(man) * 0.001953125f : float(8u + man) * __builtin_ldexpf(1.0f, int(ex) - 10);
+  const float v = __builtin_ldexpf(mag, e);
+  return (q & 0x80u) ? -v : v;
+}
+
+// One wave per 128-column group of one row (activations, blocks of 1 x 128):
+// lane l holds columns 2l, 2l+1 of the group.
+__global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                             uint8_t* __restrict__ Q, int64_t ldq,
+                                                             uint8_t* __restrict__ S, int64_t R, int64_t C) {
+  const int64_t ngroups = (C + 127) / 128;
+  const int lane = threadIdx.x & 63;
+  for (int64_t w = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6); w < R * ngroups; w += int64_t(gridDim.x) * 4) {
+    const int64_t r = w / ngroups, g = w % ngroups;
+    const int64_t c0 = g * 128 + 2 * lane;
+    const uint16_t* x = X + r * ldx;
+    const float v0 = c0 < C ? __builtin_bit_cast(float, uint32_t(x[c0]) << 16) : 0.0f;
+    const float v1 = c0 + 1 < C ? __builtin_bit_cast(float, uint32_t(x[c0 + 1]) << 16) : 0.0f;
+    float m = __builtin_fmaxf(__builtin_fabsf(v0), __builtin_fabsf(v1));
+#pragma unroll
+    for (int d = 1; d < 64; d *= 2) m = __builtin_fmaxf(m, __shfl_xor(m, d));
+    const int e = fp8_block_exponent(m);
+    uint8_t* q = Q + r * ldq;
+    if (c0 < C) q[c0] = uint8_t(f32_to_e4m3_rne(__builtin_ldexpf(v0, -e)));
+    if (c0 + 1 < C) q[c0 + 1] = uint8_t(f32_to_e4m3_rne(__builtin_ldexpf(v1, -e)));
+    if (lane == 0) S[r * ngroups + g] = uint8_t(e + 127);
+  }
+}
+
+// One workgroup per 128 x 128 block (weights): thread t takes columns
+// 2 (t % 64), +1 of rows t / 64, t / 64 + 4, ...
+__global__ __launch_bounds__(256) void fp8_quant_blocks_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                               uint8_t* __restrict__ Q, int64_t ldq,
+                                                               uint8_t* __restrict__ S, int64_t R, int64_t C) {
+  __shared__ float red[4];
+  const int64_t ngroups = (C + 127) / 128;
+  const int64_t br = blockIdx.y, g = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63;
+  const int64_t c0 = g * 128 + 2 * lane;
+  float m = 0.0f;
+  for (int i = t >> 6; i < 128; i += 4) {
+    const int64_t r = br * 128 + i;
+    if (r >= R) break;
+    const uint16_t* x = X + r * ldx;
+    if (c0 < C) m = __builtin_fmaxf(m, __builtin_fabsf(__builtin_bit_cast(float, uint32_t(x[c0]) << 16)));
+    if (c0 + 1 < C) m = __builtin_fmaxf(m, __builtin_fabsf(__builtin_bit_cast(float, uint32_t(x[c0 + 1]) << 16)));
+  }
+#pragma unroll
+  for (int d = 1; d < 64; d *= 2) m = __builtin_fmaxf(m, __shfl_xor(m, d));
+  if (lane == 0) red[t >> 6] = m;
+  __syncthreads();
+  m = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  const int e = fp8_block_exponent(m);
+  for (int i = t >> 6; i < 128; i += 4) {
+    const int64_t r = br * 128 + i;
+    if (r >= R) break;
+    const uint16_t* x = X + r * ldx;
+    uint8_t* q = Q + r * ldq;
+    if (c0 < C) q[c0] = uint8_t(f32_to_e4m3_rne(__builtin_ldexpf(__builtin_bit_cast(float, uint32_t(x[c0]) << 16), -e)));
+    if (c0 + 1 < C)
+      q[c0 + 1] = uint8_t(f32_to_e4m3_rne(__builtin_ldexpf(__builtin_bit_cast(float, uint32_t(x[c0 + 1]) << 16), -e)));
+  }
+  if (t == 0) S[br * ngroups + g] = uint8_t(e + 127);
+}
+
+// Dequantise to bf16 (exact): out[r, c] = value(Q[r, c]) * 2^e of its block
+// (block_rows rows x 128 columns).  Thread: 8 consecutive columns.
+__global__ __launch_bounds__(256) void fp8_dequant_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ S,
+                                                          int64_t R, int64_t C, int block_rows,
+                                                          uint16_t* __restrict__ out) {
+  const int64_t ngroups = (C + 127) / 128;
+  const int64_t n8 = (C + 7) / 8;
+  for (int64_t w = int64_t(blockIdx.x) * 256 + threadIdx.x; w < R * n8; w += int64_t(gridDim.x) * 256) {
+    const int64_t r = w / n8, c0 = (w % n8) * 8;
+    const int e = int(S[(r / block_rows) * ngroups + c0 / 128]) - 127;
+    const uint8_t* q = Q + r * C;
+    uint16_t* o = out + r * C;
+    for (int j = 0; j < 8 && c0 + j < C; ++j) o[c0 + j] = f32_to_bf16_rne(e4m3_scaled(q[c0 + j], e));
+  }
+}
+
 // Persistent grid: one workgroup per CU (multiple of 8 for the XCD deal), or
 // one per tile when there are fewer tiles.  Only the schedule depends on it.
 int persistent_grid(int64_t n_tiles) {
@@ -1997,6 +2117,35 @@ hipError_t launch_group_gemm(const GroupLaunch& p, hipStream_t s) {
     case 4: return launch_group_lg<4>(p, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_fp8_quantize(const uint16_t* X, int64_t ldx, uint8_t* Q, int64_t ldq, uint8_t* S, int64_t R,
+                               int64_t C, int block_rows, hipStream_t s) {
+  if (R <= 0 || C <= 0) return hipSuccess;
+  const int64_t ngroups = cdiv(C, 128);
+  if (block_rows == 1) {
+    const int64_t waves = R * ngroups;
+    const int64_t wgs = cdiv(waves, 4);
+    hipLaunchKernelGGL(fp8_quant_rows_kernel, dim3(unsigned(wgs < 65536 ? wgs : 65536)), dim3(256), 0, s, X, ldx,
+                       Q, ldq, S, R, C);
+  } else if (block_rows == 128) {
+    if (cdiv(R, 128) > 65535) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fp8_quant_blocks_kernel, dim3(unsigned(ngroups), unsigned(cdiv(R, 128))), dim3(256), 0, s,
+                       X, ldx, Q, ldq, S, R, C);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_dequant(const uint8_t* Q, const uint8_t* S, int64_t R, int64_t C, int block_rows,
+                              uint16_t* out, hipStream_t s) {
+  if (R <= 0 || C <= 0) return hipSuccess;
+  const int64_t th = R * cdiv(C, 8);
+  const int64_t wgs = cdiv(th, 256);
+  hipLaunchKernelGGL(fp8_dequant_kernel, dim3(unsigned(wgs < 65536 ? wgs : 65536)), dim3(256), 0, s, Q, S, R, C,
+                     block_rows, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_silu_mul(const float* GU, int64_t ldgu, uint16_t* out, int64_t ldo, int64_t rows, int64_t I,

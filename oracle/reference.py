@@ -42,7 +42,8 @@ Readings where the pages leave a step open:
 * R21 block FP8 (section 4.1: BF16 master weights quantised to block FP8 by
   the deployment rule, W8A8; section 4.4: per-element round to nearest): OCP
   E4M3 values (largest 448); a power-of-two scale 2^e per block, e the
-  smallest integer with amax <= 448 * 2^e (e = 0 for an all-zero block);
+  smallest integer >= -127 with amax <= 448 * 2^e (e = 0 for an all-zero
+  block; -127 is the lowest exponent of the one-byte E8M0 scale encoding);
   each element is x * 2^-e rounded to E4M3 once, to nearest even.  Weight
   blocks are 128 x 128 (rows x columns of W), activation blocks 1 x 128 (a
   token's 128 consecutive columns); a block cut by the matrix edge takes the
@@ -443,7 +444,9 @@ def f64_to_e4m3_rne(x) -> np.ndarray:
 
 
 def _block_exponent(amax) -> np.ndarray:
-    """Smallest integer e with amax <= 448 * 2^e (0 where amax == 0)."""
+    """Smallest integer e >= -127 with amax <= 448 * 2^e (0 where amax == 0);
+    -127 is the lowest exponent one E8M0 byte holds (and bf16 values never
+    need more than 120)."""
     a = np.asarray(amax, dtype=np.float64)
     _, ex = np.frexp(np.where(a > 0, a, 1.0))
     e = ex - 9                                                        # 448 * 2^(ex-9) < 2^ex
@@ -457,7 +460,7 @@ def _block_exponent(amax) -> np.ndarray:
         if not high.any():
             break
         e = e - high
-    return np.where(a > 0, e, 0).astype(np.int64)
+    return np.where(a > 0, np.maximum(e, -127), 0).astype(np.int64)
 
 
 def fp8_block_quant(X, block_rows: int, block_cols: int = 128):

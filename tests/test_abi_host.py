@@ -189,6 +189,20 @@ def test_silu_mul_arguments_rejected():
     assert lib.tig_silu_mul(None, 16, None, 8, 0, 8, None) == tig.TIG_OK
 
 
+def test_fp8_arguments_rejected():
+    lib = _raw()
+    assert lib.tig_fp8_quantize(None, 256, None, 256, None, 4, 256, 64, None) == tig.TIG_ERR_INVALID_ARG   # block
+    assert lib.tig_fp8_quantize(None, 100, None, 256, None, 4, 256, 1, None) == tig.TIG_ERR_INVALID_ARG    # ldx < C
+    assert lib.tig_fp8_quantize(None, 256, None, 256, None, 4, 256, 1, None) == tig.TIG_ERR_INVALID_ARG    # NULL
+    assert lib.tig_fp8_quantize(None, 256, None, 256, None, 0, 256, 128, None) == tig.TIG_OK
+    assert lib.tig_fp8_tree_gemm(None, None, None, None, None, 64, 0, 8, 64, 512, 8, None, 0, None) == \
+        tig.TIG_ERR_INVALID_ARG
+    assert lib.tig_fp8_tree_gemm(None, None, None, None, None, 64, 0, 8, 64, 512, 16, None, 0, None) == \
+        tig.TIG_ERR_UNSUPPORTED
+    assert lib.tig_fp8_tree_gemm(None, None, None, None, None, 64, 0, 0, 64, 512, 8, None, 0, None) == tig.TIG_OK
+    assert tig.tig_fp8_gemm_workspace_bytes(10, 20, 512) == 10 * 512 * 2 + 20 * 512 * 2
+
+
 def test_null_pointers_rejected():
     lib = _raw()
     assert lib.tig_tree_gemm(None, 512, None, 512, None, 64, 0, 4, 64, 512, 8, None) == tig.TIG_ERR_INVALID_ARG

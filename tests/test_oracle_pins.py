@@ -693,9 +693,10 @@ def test_e4m3_rounding_is_nearest_even():
 
 def test_fp8_block_exponent_closed_forms():
     from oracle.reference import _block_exponent
-    amax = np.array([448.0, 449.0, 1.0, 0.0, 0.875, 896.0, 1.75, 1.7501, 3e-5])
-    # 448 2^e >= amax > 448 2^(e-1): hand-derived (448 = 1.75 * 2^8)
-    assert _block_exponent(amax).tolist() == [0, 1, -8, 0, -9, 1, -8, -7, -23]
+    amax = np.array([448.0, 449.0, 1.0, 0.0, 0.875, 896.0, 1.75, 1.7501, 3e-5, 2.0 ** -126, 3.3895e38])
+    # 448 2^e >= amax > 448 2^(e-1): hand-derived (448 = 1.75 * 2^8); 2^-126 would need e = -134,
+    # below the E8M0 floor of -127; the largest bf16, (2 - 2^-7) 2^127, needs 120
+    assert _block_exponent(amax).tolist() == [0, 1, -8, 0, -9, 1, -8, -7, -23, -127, 120]
 
 
 def test_fp8_block_quant_hand_example():
