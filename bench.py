@@ -41,6 +41,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix-core peak
 
 
 def log(*a):
@@ -203,6 +204,22 @@ def main():
                   "algorithmic_bytes": dec_bytes, "roofline": r,
                   "frac_of_device_copy": None if copy_gbs is None else r["achieved"] / copy_gbs}
 
+    # The LM-head contraction alone in block FP8 (W8A8) on the FP8 matrix cores:
+    # W quantised once (128 x 128 blocks), the 8192 rows per token (1 x 128).
+    fp8_lmhead = None
+    if not args.no_extra and args.phase == "all":
+        QW8, SW8 = tig.fp8_quantize(Wd, 128)
+        QA8, SA8 = tig.fp8_quantize(Hd, 1)
+        C8 = torch.empty(M, V, dtype=torch.float32, device=dev)
+        ws8 = torch.empty(tig.tig_fp8_gemm_workspace_bytes(M, V, K), dtype=torch.uint8, device=dev)
+        ms8, _ = timed(lambda: tig.tig_fp8_tree_gemm(QA8, SA8, QW8, SW8, C8, L, ws8), 5, 1)
+        tf8 = 2.0 * M * K * V / (ms8 / 1e3) / 1e12
+        fp8_lmhead = {"ms": ms8, "shape": f"M={M} K={K} N={V} leaves={L}",
+                      "roofline": {"bound": "mfma", "achieved": tf8, "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                                   "frac": tf8 / PEAK_FP8_TFLOPS}}
+        log(f"fp8 lm-head gemm: {ms8:.2f} ms, {tf8:.0f} TFLOP/s")
+        del QW8, SW8, QA8, SA8, C8, ws8
+
     cpu = None
     if not args.no_cpu_baseline and args.phase == "all":
         import oracle
@@ -238,8 +255,7 @@ def main():
             linear[f"M{Mr}"] = {"ms": ms, "roofline": mfma_line(2.0 * Mr * c.K * c.N, ms)}
             log(f"linear M={Mr}: {ms * 1e3:.1f} us, {linear[f'M{Mr}']['roofline']['achieved']:.0f} TFLOP/s")
         # The same layer in block FP8 (W8A8): per-token quantisation of the 4096 rows,
-        # then the leaf-tree GEMM of the dequantised operands (the weights were
-        # quantised once; their expansion to bf16 is inside the timed call).
+        # then the leaf-tree GEMM on the FP8 matrix cores (the weights quantised once).
         QW, SW = tig.fp8_quantize(Wl, 128)
         Ar = A[:4096]
         QA = torch.empty(4096, c.K, dtype=torch.uint8, device=dev)
@@ -250,7 +266,10 @@ def main():
         ws8 = torch.empty(tig.tig_fp8_gemm_workspace_bytes(4096, c.N, c.K), dtype=torch.uint8, device=dev)
         ms_g, _ = timed(lambda: tig.tig_fp8_tree_gemm(QA, SA, QW, SW, C8, c.leaves, ws8), 20, 3)
         linear["fp8"] = {"quantize_us": ms_q * 1e3, "quantize": hbm_line(3.0 * 4096 * c.K + 4096 * c.K / 128, ms_q),
-                         "gemm_ms": ms_g, "gemm": mfma_line(2.0 * 4096 * c.K * c.N, ms_g)}
+                         "gemm_ms": ms_g, "gemm": dict(mfma_line(2.0 * 4096 * c.K * c.N, ms_g),
+                                                       peak=PEAK_FP8_TFLOPS,
+                                                       frac=2.0 * 4096 * c.K * c.N / (ms_g / 1e3) / 1e12
+                                                       / PEAK_FP8_TFLOPS)}
         log(f"linear fp8: quantize {ms_q * 1e3:.1f} us, gemm {ms_g * 1e3:.1f} us")
         del A, Wl, C, QW, SW, QA, SA, C8, ws8
 
@@ -375,6 +394,7 @@ def main():
         "decode": decode,
         "linear": linear,
         "moe": moe,
+        "fp8_lmhead_gemm": fp8_lmhead,
         "topk": topk,
         "large": large,
         "cpu_baseline": cpu,

@@ -236,17 +236,26 @@ tig_status tig_silu_mul(const float* GU, int64_t ldgu, void* out, int64_t ldo, i
 tig_status tig_fp8_quantize(const void* X, int64_t ldx, uint8_t* Q, int64_t ldq, uint8_t* scales, int64_t R,
                             int64_t C, int32_t block_rows, hipStream_t stream);
 
+/* Dequantise (exact): out bf16 [R, C] = E4M3 value of Q [R, C] (contiguous)
+ * times 2^e of its block; scales as written by tig_fp8_quantize. */
+tig_status tig_fp8_dequantize(const uint8_t* Q, const uint8_t* scales, void* out, int64_t R, int64_t C,
+                              int32_t block_rows, hipStream_t stream);
+
 /*
- * W8A8 block-FP8 leaf-tree GEMM: C = leaf-tree(dequant(A) dequant(W)^T), with
- * A quantised in 1 x 128 blocks and W in 128 x 128 blocks (tig_fp8_quantize).
- * A dequantised value (an E4M3 value times 2^e) is exact in bf16 and a product
- * of two is exact in FP32, so this is the tig_tree_gemm contract (same leaves,
- * same tree) applied to the dequantised operands: the operands are expanded to
- * bf16 in the workspace, then contracted by the bf16 matrix cores.
- *   QA [M, K] and SA [M, ceil(K/128)]; QW [N, K] and SW [ceil(N/128),
- *   ceil(K/128)], all contiguous; C [M, ldc] FP32 or bf16 (RNE).
- *   workspace >= tig_fp8_gemm_workspace_bytes(M, N, K), 256-byte aligned.
- * Limits as tig_tree_gemm (K/leaves a multiple of 64, leaves <= 16).
+ * W8A8 block-FP8 leaf-tree GEMM on the FP8 matrix cores, [BitRL, 4.1] (one
+ * accumulation order for every M) with [IsoExec, Parallelism-invariant kernels]
+ * (K cut into `leaves` contiguous leaves, FP32 per leaf, fixed binary tree):
+ * A is quantised in 1 x 128 blocks, W in 128 x 128 blocks (tig_fp8_quantize).
+ * Inside a leaf, one instruction (v_mfma_scale_f32_32x32x64_f8f6f4) takes
+ * 64-wide k-steps in ascending order from +0: each E4M3 product times the
+ * E8M0 scales of its row and column (exact: powers of two), accumulated in
+ * FP32; the leaves combine by the balanced adjacent-pair tree in FP32.  A
+ * row's result depends only on that row (its quantisation is per token).
+ *   QA [M, K] and SA [M, K/128]; QW [N, K] and SW [ceil(N/128), K/128], all
+ *   contiguous; C [M, ldc] FP32 or bf16 (RNE).
+ *   workspace >= tig_fp8_gemm_workspace_bytes(M, N, K), 256-byte aligned (the
+ *   call's scale table, built on the device).
+ * Implemented: K/leaves a multiple of 128, leaves <= 16, QA/QW 16-byte aligned.
  */
 tig_status tig_fp8_tree_gemm(const uint8_t* QA, const uint8_t* SA, const uint8_t* QW, const uint8_t* SW, void* C,
                              int64_t ldc, tig_out_dtype out_dtype, int64_t M, int64_t N, int64_t K, int32_t leaves,

@@ -22,11 +22,11 @@ __all__ = [
     "tig_tree_gemm", "tig_logprob_gather", "tig_logprob_workspace_bytes",
     "tig_moe_tree_gemm_combine", "tig_moe_workspace_bytes", "tig_moe_route", "tig_topk_positions",
     "tig_expert_gemm_masked", "tig_expert_gemm_contiguous", "tig_expert_workspace_bytes", "tig_silu_mul",
-    "tig_fp8_quantize", "tig_fp8_tree_gemm", "tig_fp8_gemm_workspace_bytes",
+    "tig_fp8_quantize", "tig_fp8_tree_gemm", "tig_fp8_gemm_workspace_bytes", "tig_fp8_dequantize",
     "tig_plan_describe",
     "tig_status_string", "tig_last_error",
     "tree_gemm", "logprob_gather", "moe_tree_gemm_combine", "moe_route", "topk_positions",
-    "expert_gemm_masked", "expert_gemm_contiguous", "silu_mul", "fp8_quantize", "fp8_tree_gemm",
+    "expert_gemm_masked", "expert_gemm_contiguous", "silu_mul", "fp8_quantize", "fp8_tree_gemm", "fp8_dequantize",
     "TIG_OK", "TIG_ERR_INVALID_ARG", "TIG_ERR_UNSUPPORTED", "TIG_ERR_WORKSPACE", "TIG_ERR_HIP",
     "TIG_OUT_F32", "TIG_OUT_BF16",
 ]
@@ -76,6 +76,7 @@ _SIGNATURES = {
     "tig_fp8_quantize": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i32, _vp]),
     "tig_fp8_tree_gemm": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
     "tig_fp8_gemm_workspace_bytes": (_i32, [_i64, _i64, _i64, ctypes.POINTER(_sz)]),
+    "tig_fp8_dequantize": (_i32, [_vp, _vp, _vp, _i64, _i64, _i32, _vp]),
     "tig_plan_describe": (_i32, [_i64, _i32, ctypes.POINTER(_Plan)]),
     "tig_status_string": (ctypes.c_char_p, [_i32]),
     "tig_last_error": (ctypes.c_char_p, []),
@@ -359,6 +360,23 @@ def tig_fp8_quantize(X, Q, scales, block_rows: int, stream=None) -> None:
     _check(st, "tig_fp8_quantize")
 
 
+def tig_fp8_dequantize(Q, scales, out, block_rows: int, stream=None) -> None:
+    """``out`` (bf16) = the E4M3 values of ``Q`` times their blocks' scales (exact)."""
+    torch = _torch()
+    _need(Q, "Q", torch.uint8, 2)
+    _need(scales, "scales", torch.uint8, 2)
+    _need(out, "out", torch.bfloat16, 2)
+    _same_device(Q, scales, out)
+    for t, n in ((Q, "Q"), (scales, "scales"), (out, "out")):
+        _contig(t, n)
+    R, C = Q.shape
+    if tuple(out.shape) != (R, C):
+        raise ValueError("out must have Q's shape")
+    st = load().tig_fp8_dequantize(Q.data_ptr(), scales.data_ptr(), out.data_ptr(), R, C, int(block_rows),
+                                   _stream(stream))
+    _check(st, "tig_fp8_dequantize")
+
+
 def tig_fp8_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
     out = _sz(0)
     _check(load().tig_fp8_gemm_workspace_bytes(int(M), int(N), int(K), ctypes.byref(out)),
@@ -527,3 +545,11 @@ def fp8_tree_gemm(QA, SA, QW, SW, leaves: int, out_dtype=None, workspace=None, s
     C = torch.empty((M, N), dtype=out_dtype or torch.float32, device=QA.device)
     tig_fp8_tree_gemm(QA, SA, QW, SW, C, leaves, workspace, stream)
     return C
+
+
+def fp8_dequantize(Q, scales, block_rows: int, stream=None):
+    """Allocate and return the bf16 output of tig_fp8_dequantize."""
+    torch = _torch()
+    out = torch.empty(Q.shape, dtype=torch.bfloat16, device=Q.device)
+    tig_fp8_dequantize(Q, scales, out, block_rows, stream)
+    return out

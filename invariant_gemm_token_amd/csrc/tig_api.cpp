@@ -391,14 +391,22 @@ tig_status tig_fp8_quantize(const void* X, int64_t ldx, uint8_t* Q, int64_t ldq,
   return ok();
 }
 
-static size_t fp8_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  return tig::align256(size_t(M) * size_t(K) * 2) + tig::align256(size_t(N) * size_t(K) * 2);
+tig_status tig_fp8_dequantize(const uint8_t* Q, const uint8_t* scales, void* out, int64_t R, int64_t C,
+                              int32_t block_rows, hipStream_t stream) {
+  if (R < 0 || C < 0) return fail(TIG_ERR_INVALID_ARG, "R and C must be >= 0");
+  if (block_rows != 1 && block_rows != 128) return fail(TIG_ERR_INVALID_ARG, "block_rows must be 1 or 128");
+  if (R == 0 || C == 0) return ok();
+  if (!Q || !scales || !out) return fail(TIG_ERR_INVALID_ARG, "Q, scales and out must not be NULL");
+  if (!aligned(out, 2)) return fail(TIG_ERR_INVALID_ARG, "out misaligned");
+  const hipError_t e = tig::launch_fp8_dequant(Q, scales, R, C, block_rows, static_cast<uint16_t*>(out), stream);
+  if (e != hipSuccess) return fail(TIG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
 }
 
 tig_status tig_fp8_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, size_t* bytes) {
   if (!bytes) return fail(TIG_ERR_INVALID_ARG, "bytes is NULL");
   if (M < 0 || N < 0 || K < 0) return fail(TIG_ERR_INVALID_ARG, "M, N and K must be >= 0");
-  *bytes = fp8_ws_bytes(M, N, K);
+  *bytes = tig::fp8_ws_bytes(M, N, K);
   return ok();
 }
 
@@ -408,27 +416,32 @@ tig_status tig_fp8_tree_gemm(const uint8_t* QA, const uint8_t* SA, const uint8_t
   if (M < 0 || N < 0) return fail(TIG_ERR_INVALID_ARG, "M and N must be >= 0");
   tig_status s = check_k_leaves(K, leaves);
   if (s != TIG_OK) return s;
+  if (K % (128 * int64_t(leaves)))
+    return fail(TIG_ERR_UNSUPPORTED, "K/leaves must be a multiple of 128 (one scale block per k-tile)");
   if (out_dtype != TIG_OUT_F32 && out_dtype != TIG_OUT_BF16)
     return fail(TIG_ERR_INVALID_ARG, "unknown out_dtype %d", int(out_dtype));
   if (ldc < N) return fail(TIG_ERR_INVALID_ARG, "ldc must be >= N");
   if (M == 0 || N == 0) return ok();
   if (!QA || !SA || !QW || !SW || !C) return fail(TIG_ERR_INVALID_ARG, "QA, SA, QW, SW and C must not be NULL");
-  if (K % 8) return fail(TIG_ERR_UNSUPPORTED, "K must be a multiple of 8");
+  if (!aligned(QA, 16) || !aligned(QW, 16)) return fail(TIG_ERR_UNSUPPORTED, "QA and QW must be 16-byte aligned");
   if (!aligned(C, out_dtype == TIG_OUT_F32 ? 4 : 2)) return fail(TIG_ERR_INVALID_ARG, "C is misaligned");
-  const size_t need = fp8_ws_bytes(M, N, K);
+  if ((s = check_span("A tile", 128, K / 2)) != TIG_OK) return s;
+  if ((s = check_span("W tile", tig::kBlockN, K / 2)) != TIG_OK) return s;
+  if (tig::cdiv(M, 128) * tig::cdiv(N, tig::kBlockN) >= (int64_t(1) << 31) - 8)
+    return fail(TIG_ERR_UNSUPPORTED, "too many output tiles");
+  if ((K / 128) * tig::fp8_table_width(M, N) >= (int64_t(1) << 32))
+    return fail(TIG_ERR_UNSUPPORTED, "scale table too large");
+  const size_t need = tig::fp8_ws_bytes(M, N, K);
   if (!workspace || workspace_bytes < need)
     return fail(TIG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : size_t(0));
   if (!aligned(workspace, 256)) return fail(TIG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  uint16_t* A16 = static_cast<uint16_t*>(workspace);
-  uint16_t* W16 = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + tig::align256(size_t(M) * K * 2));
-  // The dequantised values are exact in bf16 (4 significant bits times a power
-  // of two), and so are their products in FP32: the leaf-tree contraction of
-  // the dequantised operands is the W8A8 product with FP32 accumulation.
-  hipError_t e = tig::launch_fp8_dequant(QA, SA, M, K, 1, A16, stream);
-  if (e == hipSuccess) e = tig::launch_fp8_dequant(QW, SW, N, K, 128, W16, stream);
+  tig::Fp8GemmLaunch p{QA, SA, QW, SW, C, ldc, out_dtype == TIG_OUT_F32 ? tig::kEpiF32 : tig::kEpiBF16, M, N, K,
+                       log2i(leaves), static_cast<uint8_t*>(workspace), tig::fp8_table_rows(M),
+                       tig::fp8_table_width(M, N)};
+  const hipError_t e = tig::launch_fp8_gemm(p, stream);
   if (e != hipSuccess) return fail(TIG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
-  return tig_tree_gemm(A16, K, W16, K, C, ldc, out_dtype, M, N, K, leaves, stream);
+  return ok();
 }
 
 tig_status tig_topk_positions(const float* scores, int64_t ld, const int32_t* lengths, int64_t R,

@@ -159,6 +159,22 @@ hipError_t launch_fp8_quantize(const uint16_t* X, int64_t ldx, uint8_t* Q, int64
                                int64_t C, int block_rows, hipStream_t stream);
 hipError_t launch_fp8_dequant(const uint8_t* Q, const uint8_t* S, int64_t R, int64_t C, int block_rows,
                               uint16_t* out, hipStream_t stream);
+// W8A8 block-FP8 leaf-tree GEMM on the FP8 matrix cores.  table: workspace
+// for the per-call scale table [K/128][scw], scw = fp8_table_width(M, N).
+struct Fp8GemmLaunch {
+  const uint8_t* QA; const uint8_t* SA; const uint8_t* QW; const uint8_t* SW;
+  void* C; int64_t ldc;
+  int epi;
+  int64_t M, N, K;
+  int leaves_log2;
+  uint8_t* table; int64_t mrows, scw;
+};
+inline int64_t fp8_table_rows(int64_t M) { return cdiv(M, 128) * 128; }
+inline int64_t fp8_table_width(int64_t M, int64_t N) { return (fp8_table_rows(M) + cdiv(N, 128) + 3) / 4 * 4; }
+inline size_t fp8_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  return align256(size_t(K / 128) * size_t(fp8_table_width(M, N)));
+}
+hipError_t launch_fp8_gemm(const Fp8GemmLaunch& p, hipStream_t stream);
 // out[r, i] = bf16(SiLU(g) * u) in FP32, g = GU[r, i], u = GU[r, I + i], one rounding.
 hipError_t launch_silu_mul(const float* GU, int64_t ldgu, uint16_t* out, int64_t ldo, int64_t rows, int64_t I,
                            hipStream_t stream);

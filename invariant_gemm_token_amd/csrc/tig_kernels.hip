@@ -609,6 +609,251 @@ void tree_gemm_kernel(DenseOperands op, void* __restrict__ C, int64_t ldc, int k
 }
 
 // ---------------------------------------------------------------------------
+// Block-FP8 W8A8 leaf-tree GEMM on the FP8 matrix cores [BitRL, 4.1]:
+// v_mfma_scale_f32_32x32x64_f8f6f4 takes E4M3 operands and multiplies each
+// product by the E8M0 scales of its A row and W column (exact for these
+// power-of-two scales), accumulating in FP32.  The operand bytes ride the
+// bf16 DMA path unchanged: a row of K E4M3 bytes is K/2 16-bit words, and a
+// k-tile of 64 words is 128 values, one scale block.  Each stage adds one DMA
+// per wave: the k-tile's 128 A-row scales and the tile's W scale, from a table
+// SC [K/128][scw] built per call (the A rows' scales, then the n-blocks'),
+// into a 256-byte area of the wave's own; every wave issues the same number of
+// DMAs, so the constant wait count of the ring holds.  Two k-steps of 64 per
+// k-tile; the leaves and their tree are those of the bf16 kernel.
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+struct GeoF8 {
+  static constexpr int MI = 2;
+  static constexpr int BM = 128;
+  static constexpr int A_BYTES = BM * 128;
+  static constexpr int W_BYTES = BN * 128;
+  static constexpr int SC_OFF = A_BYTES + W_BYTES;     // the four waves' scale areas
+  static constexpr int STAGE = SC_OFF + 4 * 256;
+  static constexpr int STAGES = kLdsBytes / STAGE;     // 4
+  static constexpr int A_SEG = 4;                      // 1 KiB A segments per wave, as the bf16 tile of 128 rows
+  static constexpr int VM_PER_STAGE = A_SEG + 4 + 1;   // A, W, scales
+  static_assert(STAGES >= 3, "ring too shallow");
+  static_assert(VM_PER_STAGE * (STAGES - 2) < 64, "vmcnt range");
+  static_assert(64 * BN * 4 <= STAGE, "epilogue pass must fit one ring buffer");
+};
+
+struct F8Operands {
+  DenseOperands op;            // the E4M3 bytes as 16-bit words: lda = ldw = K / 2
+  const uint8_t* sc;           // scale table [K/128][scw]
+  int64_t scw, mrows, ksc;     // its row length, the A part of a row (M rounded up to 128), K/128
+};
+
+struct LoaderF8 : Loader<2> {
+  F8Operands f;
+  __amdgpu_buffer_rsrc_t rsc;
+  uint32_t osc;                // this lane's byte offset in a row of the table (or past its end)
+
+  __device__ __forceinline__ void setup(int mt, int nt) {
+    Loader<2>::setup(mt, nt);
+    const int lane = threadIdx.x & 63;
+    rsc = make_rsrc(f.sc, uint32_t(f.ksc * f.scw));
+    osc = lane < 32 ? uint32_t(int64_t(mt) * GeoF8::BM + 4 * lane)
+                    : (lane == 32 ? uint32_t(f.mrows + (nt & ~3)) : OOB);
+  }
+  template <int J>
+  __device__ __forceinline__ void seg(char* stage, int kt) const {
+    if constexpr (J < GeoF8::A_SEG + 4) {
+      Loader<2>::template seg<J>(stage, kt);
+    } else {
+      const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (LDS_AS void*)(stage + GeoF8::SC_OFF + wave * 256), 4, osc,
+                                               uint32_t(kt) * uint32_t(f.scw), 0, 0);
+    }
+  }
+  template <int J0, int D>
+  __device__ __forceinline__ void segs(char* stage, int kt) const {
+    if constexpr (D > 0) {
+      seg<J0>(stage, kt);
+      segs<J0 + 1, D - 1>(stage, kt);
+    }
+  }
+  __device__ __forceinline__ void issue_all(char* stage, int kt) const {
+    segs<0, GeoF8::VM_PER_STAGE>(stage, kt);
+  }
+};
+
+// Fragments of one k-step of 64: 32 bytes of a row per lane (two 16-byte
+// chunks, logical chunks 4 s + 2 (lane / 32) and the next).
+struct FragF8 { i32x8 a[2], b0, b1; };
+
+struct FragAddrF8 {
+  uint32_t a0, w0, w1;
+  int fr, fk;
+  __device__ __forceinline__ i32x8 pair(const char* st, uint32_t row_off, int s) const {
+    const int sw = (fr >> 1) & 7;
+    const int c0 = 4 * s + 2 * fk;
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(st + row_off + uint32_t((c0 ^ sw) << 4));
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(st + row_off + uint32_t(((c0 + 1) ^ sw) << 4));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  __device__ __forceinline__ void read(FragF8& f, const char* st, int s) const {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) f.a[i] = pair(st, a0 + i * 32 * 128, s);
+    f.b0 = pair(st, w0, s);
+    f.b1 = pair(st, w1, s);
+  }
+};
+
+template <bool FIRST>
+__device__ __forceinline__ void mfma_step_f8(AccT<2>& c, const FragF8& f, const int (&sa)[2], int sw) {
+  const f32x16 z = {};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    c.c[i][0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b0, FIRST ? z : c.c[i][0], 0, 0, 0, sa[i],
+                                                                0, sw);
+    c.c[i][1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b1, FIRST ? z : c.c[i][1], 0, 0, 0, sa[i],
+                                                                0, sw);
+  }
+}
+
+// Scheduling hint for one FP8 step: 4 MFMAs with the 8 fragment reads of the
+// next step and D DMA instructions between them.
+template <int D>
+__device__ __forceinline__ void sched_step_f8() {
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    if (((t + 1) * D) / 4 > (t * D) / 4) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+  }
+}
+
+// The persistent leaf-tree loop of leaf_tree_persistent with FP8 stages: the
+// same ring discipline (constant DMA count per stage, the mid-stage wait and
+// barrier, the last k-tile re-issued past the end), two k-steps per stage,
+// fragments read one step ahead, the stage's scales read at its start.
+template <int LG, class Epi>
+__device__ __forceinline__ void leaf_tree_persistent_f8(LoaderF8& ld, int ktiles, const TileSched& ts, Epi& epi,
+                                                        char* smem) {
+  using G = GeoF8;
+  constexpr int STAGES = G::STAGES;
+  constexpr uint32_t RING = uint32_t(STAGES * G::STAGE);
+  const int n_my = ts.count();
+  if (n_my == 0) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  FragAddrF8 fa;
+  fa.fr = lane & 31;
+  fa.fk = lane >> 5;
+  fa.a0 = uint32_t((wm * 64 + fa.fr) * 128);
+  fa.w0 = uint32_t(G::A_BYTES + (wn * 64 + fa.fr) * 128);
+  fa.w1 = fa.w0 + 32 * 128;
+  const uint32_t sc_off = uint32_t(G::SC_OFF + wave * 256);
+  constexpr int L = 1 << LG;
+  const int kpl = ktiles >> LG;
+  const int total = n_my * ktiles;
+  const int m0 = __builtin_amdgcn_readfirstlane(ts.lmask & (L - 1));
+  int l_tile = 0, l_pos = 0, l_j = 0, kt = m0 * kpl, issued = 0;
+  {
+    int mt, nt;
+    ts.coords(0, mt, nt);
+    ld.setup(mt, nt);
+  }
+  auto advance = [&]() {
+    if (++issued >= total) return;
+    ++kt;
+    if (++l_j == kpl) {
+      l_j = 0;
+      if (++l_pos == L) {
+        l_pos = 0;
+        ++l_tile;
+        int mt, nt;
+        ts.coords(l_tile, mt, nt);
+        ld.setup(mt, nt);
+      }
+      kt = (l_pos ^ m0 ^ ((l_tile & 1) ? (L - 1) : 0)) * kpl;
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p) {
+    ld.issue_all(smem + p * G::STAGE, kt);
+    advance();
+  }
+  uint32_t off_q = 0, off_pf = RING - uint32_t(G::STAGE);
+  FragF8 F0, F1;
+  wait_vmcnt_lgkm0<G::VM_PER_STAGE * (STAGES - 2)>();
+  bar();
+  fa.read(F0, smem, 0);
+
+  constexpr int VM = G::VM_PER_STAGE;
+  constexpr int D0 = VM / 2, D1 = VM - VM / 2;
+  constexpr int MID_WAIT = VM * (STAGES - 3) + D0;
+  int wsel = 0;                 // byte of the W scale in its dword: the tile's n-block % 4
+  auto stage = [&](AccT<2>& cur, auto first) {
+    const char* st = smem + off_q;
+    char* pb = smem + off_pf;
+    const uint32_t off_n = off_q + G::STAGE == RING ? 0u : off_q + uint32_t(G::STAGE);
+    int sa[2];
+    sa[0] = *reinterpret_cast<const uint8_t*>(st + sc_off + wm * 64 + fa.fr);
+    sa[1] = *reinterpret_cast<const uint8_t*>(st + sc_off + wm * 64 + 32 + fa.fr);
+    const int sw = *reinterpret_cast<const uint8_t*>(st + sc_off + 128 + wsel);
+    fa.read(F1, st, 1);
+    mfma_step_f8<decltype(first)::value>(cur, F0, sa, sw);
+    ld.template segs<0, D0>(pb, kt);
+    sched_step_f8<D0>();
+    wait_vmcnt_lgkm0<MID_WAIT>();   // stage q+1 landed; this wave's reads of stage q returned
+    bar();                          // every wave is done with stage q's buffer
+    fa.read(F0, smem + off_n, 0);
+    mfma_step_f8<false>(cur, F1, sa, sw);
+    ld.template segs<D0, D1>(pb, kt);
+    sched_step_f8<D1>();
+    advance();
+    off_pf = off_q;
+    off_q = off_n;
+  };
+
+  for (int ti = 0; ti < n_my; ++ti) {
+    int mt, nt;
+    ts.coords(ti, mt, nt);
+    wsel = nt & 3;
+    AccT<2> pend[LG > 0 ? LG : 1];
+    AccT<2> cur;
+#pragma unroll 1
+    for (int pos = 0; pos < L; ++pos) {
+      stage(cur, std::true_type{});
+      for (int j = 1; j < kpl; ++j) stage(cur, std::false_type{});
+      tree_fold<0, LG>(pend, cur, pos);
+    }
+    epi(cur, mt, nt, smem + off_pf);
+  }
+  wait_vmcnt<0>();
+}
+
+template <int LG, int EPI>
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fp8_tree_gemm_kernel(F8Operands f, void* __restrict__ C, int64_t ldc, int ktiles, int n_mt, int n_nt) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  TileSched ts;
+  ts.init(n_mt, n_nt);
+  StoreEpi<EPI, 2> epi{C, ldc, f.op.M, f.op.N};
+  LoaderF8 ld;
+  ld.op = f.op;
+  ld.f = f;
+  leaf_tree_persistent_f8<LG>(ld, ktiles, ts, epi, smem);
+}
+
+// The scale table of one call: row kb = [the A rows' scales (127 = 1 past M)
+// up to mrows][the n-blocks' W scales][127 up to scw].
+__global__ __launch_bounds__(256) void fp8_scale_table_kernel(const uint8_t* __restrict__ SA,
+                                                              const uint8_t* __restrict__ SW, int64_t M, int64_t nb,
+                                                              int64_t ksc, int64_t mrows, int64_t scw,
+                                                              uint8_t* __restrict__ sc) {
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < ksc * scw; i += int64_t(gridDim.x) * 256) {
+    const int64_t kb = i / scw, c = i % scw;
+    uint8_t v = 127;
+    if (c < M) v = SA[c * ksc + kb];
+    else if (c >= mrows && c < mrows + nb) v = SW[(c - mrows) * ksc + kb];
+    sc[i] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // logprob, pass 1: per (row, 128-column vocabulary tile) the max m_t and
 // s_t = sum exp2((x - m_t) log2 e) by the balanced adjacent-pair tree over the
 // 128 columns (padded columns add +0), plus the sampled token's logit.
@@ -1630,6 +1875,27 @@ hipError_t launch_group_lg(const GroupLaunch& p, hipStream_t s) {
   else return launch_group_mi<LG, 2>(p, s);
 }
 
+template <int LG>
+hipError_t launch_fp8_lg(const Fp8GemmLaunch& p, hipStream_t s) {
+  const int64_t ksc = p.K / 128, nb = cdiv(p.N, 128);
+  hipLaunchKernelGGL(fp8_scale_table_kernel, dim3(unsigned(cdiv(ksc * p.scw, 256) < 4096 ? cdiv(ksc * p.scw, 256) : 4096)),
+                     dim3(256), 0, s, p.SA, p.SW, p.M, nb, ksc, p.mrows, p.scw, p.table);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int n_mt = int(cdiv(p.M, GeoF8::BM)), n_nt = int(cdiv(p.N, BN));
+  const F8Operands f{DenseOperands{reinterpret_cast<const uint16_t*>(p.QA), p.K / 2, p.M,
+                                   reinterpret_cast<const uint16_t*>(p.QW), p.K / 2, p.N},
+                     p.table, p.scw, p.mrows, ksc};
+  const dim3 grid(persistent_grid(int64_t(n_mt) * n_nt));
+  if (p.epi == kEpiF32)
+    hipLaunchKernelGGL((fp8_tree_gemm_kernel<LG, kEpiF32>), grid, dim3(NTHREADS), 0, s, f, p.C, p.ldc, int(ksc), n_mt,
+                       n_nt);
+  else
+    hipLaunchKernelGGL((fp8_tree_gemm_kernel<LG, kEpiBF16>), grid, dim3(NTHREADS), 0, s, f, p.C, p.ldc, int(ksc), n_mt,
+                       n_nt);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_tree_gemm(const TreeGemmLaunch& p, hipStream_t s) {
@@ -2136,6 +2402,17 @@ hipError_t launch_fp8_quantize(const uint16_t* X, int64_t ldx, uint8_t* Q, int64
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_fp8_gemm(const Fp8GemmLaunch& p, hipStream_t s) {
+  switch (p.leaves_log2) {
+    case 0: return launch_fp8_lg<0>(p, s);
+    case 1: return launch_fp8_lg<1>(p, s);
+    case 2: return launch_fp8_lg<2>(p, s);
+    case 3: return launch_fp8_lg<3>(p, s);
+    case 4: return launch_fp8_lg<4>(p, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_fp8_dequant(const uint8_t* Q, const uint8_t* S, int64_t R, int64_t C, int block_rows,

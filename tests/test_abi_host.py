@@ -195,12 +195,15 @@ def test_fp8_arguments_rejected():
     assert lib.tig_fp8_quantize(None, 100, None, 256, None, 4, 256, 1, None) == tig.TIG_ERR_INVALID_ARG    # ldx < C
     assert lib.tig_fp8_quantize(None, 256, None, 256, None, 4, 256, 1, None) == tig.TIG_ERR_INVALID_ARG    # NULL
     assert lib.tig_fp8_quantize(None, 256, None, 256, None, 0, 256, 128, None) == tig.TIG_OK
-    assert lib.tig_fp8_tree_gemm(None, None, None, None, None, 64, 0, 8, 64, 512, 8, None, 0, None) == \
+    assert lib.tig_fp8_tree_gemm(None, None, None, None, None, 64, 0, 8, 64, 1024, 8, None, 0, None) == \
         tig.TIG_ERR_INVALID_ARG
-    assert lib.tig_fp8_tree_gemm(None, None, None, None, None, 64, 0, 8, 64, 512, 16, None, 0, None) == \
+    # K/leaves must hold whole 128-wide scale blocks
+    assert lib.tig_fp8_tree_gemm(None, None, None, None, None, 64, 0, 8, 64, 512, 8, None, 0, None) == \
         tig.TIG_ERR_UNSUPPORTED
-    assert lib.tig_fp8_tree_gemm(None, None, None, None, None, 64, 0, 0, 64, 512, 8, None, 0, None) == tig.TIG_OK
-    assert tig.tig_fp8_gemm_workspace_bytes(10, 20, 512) == 10 * 512 * 2 + 20 * 512 * 2
+    assert lib.tig_fp8_tree_gemm(None, None, None, None, None, 64, 0, 0, 64, 1024, 8, None, 0, None) == tig.TIG_OK
+    # the scale table: K/128 rows of (M rounded up to 128) + ceil(N/128) bytes, rounded up to 4
+    assert tig.tig_fp8_gemm_workspace_bytes(10, 20, 512) == 768          # 4 * 132 = 528 -> 768
+    assert lib.tig_fp8_dequantize(None, None, None, 4, 128, 2, None) == tig.TIG_ERR_INVALID_ARG
 
 
 def test_null_pointers_rejected():

@@ -60,8 +60,9 @@ def _quant_pair(gpu_lib, A, W):
     return QA, SA, QW, SW
 
 
-@pytest.mark.parametrize("M,N,K,L", [(257, 300, 1024, 8), (1, 130, 512, 8), (64, 256, 2048, 16)])
-def test_fp8_gemm_matches_oracle_and_is_the_dequantised_tree(gpu_lib, M, N, K, L):
+@pytest.mark.parametrize("M,N,K,L", [(257, 300, 1024, 8), (1, 130, 1024, 8), (64, 256, 2048, 16),
+                                     (300, 129, 512, 1), (129, 640, 4096, 4)])
+def test_fp8_gemm_matches_oracle(gpu_lib, M, N, K, L):
     rng = np.random.default_rng(4200 + M + N + K)
     A = wl.normal_bf16(rng, (M, K), 1.0)
     W = wl.normal_bf16(rng, (N, K), 0.02)
@@ -73,13 +74,74 @@ def test_fp8_gemm_matches_oracle_and_is_the_dequantised_tree(gpu_lib, M, N, K, L
     ref = oracle.fp8_gemm_ref(qa, ea, qw, ew)
     worst = assert_gemm_close(C.cpu().numpy(), ref, what="fp8 gemm")
     say(f"fp8 gemm worst relative error {worst:.3e}")
-    # the dequantised operands are exact bf16 values: the product is tig_tree_gemm on them
-    Ad = wl.f32_to_bf16_bits(oracle.fp8_dequant(qa, ea, 1).astype(np.float32))
-    Wd = wl.f32_to_bf16_bits(oracle.fp8_dequant(qw, ew, 128).astype(np.float32))
-    assert np.array_equal(oracle.bf16_bits_to_f64(Ad), oracle.fp8_dequant(qa, ea, 1))
-    assert_bitwise(C, gpu_lib.tree_gemm(dev_bf16(Ad), dev_bf16(Wd), L), "fp8 gemm vs tree_gemm of dequantised")
+    # the same product through the bf16 matrix cores (exact operands, another order)
+    Ad = gpu_lib.fp8_dequantize(QA, SA, 1)
+    Wd = gpu_lib.fp8_dequantize(QW, SW, 128)
+    assert_gemm_close(gpu_lib.tree_gemm(Ad, Wd, L).cpu().numpy(), ref, what="bf16 path of the same values")
     Cb = gpu_lib.fp8_tree_gemm(QA, SA, QW, SW, L, torch.bfloat16)
     assert np.array_equal(Cb.cpu().view(torch.int16).numpy().view(np.uint16), wl.f32_to_bf16_bits(C.cpu().numpy()))
+
+
+def test_fp8_dequantize_is_exact(gpu_lib):
+    rng = np.random.default_rng(4250)
+    for br, (R, C) in ((1, (50, 384)), (128, (200, 260))):
+        X = _special(wl.normal_bf16(rng, (R, C), 0.3), rng)
+        Q, S = gpu_lib.fp8_quantize(dev_bf16(X), br)
+        D = gpu_lib.fp8_dequantize(Q, S, br).cpu().view(torch.int16).numpy().view(np.uint16)
+        ref = oracle.fp8_dequant(Q.cpu().numpy(), S.cpu().numpy().astype(np.int64) - 127, br)
+        # exact in bf16, except a largest-magnitude value that rounded up to 2^8 * 2^120 = 2^128,
+        # which overflows to an infinity: compare with the rounding of the exact value
+        assert np.array_equal(D, oracle.f64_to_bf16_rne(ref))
+
+
+def _codes(vals):
+    """E4M3 codes of exactly representable values."""
+    return oracle.f64_to_e4m3_rne(np.asarray(vals, dtype=np.float64))
+
+
+def test_fp8_gemm_exact_on_integer_products(gpu_lib):
+    """Small integer values (codes of -4 .. 4, scales 1): every product and
+    partial sum is an integer far below 2^24, so any order gives the exact sum."""
+    rng = np.random.default_rng(4260)
+    M, N, K, L = 200, 260, 1024, 8
+    qa = _codes(rng.integers(-4, 5, size=(M, K)))
+    qw = _codes(rng.integers(-4, 5, size=(N, K)))
+    SA = torch.full((M, K // 128), 127, dtype=torch.uint8, device=DEV)
+    SW = torch.full((-(-N // 128), K // 128), 127, dtype=torch.uint8, device=DEV)
+    C = gpu_lib.fp8_tree_gemm(torch.from_numpy(qa).to(DEV), SA, torch.from_numpy(qw).to(DEV), SW, L)
+    exact = oracle.e4m3_value(qa).astype(np.int64) @ oracle.e4m3_value(qw).astype(np.int64).T
+    assert np.array_equal(C.cpu().numpy().astype(np.int64), exact)
+
+
+def test_fp8_gemm_leaf_tree_closed_form(gpu_lib):
+    """K = 8 leaves of 128; leaf partials 2^24 (one product 2^12 * 2^12 through the
+    scales) and seven 1s (1 * 1).  The balanced tree gives ((2^24 + 1) + 2) + 4 =
+    2^24 + 6 (2^24 + 1 ties to 2^24); a sequential sum gives 2^24, the exact sum
+    2^24 + 7.  The large leaf sits at every position in turn."""
+    L, K, N = 8, 1024, 128
+    M = L
+    qa = np.zeros((M, K), np.uint8)
+    qw = np.zeros((N, K), np.uint8)
+    one = int(_codes([1.0])[0])
+    ea = np.zeros((M, K // 128), np.int64)
+    ew = np.zeros((1, K // 128), np.int64)
+    for r in range(M):
+        for leaf in range(L):
+            qa[r, leaf * 128] = one
+            if leaf == r:
+                ea[r, leaf] = 12
+    qw[:, :] = 0
+    qw[:, ::128] = one
+    ew[0, :] = 12
+    # W's scale applies to all rows: undo it on the small leaves through A's scale
+    for r in range(M):
+        for leaf in range(L):
+            if leaf != r:
+                ea[r, leaf] = -12
+    C = gpu_lib.fp8_tree_gemm(torch.from_numpy(qa).to(DEV), torch.from_numpy((ea + 127).astype(np.uint8)).to(DEV),
+                              torch.from_numpy(qw).to(DEV), torch.from_numpy((ew + 127).astype(np.uint8)).to(DEV),
+                              L).cpu().numpy()
+    assert np.all(C == np.float32(2.0 ** 24 + 6)), np.unique(C)
 
 
 def test_fp8_path_rows_do_not_depend_on_the_batch(gpu_lib):
