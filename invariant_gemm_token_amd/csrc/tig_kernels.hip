@@ -1678,6 +1678,41 @@ __global__ __launch_bounds__(256) void fp8_quant_rows_kernel(const uint16_t* __r
   }
 }
 
+// The same for C % 4 == 0 with 8-byte aligned rows: one wave per two groups
+// (256 columns) of a row, lane l holding columns 4l .. 4l+3 (one 8-byte load,
+// one 4-byte store); each half-wave reduces its group's amax.
+__global__ __launch_bounds__(256) void fp8_quant_rows4_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                              uint8_t* __restrict__ Q, int64_t ldq,
+                                                              uint8_t* __restrict__ S, int64_t R, int64_t C) {
+  const int64_t ngroups = (C + 127) / 128, npairs = (ngroups + 1) / 2;
+  const int lane = threadIdx.x & 63;
+  for (int64_t r = blockIdx.y; r < R; r += gridDim.y)
+  for (int64_t gp = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6); gp < npairs; gp += int64_t(gridDim.x) * 4) {
+    const int64_t c0 = gp * 256 + 4 * lane;
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (c0 < C) {
+      const uint2 d = *reinterpret_cast<const uint2*>(X + r * ldx + c0);
+      v[0] = __builtin_bit_cast(float, d.x << 16);
+      v[1] = __builtin_bit_cast(float, d.x & 0xFFFF0000u);
+      v[2] = __builtin_bit_cast(float, d.y << 16);
+      v[3] = __builtin_bit_cast(float, d.y & 0xFFFF0000u);
+    }
+    float m = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
+                              __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3])));
+#pragma unroll
+    for (int d = 1; d < 32; d *= 2) m = __builtin_fmaxf(m, __shfl_xor(m, d));
+    const int e = fp8_block_exponent(m);
+    if (c0 < C) {
+      uint32_t q = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q |= f32_to_e4m3_rne(__builtin_ldexpf(v[i], -e)) << (8 * i);
+      *reinterpret_cast<uint32_t*>(Q + r * ldq + c0) = q;
+    }
+    const int64_t g = 2 * gp + (lane >> 5);
+    if ((lane & 31) == 0 && g < ngroups) S[r * ngroups + g] = uint8_t(e + 127);
+  }
+}
+
 // One workgroup per 128 x 128 block (weights): thread t takes columns
 // 2 (t % 64), +1 of rows t / 64, t / 64 + 4, ...
 __global__ __launch_bounds__(256) void fp8_quant_blocks_kernel(const uint16_t* __restrict__ X, int64_t ldx,
@@ -2389,7 +2424,13 @@ hipError_t launch_fp8_quantize(const uint16_t* X, int64_t ldx, uint8_t* Q, int64
                                int64_t C, int block_rows, hipStream_t s) {
   if (R <= 0 || C <= 0) return hipSuccess;
   const int64_t ngroups = cdiv(C, 128);
-  if (block_rows == 1) {
+  if (block_rows == 1 && C % 4 == 0 && ldx % 4 == 0 && ldq % 4 == 0 && (reinterpret_cast<uintptr_t>(X) & 7) == 0 &&
+      (reinterpret_cast<uintptr_t>(Q) & 3) == 0) {
+    // One workgroup per row (its four waves walk the row's group pairs):
+    // short waves would leave the launch dominated by dispatch.
+    hipLaunchKernelGGL(fp8_quant_rows4_kernel, dim3(1u, unsigned(R < 65535 ? R : 65535)), dim3(256), 0, s, X, ldx, Q,
+                       ldq, S, R, C);
+  } else if (block_rows == 1) {
     const int64_t waves = R * ngroups;
     const int64_t wgs = cdiv(waves, 4);
     hipLaunchKernelGGL(fp8_quant_rows_kernel, dim3(unsigned(wgs < 65536 ? wgs : 65536)), dim3(256), 0, s, X, ldx,
