@@ -108,6 +108,20 @@ def test_expert_gemm_bf16_output_is_the_rounded_f32(gpu_lib):
         assert np.array_equal(b16[sl], wl.f32_to_bf16_bits(f32[sl]))
 
 
+def test_expert_gemm_repeat_calls_identical(gpu_lib):
+    rng = np.random.default_rng(3250)
+    E, K, N, L = 5, 1024, 384, 8
+    counts_l = (300, 7, 0, 129, 64)
+    rows_e = [wl.normal_bf16(rng, (c, K), 1.0) for c in counts_l]
+    W = wl.normal_bf16(rng, (E, N, K), 0.02)
+    counts, Xm, Xc, starts = _layouts(rng, rows_e, K, 320, 128)
+    first = _masked(gpu_lib, Xm, counts, W, L)
+    for _ in range(3):
+        again = _masked(gpu_lib, Xm, counts, W, L)
+        for e, c in enumerate(counts_l):          # rows no expert owns are not written
+            assert_bitwise(again[e, :c], first[e, :c], f"masked repeat, expert {e}")
+
+
 def test_expert_counts_clamped(gpu_lib):
     """Masked: a count above cap keeps the block's cap rows; below 0 counts as
     0.  Contiguous: rows that would lie past M are not computed (not written)."""

@@ -145,6 +145,18 @@ def test_fp8_gemm_leaf_tree_closed_form(gpu_lib):
     assert np.all(C == np.float32(2.0 ** 24 + 6)), np.unique(C)
 
 
+def test_fp8_repeat_calls_identical(gpu_lib):
+    rng = np.random.default_rng(4280)
+    A = wl.normal_bf16(rng, (700, 2048), 1.0)
+    W = wl.normal_bf16(rng, (520, 2048), 0.02)
+    QA, SA, QW, SW = _quant_pair(gpu_lib, A, W)
+    first = gpu_lib.fp8_tree_gemm(QA, SA, QW, SW, 8)
+    for _ in range(3):
+        assert_bitwise(gpu_lib.fp8_tree_gemm(QA, SA, QW, SW, 8), first, "fp8 gemm repeat")
+        Q2, S2 = gpu_lib.fp8_quantize(dev_bf16(A), 1)
+        assert torch.equal(Q2, QA) and torch.equal(S2, SA)
+
+
 def test_fp8_path_rows_do_not_depend_on_the_batch(gpu_lib):
     """Quantise + GEMM of a row alone equals the same row inside batches of
     several sizes (per-token activation blocks, one accumulation order)."""

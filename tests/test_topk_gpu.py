@@ -116,6 +116,15 @@ def test_topk_row_position_invariance(gpu_lib):
         assert np.array_equal(got, oracle.topk_positions(batch, lengths, k))
 
 
+def test_topk_repeat_calls_identical(gpu_lib):
+    rng = np.random.default_rng(7400)
+    scores = wl.indexer_scores(rng, 64, 65536, "int")
+    lengths = wl.request_lengths(rng, 64, 0, 65536)
+    first = _run(gpu_lib, scores, lengths, 2048)
+    for _ in range(3):
+        assert np.array_equal(_run(gpu_lib, scores, lengths, 2048), first)
+
+
 @pytest.mark.slow
 def test_topk_indexer_config(gpu_lib):
     """The indexer workload the bench times (128 rows, pitch 65536, k = 2048,
