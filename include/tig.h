@@ -47,7 +47,10 @@
  *     launches nothing and returns a status; tig_last_error() gives a message
  *     for the calling thread's last failure;
  *   - bf16 pointers must be 16-byte aligned and their row strides multiples of
- *     8 elements (16 bytes), else TIG_ERR_UNSUPPORTED.
+ *     8 elements (16 bytes), else TIG_ERR_UNSUPPORTED;
+ *   - a workspace holds one call's intermediate data from its launch to its
+ *     last kernel: calls that may run at the same time (other streams) need
+ *     workspaces of their own; outputs must not overlap inputs.
  */
 #ifndef TIG_H
 #define TIG_H
