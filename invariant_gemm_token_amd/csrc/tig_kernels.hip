@@ -173,7 +173,6 @@ struct Geo {
   static constexpr int VM_PER_STAGE = A_SEG + 4;        // DMA instructions per wave per k-tile
   static_assert(STAGES >= 3, "ring too shallow");
   static_assert(VM_PER_STAGE * (STAGES - 2) < 64, "vmcnt range");
-  static_assert(64 * BN * 4 <= STAGE, "epilogue pass must fit one ring buffer");
 };
 
 
@@ -502,6 +501,7 @@ struct StoreEpi {
 // ring, which returns in order.)
 template <int MI, bool SPLIT = false>
 struct LogprobEpi {
+  static_assert(64 * BN * 4 <= Geo<MI>::STAGE, "the transpose pass must fit one ring buffer");
   static constexpr bool kSplitTop = SPLIT;
   float2* part; int64_t M, V; int n_vt;
   float* scratch;   // SPLIT: this launch's spill area, kSpillBytesPerGroup bytes per workgroup
@@ -1800,6 +1800,7 @@ hipError_t launch_tree_gemm_mi(const TreeGemmLaunch& p, hipStream_t s) {
 
 template <int LG>
 hipError_t launch_tree_gemm_lg(const TreeGemmLaunch& p, hipStream_t s) {
+  if (tree_gemm_block_m(p.M, p.N, LG) == 64) return launch_tree_gemm_mi<LG, 1>(p, s);
   if constexpr (block_m_for_log2(LG) == 192) {
     if (block_m_for(p.M, LG) == 192) return launch_tree_gemm_mi<LG, 3>(p, s);
   }

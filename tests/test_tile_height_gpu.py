@@ -1,7 +1,8 @@
 """Schedule freedom on the GPU: tile height, leaf visiting order, sampled-logit pass.
 
 The dense kernels use 192-row tiles where that needs fewer tiles than 128-row
-ones (and 128 rows otherwise; tree_gemm always at 16 leaves, while the logprob
+ones (and 128 rows otherwise; tree_gemm also 64 rows when 128-row tiles would
+fill fewer than 128 CUs, and always 128 at 16 leaves, while the logprob
 path then keeps the left half of each tile's leaf tree in scratch and adds it
 to the right half's root at the end), and a workgroup that runs several tiles
 visits the leaves of every other tile last to first.  Only the schedule may
@@ -26,7 +27,9 @@ from gpu_util import assert_bitwise, dev_bf16, say
 pytestmark = pytest.mark.gpu
 
 
-def _block_m(M, L, logprob=False):
+def _block_m(M, L, logprob=False, N=None):
+    if not logprob and -(-M // 128) * -(-N // 128) < 128:
+        return 64                                   # tree_gemm on small grids
     tall = 192 if L <= 8 or logprob else 128
     return 192 if tall == 192 and -(-M // 192) < -(-M // 128) else 128
 
@@ -56,15 +59,25 @@ def test_logprob_rows_identical_across_tile_heights(gpu_lib, L):
 
 @pytest.mark.parametrize("L", [2, 8, 16])
 def test_tree_gemm_rows_identical_across_tile_heights(gpu_lib, L):
-    K, N, M = 1024, 300, 577
+    """64 columns of n-tiles: a slice of 128 rows or fewer runs on 64-row tiles
+    (fewer than 128 tiles of 128 rows), longer slices on 128- or 192-row tiles;
+    the last columns (N = 8187) leave a ragged n-tile; a narrow W (300 columns)
+    puts the whole batch on 64-row tiles."""
+    K, N, M = 1024, 8187, 577
     rng = np.random.default_rng(777 + L)
     A = dev_bf16(wl.normal_bf16(rng, (M, K), 1.0))
     W = dev_bf16(wl.normal_bf16(rng, (N, K), 0.02))
     full = gpu_lib.tree_gemm(A, W, L)
+    narrow = gpu_lib.tree_gemm(A, W[:300].contiguous(), L)
+    assert_bitwise(narrow, full[:, :300], f"tree_gemm narrow W L={L}")
+    heights = {_block_m(M, L, N=300)}
     for a, b in SLICES:
-        say(f"tree_gemm L={L} rows [{a}, {b}) tile rows {_block_m(b - a, L)}")
+        h = _block_m(b - a, L, N=N)
+        heights.add(h)
+        say(f"tree_gemm L={L} rows [{a}, {b}) tile rows {h}")
         part = gpu_lib.tree_gemm(A[a:b].contiguous(), W, L)
         assert_bitwise(part, full[a:b], f"tree_gemm rows [{a},{b}) L={L}")
+    assert heights == ({64, 128, 192} if L <= 8 else {64, 128})
 
 
 @pytest.mark.parametrize("L", [1, 2, 4, 8, 16])
