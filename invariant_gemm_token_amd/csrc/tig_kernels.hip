@@ -1713,6 +1713,53 @@ __global__ __launch_bounds__(256) void fp8_quant_rows4_kernel(const uint16_t* __
   }
 }
 
+// The same for C % 4 == 0 with 8-byte aligned rows: lane l of wave w takes
+// columns 4 (l % 32) .. +3 of rows 8 i + 2 w + l / 32 (i = 0 .. 15), all 16
+// loads in flight at once and the 64 values kept in registers between the
+// block's amax and its rounding.
+__global__ __launch_bounds__(256) void fp8_quant_blocks4_kernel(const uint16_t* __restrict__ X, int64_t ldx,
+                                                                uint8_t* __restrict__ Q, int64_t ldq,
+                                                                uint8_t* __restrict__ S, int64_t R, int64_t C) {
+  __shared__ float red[4];
+  const int64_t ngroups = (C + 127) / 128;
+  const int64_t br = blockIdx.y, g = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t c0 = g * 128 + 4 * (lane & 31);
+  const bool col_ok = c0 < C;
+  uint2 d[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t r = br * 128 + 8 * i + 2 * wave + (lane >> 5);
+    d[i] = r < R && col_ok ? *reinterpret_cast<const uint2*>(X + r * ldx + c0) : make_uint2(0u, 0u);
+  }
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    m = __builtin_fmaxf(m, __builtin_fabsf(__builtin_bit_cast(float, d[i].x << 16)));
+    m = __builtin_fmaxf(m, __builtin_fabsf(__builtin_bit_cast(float, d[i].x & 0xFFFF0000u)));
+    m = __builtin_fmaxf(m, __builtin_fabsf(__builtin_bit_cast(float, d[i].y << 16)));
+    m = __builtin_fmaxf(m, __builtin_fabsf(__builtin_bit_cast(float, d[i].y & 0xFFFF0000u)));
+  }
+#pragma unroll
+  for (int k = 1; k < 64; k *= 2) m = __builtin_fmaxf(m, __shfl_xor(m, k));
+  if (lane == 0) red[wave] = m;
+  __syncthreads();
+  m = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  const int e = fp8_block_exponent(m);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t r = br * 128 + 8 * i + 2 * wave + (lane >> 5);
+    if (r < R && col_ok) {
+      const uint32_t q = f32_to_e4m3_rne(__builtin_ldexpf(__builtin_bit_cast(float, d[i].x << 16), -e)) |
+                         (f32_to_e4m3_rne(__builtin_ldexpf(__builtin_bit_cast(float, d[i].x & 0xFFFF0000u), -e)) << 8) |
+                         (f32_to_e4m3_rne(__builtin_ldexpf(__builtin_bit_cast(float, d[i].y << 16), -e)) << 16) |
+                         (f32_to_e4m3_rne(__builtin_ldexpf(__builtin_bit_cast(float, d[i].y & 0xFFFF0000u), -e)) << 24);
+      *reinterpret_cast<uint32_t*>(Q + r * ldq + c0) = q;
+    }
+  }
+  if (t == 0) S[br * ngroups + g] = uint8_t(e + 127);
+}
+
 // One workgroup per 128 x 128 block (weights): thread t takes columns
 // 2 (t % 64), +1 of rows t / 64, t / 64 + 4, ...
 __global__ __launch_bounds__(256) void fp8_quant_blocks_kernel(const uint16_t* __restrict__ X, int64_t ldx,
@@ -2438,8 +2485,13 @@ hipError_t launch_fp8_quantize(const uint16_t* X, int64_t ldx, uint8_t* Q, int64
                        Q, ldq, S, R, C);
   } else if (block_rows == 128) {
     if (cdiv(R, 128) > 65535) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fp8_quant_blocks_kernel, dim3(unsigned(ngroups), unsigned(cdiv(R, 128))), dim3(256), 0, s,
-                       X, ldx, Q, ldq, S, R, C);
+    if (C % 4 == 0 && ldx % 4 == 0 && ldq % 4 == 0 && (reinterpret_cast<uintptr_t>(X) & 7) == 0 &&
+        (reinterpret_cast<uintptr_t>(Q) & 3) == 0)
+      hipLaunchKernelGGL(fp8_quant_blocks4_kernel, dim3(unsigned(ngroups), unsigned(cdiv(R, 128))), dim3(256), 0, s,
+                         X, ldx, Q, ldq, S, R, C);
+    else
+      hipLaunchKernelGGL(fp8_quant_blocks_kernel, dim3(unsigned(ngroups), unsigned(cdiv(R, 128))), dim3(256), 0, s,
+                         X, ldx, Q, ldq, S, R, C);
   } else {
     return hipErrorInvalidValue;
   }

@@ -35,7 +35,7 @@ def _special(X, rng):
 
 
 @pytest.mark.parametrize("block_rows,R,C", [(1, 77, 1000), (1, 6, 128), (1, 9, 130), (1, 7, 384),
-                                            (128, 300, 260), (128, 128, 384)])
+                                            (128, 300, 260), (128, 128, 384), (128, 130, 130)])
 def test_fp8_quantize_bitwise(gpu_lib, block_rows, R, C):
     rng = np.random.default_rng(4000 + R + C)
     X = _special(wl.normal_bf16(rng, (R, C), 0.5 if block_rows == 1 else 0.02), rng)
