@@ -2022,11 +2022,12 @@ __device__ __forceinline__ int route_key(float v) {
   return b >= 0 ? b : (b ^ 0x7FFFFFFF);
 }
 
-constexpr int ROUTE_PER_LANE = kMaxRouteExperts / 64;
-
+// PER = candidates per lane: ceil(E / 64) rounded up to a power of two (<= 16).
+template <int PER>
 __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict__ logits, int64_t T, int E,
                                                         int topk, int32_t* __restrict__ ids,
                                                         float* __restrict__ gates) {
+  constexpr int ROUTE_PER_LANE = PER;
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;   // the whole wave
@@ -2088,8 +2089,18 @@ hipError_t launch_moe_route(const float* logits, int64_t T, int n_experts, int t
   if (T <= 0) return hipSuccess;
   if (n_experts < 1 || n_experts > kMaxRouteExperts || topk < 1 || topk > n_experts || topk > 64)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(moe_route_kernel, dim3(unsigned((T + 3) / 4)), dim3(256), 0, s, logits, T, n_experts, topk,
-                     topk_ids, topk_w);
+  const dim3 grid(unsigned((T + 3) / 4)), block(256);
+  const int per = (n_experts + 63) / 64;
+  if (per <= 1)
+    hipLaunchKernelGGL(moe_route_kernel<1>, grid, block, 0, s, logits, T, n_experts, topk, topk_ids, topk_w);
+  else if (per <= 2)
+    hipLaunchKernelGGL(moe_route_kernel<2>, grid, block, 0, s, logits, T, n_experts, topk, topk_ids, topk_w);
+  else if (per <= 4)
+    hipLaunchKernelGGL(moe_route_kernel<4>, grid, block, 0, s, logits, T, n_experts, topk, topk_ids, topk_w);
+  else if (per <= 8)
+    hipLaunchKernelGGL(moe_route_kernel<8>, grid, block, 0, s, logits, T, n_experts, topk, topk_ids, topk_w);
+  else
+    hipLaunchKernelGGL(moe_route_kernel<16>, grid, block, 0, s, logits, T, n_experts, topk, topk_ids, topk_w);
   return hipGetLastError();
 }
 
