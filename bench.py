@@ -323,6 +323,33 @@ def main():
         act = torch.empty(int(cnt.sum()), c.N, dtype=torch.bfloat16, device=dev)
         ms, _ = timed(lambda: tig.tig_silu_mul(GU, act), 50, 3)
         expert["silu_mul"] = {"us": ms * 1e3, "roofline": hbm_line(10.0 * act.numel(), ms)}
+        # The same rows and experts in block FP8 (per-token activations, 128 x 128
+        # weight blocks quantised once), and SiLU * up with its FP8 quantisation.
+        QXm, SXm = tig.fp8_quantize(Xm.reshape(c.experts * cap, c.K), 1)
+        QXc, SXc = tig.fp8_quantize(Xc, 1)
+        qws = [tig.fp8_quantize(We[e], 128) for e in range(c.experts)]
+        QWe, SWe = torch.stack([q for q, _ in qws]), torch.stack([x for _, x in qws])
+        del qws
+        wsf = torch.empty(tig.tig_expert_fp8_workspace_bytes(max(Mc, c.experts * cap), c.experts, c.N, c.K),
+                          dtype=torch.uint8, device=dev)
+        ms, _ = timed(lambda: tig.tig_expert_fp8_gemm_masked(QXm.reshape(c.experts, cap, c.K),
+                                                             SXm.reshape(c.experts, cap, c.K // 128), cntd, QWe, SWe,
+                                                             Ym, c.leaves, wsf), 20, 3)
+        f8 = flops / (ms / 1e3) / 1e12
+        expert["fp8_masked"] = {"ms": ms, "roofline": {"bound": "mfma", "achieved": f8, "peak": PEAK_FP8_TFLOPS,
+                                                       "unit": "TFLOP/s", "frac": f8 / PEAK_FP8_TFLOPS}}
+        ms, _ = timed(lambda: tig.tig_expert_fp8_gemm_contiguous(QXc, SXc, cntd, QWe, SWe, Yc, 128, c.leaves, wsf),
+                      20, 3)
+        f8 = flops / (ms / 1e3) / 1e12
+        expert["fp8_contiguous"] = {"ms": ms, "roofline": {"bound": "mfma", "achieved": f8, "peak": PEAK_FP8_TFLOPS,
+                                                           "unit": "TFLOP/s", "frac": f8 / PEAK_FP8_TFLOPS}}
+        QA8 = torch.empty(int(cnt.sum()), c.N, dtype=torch.uint8, device=dev)
+        SA8 = torch.empty(int(cnt.sum()), -(-c.N // 128), dtype=torch.uint8, device=dev)
+        ms, _ = timed(lambda: tig.tig_silu_mul_fp8(GU, QA8, SA8), 50, 3)
+        expert["silu_mul_fp8"] = {"us": ms * 1e3, "roofline": hbm_line(9.0 * QA8.numel(), ms)}
+        log(f"expert fp8 gemm masked {expert['fp8_masked']['ms'] * 1e3:.1f} us, contiguous "
+            f"{expert['fp8_contiguous']['ms'] * 1e3:.1f} us; silu_mul_fp8 {expert['silu_mul_fp8']['us']:.1f} us")
+        del QXm, SXm, QXc, SXc, QWe, SWe, wsf, QA8, SA8
         moe["expert"] = expert
         log(f"expert gemm masked {expert['masked']['ms'] * 1e3:.1f} us, contiguous "
             f"{expert['contiguous']['ms'] * 1e3:.1f} us; silu_mul {expert['silu_mul']['us']:.1f} us")

@@ -222,6 +222,46 @@ tig_status tig_silu_mul(const float* GU, int64_t ldgu, void* out, int64_t ldo, i
                         hipStream_t stream);
 
 /*
+ * The expert GEMM of the two layouts in block FP8 on the FP8 matrix cores,
+ * [BitRL, 4.4] (the experts' FP8 grouped GEMM; condition 1: the same FP8
+ * input in both layouts, rounded per element to nearest; condition 2: a
+ * layout-independent per-row result): the rows and layouts of
+ * tig_expert_gemm_masked / _contiguous, the contraction of tig_fp8_tree_gemm
+ * (so a row's result equals tig_fp8_tree_gemm on that row alone against its
+ * expert's W).
+ *   QX [rows, K] E4M3 and SX [rows, K/128] E8M0 (per row and 128 columns, as
+ *   tig_fp8_quantize with block_rows = 1 writes them); QW [n_experts, N, K]
+ *   and SW [n_experts, ceil(N/128), K/128] (each expert's W quantised in
+ *   128 x 128 blocks); Y [rows, N] FP32 or bf16, rows no expert owns not
+ *   written; workspace >= tig_expert_fp8_workspace_bytes(rows, n_experts, N,
+ *   K), 256-byte aligned (work items and the call's scale table).
+ * Implemented: n_experts <= 1024, K/leaves a multiple of 128, leaves <= 16.
+ */
+tig_status tig_expert_fp8_gemm_masked(const uint8_t* QX, const uint8_t* SX, const int32_t* counts, const uint8_t* QW,
+                                      const uint8_t* SW, void* Y, tig_out_dtype out_dtype, int32_t n_experts,
+                                      int64_t cap, int64_t N, int64_t K, int32_t leaves, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+tig_status tig_expert_fp8_gemm_contiguous(const uint8_t* QX, const uint8_t* SX, const int32_t* counts, int64_t align,
+                                          const uint8_t* QW, const uint8_t* SW, void* Y, tig_out_dtype out_dtype,
+                                          int32_t n_experts, int64_t M, int64_t N, int64_t K, int32_t leaves,
+                                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+tig_status tig_expert_fp8_workspace_bytes(int64_t rows, int32_t n_experts, int64_t N, int64_t K, size_t* bytes);
+
+/*
+ * The activation between the expert GEMMs and the FP8 input of the second,
+ * [BitRL, 4.4] condition 3: SiLU(gate) * up in FP32, rounded to bf16 once
+ * (exactly tig_silu_mul), then quantised to block FP8 in 1 x 128 blocks per
+ * row (exactly tig_fp8_quantize with block_rows = 1 on that bf16 result).
+ *   GU      float [rows, ldgu]: gate in columns 0 .. I-1, up in I .. 2I-1
+ *   Q       uint8 [rows, ldq] out: E4M3 bytes; scales uint8 [rows, ceil(I/128)]
+ *           out: E8M0 bytes
+ * Needs I, ldgu and ldq multiples of 4, GU 16-byte and Q 4-byte aligned
+ * (TIG_ERR_UNSUPPORTED otherwise).
+ */
+tig_status tig_silu_mul_fp8(const float* GU, int64_t ldgu, uint8_t* Q, int64_t ldq, uint8_t* scales, int64_t rows,
+                            int64_t I, hipStream_t stream);
+
+/*
  * Block FP8 quantisation, [BitRL, 4.1] (BF16 master weights quantised to block
  * FP8 by the deployment rule, W8A8) and [BitRL, 4.4] (per-element round to
  * nearest): OCP E4M3 values (largest 448) with one power-of-two scale 2^e per

@@ -23,10 +23,13 @@ __all__ = [
     "tig_moe_tree_gemm_combine", "tig_moe_workspace_bytes", "tig_moe_route", "tig_topk_positions",
     "tig_expert_gemm_masked", "tig_expert_gemm_contiguous", "tig_expert_workspace_bytes", "tig_silu_mul",
     "tig_fp8_quantize", "tig_fp8_tree_gemm", "tig_fp8_gemm_workspace_bytes", "tig_fp8_dequantize",
+    "tig_silu_mul_fp8", "tig_expert_fp8_gemm_masked", "tig_expert_fp8_gemm_contiguous",
+    "tig_expert_fp8_workspace_bytes",
     "tig_plan_describe",
     "tig_status_string", "tig_last_error",
     "tree_gemm", "logprob_gather", "moe_tree_gemm_combine", "moe_route", "topk_positions",
     "expert_gemm_masked", "expert_gemm_contiguous", "silu_mul", "fp8_quantize", "fp8_tree_gemm", "fp8_dequantize",
+    "silu_mul_fp8", "expert_fp8_gemm_masked", "expert_fp8_gemm_contiguous",
     "TIG_OK", "TIG_ERR_INVALID_ARG", "TIG_ERR_UNSUPPORTED", "TIG_ERR_WORKSPACE", "TIG_ERR_HIP",
     "TIG_OUT_F32", "TIG_OUT_BF16",
 ]
@@ -77,6 +80,12 @@ _SIGNATURES = {
     "tig_fp8_tree_gemm": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
     "tig_fp8_gemm_workspace_bytes": (_i32, [_i64, _i64, _i64, ctypes.POINTER(_sz)]),
     "tig_fp8_dequantize": (_i32, [_vp, _vp, _vp, _i64, _i64, _i32, _vp]),
+    "tig_silu_mul_fp8": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _vp]),
+    "tig_expert_fp8_gemm_masked": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i64, _i32, _vp, _sz,
+                                          _vp]),
+    "tig_expert_fp8_gemm_contiguous": (_i32, [_vp, _vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i64, _i64, _i64, _i32,
+                                              _vp, _sz, _vp]),
+    "tig_expert_fp8_workspace_bytes": (_i32, [_i64, _i32, _i64, _i64, ctypes.POINTER(_sz)]),
     "tig_plan_describe": (_i32, [_i64, _i32, ctypes.POINTER(_Plan)]),
     "tig_status_string": (ctypes.c_char_p, [_i32]),
     "tig_last_error": (ctypes.c_char_p, []),
@@ -339,6 +348,79 @@ def tig_silu_mul(GU, out, stream=None) -> None:
     _check(st, "tig_silu_mul")
 
 
+def tig_expert_fp8_workspace_bytes(rows: int, n_experts: int, N: int, K: int) -> int:
+    out = _sz(0)
+    _check(load().tig_expert_fp8_workspace_bytes(int(rows), int(n_experts), int(N), int(K), ctypes.byref(out)),
+           "tig_expert_fp8_workspace_bytes")
+    return int(out.value)
+
+
+def _expert_fp8_args(QX, SX, counts, QW, SW, Y):
+    torch = _torch()
+    for t, n in ((QX, "QX"), (SX, "SX"), (QW, "QW"), (SW, "SW")):
+        _need(t, n, torch.uint8, t.dim())
+        _contig(t, n)
+    _need(counts, "counts", torch.int32, 1)
+    if Y.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("Y must be float32 or bfloat16")
+    _same_device(QX, SX, counts, QW, SW, Y)
+    _contig(counts, "counts")
+    _contig(Y, "Y")
+    if QW.dim() != 3 or SW.dim() != 3:
+        raise ValueError("QW must be [E, N, K] and SW [E, ceil(N/128), K/128]")
+    E, N, K = QW.shape
+    if counts.shape[0] != E or tuple(SW.shape) != (E, -(-N // 128), -(-K // 128)):
+        raise ValueError("counts, QW and SW do not match")
+    if QX.shape[-1] != K or SX.shape[-1] != -(-K // 128) or Y.shape[-1] != N or QX.shape[:-1] != Y.shape[:-1] or \
+            SX.shape[:-1] != QX.shape[:-1]:
+        raise ValueError("QX, SX and Y do not match")
+    return E, N, K, (TIG_OUT_F32 if Y.dtype == torch.float32 else TIG_OUT_BF16)
+
+
+def tig_expert_fp8_gemm_masked(QX, SX, counts, QW, SW, Y, leaves: int, workspace, stream=None) -> None:
+    """Masked layout in block FP8: QX ``[E, cap, K]``, SX ``[E, cap, K/128]``, Y ``[E, cap, N]``."""
+    if QX.dim() != 3:
+        raise ValueError("QX must be [n_experts, cap, K]")
+    E, N, K, od = _expert_fp8_args(QX, SX, counts, QW, SW, Y)
+    st = load().tig_expert_fp8_gemm_masked(QX.data_ptr(), SX.data_ptr(), counts.data_ptr(), QW.data_ptr(),
+                                           SW.data_ptr(), Y.data_ptr(), od, E, QX.shape[1], N, K, int(leaves),
+                                           workspace.data_ptr(), workspace.numel(), _stream(stream))
+    _check(st, "tig_expert_fp8_gemm_masked")
+
+
+def tig_expert_fp8_gemm_contiguous(QX, SX, counts, QW, SW, Y, align: int, leaves: int, workspace,
+                                   stream=None) -> None:
+    """Contiguous layout in block FP8: QX ``[M, K]``, SX ``[M, K/128]``, Y ``[M, N]``."""
+    if QX.dim() != 2:
+        raise ValueError("QX must be [M, K]")
+    E, N, K, od = _expert_fp8_args(QX, SX, counts, QW, SW, Y)
+    st = load().tig_expert_fp8_gemm_contiguous(QX.data_ptr(), SX.data_ptr(), counts.data_ptr(), int(align),
+                                               QW.data_ptr(), SW.data_ptr(), Y.data_ptr(), od, E, QX.shape[0], N, K,
+                                               int(leaves), workspace.data_ptr(), workspace.numel(),
+                                               _stream(stream))
+    _check(st, "tig_expert_fp8_gemm_contiguous")
+
+
+def tig_silu_mul_fp8(GU, Q, scales, stream=None) -> None:
+    """``bf16(SiLU(g) u)`` (one rounding), then block FP8 in 1 x 128 blocks per row."""
+    torch = _torch()
+    _need(GU, "GU", torch.float32, 2)
+    _need(Q, "Q", torch.uint8, 2)
+    _need(scales, "scales", torch.uint8, 2)
+    _same_device(GU, Q, scales)
+    _rowmajor(GU, "GU")
+    _rowmajor(Q, "Q")
+    _contig(scales, "scales")
+    rows, I = Q.shape
+    if GU.shape[0] != rows or GU.shape[1] != 2 * I or tuple(scales.shape) != (rows, -(-I // 128)):
+        raise ValueError("GU must be [rows, 2 I], Q [rows, I] and scales [rows, ceil(I/128)]")
+    ldgu = GU.stride(0) if rows > 1 else 2 * I
+    ldq = Q.stride(0) if rows > 1 else I
+    st = load().tig_silu_mul_fp8(GU.data_ptr(), ldgu, Q.data_ptr(), ldq, scales.data_ptr(), rows, I,
+                                 _stream(stream))
+    _check(st, "tig_silu_mul_fp8")
+
+
 def tig_fp8_quantize(X, Q, scales, block_rows: int, stream=None) -> None:
     """Block FP8 (E4M3, power-of-two block scales as E8M0 bytes) of bf16 ``X [R, C]``."""
     torch = _torch()
@@ -553,3 +635,44 @@ def fp8_dequantize(Q, scales, block_rows: int, stream=None):
     out = torch.empty(Q.shape, dtype=torch.bfloat16, device=Q.device)
     tig_fp8_dequantize(Q, scales, out, block_rows, stream)
     return out
+
+
+def silu_mul_fp8(GU, stream=None):
+    """Allocate and return ``(Q, scales)`` of tig_silu_mul_fp8."""
+    torch = _torch()
+    rows, I = GU.shape[0], GU.shape[1] // 2
+    Q = torch.empty((rows, I), dtype=torch.uint8, device=GU.device)
+    S = torch.empty((rows, -(-I // 128)), dtype=torch.uint8, device=GU.device)
+    tig_silu_mul_fp8(GU, Q, S, stream)
+    return Q, S
+
+
+def _expert_fp8_ws(rows, E, N, K, device, workspace):
+    torch = _torch()
+    need = tig_expert_fp8_workspace_bytes(rows, E, N, K)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def expert_fp8_gemm_masked(QX, SX, counts, QW, SW, leaves: int, out_dtype=None, workspace=None, stream=None):
+    """Allocate and return Y ``[E, cap, N]`` of tig_expert_fp8_gemm_masked."""
+    torch = _torch()
+    E, cap, K = QX.shape
+    N = QW.shape[1]
+    Y = torch.empty((E, cap, N), dtype=out_dtype or torch.float32, device=QX.device)
+    tig_expert_fp8_gemm_masked(QX, SX, counts, QW, SW, Y, leaves,
+                               _expert_fp8_ws(E * cap, E, N, K, QX.device, workspace), stream)
+    return Y
+
+
+def expert_fp8_gemm_contiguous(QX, SX, counts, QW, SW, align: int, leaves: int, out_dtype=None, workspace=None,
+                               stream=None):
+    """Allocate and return Y ``[M, N]`` of tig_expert_fp8_gemm_contiguous."""
+    torch = _torch()
+    M, K = QX.shape
+    E, N = QW.shape[0], QW.shape[1]
+    Y = torch.empty((M, N), dtype=out_dtype or torch.float32, device=QX.device)
+    tig_expert_fp8_gemm_contiguous(QX, SX, counts, QW, SW, Y, align, leaves,
+                                   _expert_fp8_ws(M, E, N, K, QX.device, workspace), stream)
+    return Y

@@ -444,6 +444,90 @@ tig_status tig_fp8_tree_gemm(const uint8_t* QA, const uint8_t* SA, const uint8_t
   return ok();
 }
 
+tig_status tig_expert_fp8_workspace_bytes(int64_t rows, int32_t n_experts, int64_t N, int64_t K, size_t* bytes) {
+  if (!bytes) return fail(TIG_ERR_INVALID_ARG, "bytes is NULL");
+  if (rows < 0 || N < 0 || K < 0) return fail(TIG_ERR_INVALID_ARG, "rows, N and K must be >= 0");
+  if (n_experts < 1) return fail(TIG_ERR_INVALID_ARG, "n_experts must be >= 1");
+  if (n_experts > tig::kMaxGroupExperts)
+    return fail(TIG_ERR_UNSUPPORTED, "n_experts > %d not implemented", tig::kMaxGroupExperts);
+  *bytes = tig::fp8_group_ws(rows, n_experts, N, K).total;
+  return ok();
+}
+
+static tig_status expert_fp8_gemm(bool masked, const uint8_t* QX, const uint8_t* SX, const int32_t* counts,
+                                  const uint8_t* QW, const uint8_t* SW, void* Y, tig_out_dtype out_dtype,
+                                  int32_t n_experts, int64_t rows, int64_t cap, int64_t align, int64_t N, int64_t K,
+                                  int32_t leaves, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (rows < 0 || N < 0) return fail(TIG_ERR_INVALID_ARG, "row count and N must be >= 0");
+  size_t need = 0;
+  tig_status s = tig_expert_fp8_workspace_bytes(rows, n_experts, N, K, &need);
+  if (s != TIG_OK) return s;
+  if ((s = check_k_leaves(K, leaves)) != TIG_OK) return s;
+  if (K % (128 * int64_t(leaves)))
+    return fail(TIG_ERR_UNSUPPORTED, "K/leaves must be a multiple of 128 (one scale block per k-tile)");
+  if (out_dtype != TIG_OUT_F32 && out_dtype != TIG_OUT_BF16)
+    return fail(TIG_ERR_INVALID_ARG, "unknown out_dtype %d", int(out_dtype));
+  if (rows >= (int64_t(1) << 31) - 256) return fail(TIG_ERR_UNSUPPORTED, "too many rows");
+  if (rows == 0 || N == 0) return ok();
+  if (!QX || !SX || !counts || !QW || !SW || !Y)
+    return fail(TIG_ERR_INVALID_ARG, "QX, SX, counts, QW, SW and Y must not be NULL");
+  if (!aligned(QX, 16) || !aligned(QW, 16)) return fail(TIG_ERR_UNSUPPORTED, "QX and QW must be 16-byte aligned");
+  if (!aligned(counts, 4) || !aligned(Y, out_dtype == TIG_OUT_F32 ? 4 : 2))
+    return fail(TIG_ERR_INVALID_ARG, "counts or Y misaligned");
+  if ((s = check_span("X tile", 128, K / 2)) != TIG_OK) return s;
+  if ((s = check_span("W tile", tig::kBlockN, K / 2)) != TIG_OK) return s;
+  if (tig::group_max_items(rows, n_experts) * tig::cdiv(N, tig::kBlockN) >= (int64_t(1) << 31) - 8)
+    return fail(TIG_ERR_UNSUPPORTED, "too many output tiles");
+  if ((K / 128) * tig::fp8_group_table_width(rows, n_experts, N) >= (int64_t(1) << 32))
+    return fail(TIG_ERR_UNSUPPORTED, "scale table too large");
+  if (!workspace || workspace_bytes < need)
+    return fail(TIG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
+                workspace ? workspace_bytes : size_t(0));
+  if (!aligned(workspace, 256)) return fail(TIG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  const tig::Fp8GroupWs w = tig::fp8_group_ws(rows, n_experts, N, K);
+  tig::Fp8GroupLaunch p{QX, SX, counts, QW, SW, Y, out_dtype == TIG_OUT_F32 ? tig::kEpiF32 : tig::kEpiBF16, masked,
+                        rows, cap, align, N, K, n_experts, log2i(leaves), reinterpret_cast<int32_t*>(ws),
+                        reinterpret_cast<int32_t*>(ws + w.items), reinterpret_cast<uint8_t*>(ws + w.table)};
+  const hipError_t e = tig::launch_fp8_group_gemm(p, stream);
+  if (e != hipSuccess) return fail(TIG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+tig_status tig_expert_fp8_gemm_masked(const uint8_t* QX, const uint8_t* SX, const int32_t* counts, const uint8_t* QW,
+                                      const uint8_t* SW, void* Y, tig_out_dtype out_dtype, int32_t n_experts,
+                                      int64_t cap, int64_t N, int64_t K, int32_t leaves, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  if (cap < 0) return fail(TIG_ERR_INVALID_ARG, "cap must be >= 0");
+  if (n_experts >= 1 && cap > ((int64_t(1) << 31) - 256) / n_experts)
+    return fail(TIG_ERR_UNSUPPORTED, "n_experts * cap too large");
+  return expert_fp8_gemm(true, QX, SX, counts, QW, SW, Y, out_dtype, n_experts,
+                         int64_t(n_experts < 0 ? 0 : n_experts) * cap, cap, 1, N, K, leaves, workspace,
+                         workspace_bytes, stream);
+}
+
+tig_status tig_expert_fp8_gemm_contiguous(const uint8_t* QX, const uint8_t* SX, const int32_t* counts, int64_t align,
+                                          const uint8_t* QW, const uint8_t* SW, void* Y, tig_out_dtype out_dtype,
+                                          int32_t n_experts, int64_t M, int64_t N, int64_t K, int32_t leaves,
+                                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (align < 1 || align > (int64_t(1) << 20)) return fail(TIG_ERR_INVALID_ARG, "align must be in [1, 2^20]");
+  return expert_fp8_gemm(false, QX, SX, counts, QW, SW, Y, out_dtype, n_experts, M, 0, align, N, K, leaves,
+                         workspace, workspace_bytes, stream);
+}
+
+tig_status tig_silu_mul_fp8(const float* GU, int64_t ldgu, uint8_t* Q, int64_t ldq, uint8_t* scales, int64_t rows,
+                            int64_t I, hipStream_t stream) {
+  if (rows < 0 || I < 0) return fail(TIG_ERR_INVALID_ARG, "rows and I must be >= 0");
+  if (ldgu < 2 * I || ldq < I) return fail(TIG_ERR_INVALID_ARG, "ldgu must be >= 2 I and ldq >= I");
+  if (rows == 0 || I == 0) return ok();
+  if (!GU || !Q || !scales) return fail(TIG_ERR_INVALID_ARG, "GU, Q and scales must not be NULL");
+  if (I % 4 || ldgu % 4 || ldq % 4 || !aligned(GU, 16) || !aligned(Q, 4))
+    return fail(TIG_ERR_UNSUPPORTED, "needs I, ldgu, ldq multiples of 4, GU 16-byte and Q 4-byte aligned");
+  const hipError_t e = tig::launch_silu_mul_fp8(GU, ldgu, Q, ldq, scales, rows, I, stream);
+  if (e != hipSuccess) return fail(TIG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 tig_status tig_topk_positions(const float* scores, int64_t ld, const int32_t* lengths, int64_t R,
                               int32_t k, int32_t* out, hipStream_t stream) {
   if (R < 0 || ld < 0) return fail(TIG_ERR_INVALID_ARG, "R and ld must be >= 0");

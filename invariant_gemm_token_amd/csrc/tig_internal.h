@@ -165,6 +165,9 @@ hipError_t launch_fp8_quantize(const uint16_t* X, int64_t ldx, uint8_t* Q, int64
                                int64_t C, int block_rows, hipStream_t stream);
 hipError_t launch_fp8_dequant(const uint8_t* Q, const uint8_t* S, int64_t R, int64_t C, int block_rows,
                               uint16_t* out, hipStream_t stream);
+// SiLU(g) * u rounded to bf16 once, then quantised to block FP8 (1 x 128).
+hipError_t launch_silu_mul_fp8(const float* GU, int64_t ldgu, uint8_t* Q, int64_t ldq, uint8_t* S, int64_t R,
+                               int64_t I, hipStream_t stream);
 // W8A8 block-FP8 leaf-tree GEMM on the FP8 matrix cores.  table: workspace
 // for the per-call scale table [K/128][scw], scw = fp8_table_width(M, N).
 struct Fp8GemmLaunch {
@@ -181,6 +184,28 @@ inline size_t fp8_ws_bytes(int64_t M, int64_t N, int64_t K) {
   return align256(size_t(K / 128) * size_t(fp8_table_width(M, N)));
 }
 hipError_t launch_fp8_gemm(const Fp8GemmLaunch& p, hipStream_t stream);
+// The expert GEMM of the two layouts (as GroupLaunch) on the FP8 matrix cores:
+// QX [rows, K] E4M3 with SX [rows, K/128], QW [E, N, K] with SW [E, nb, K/128].
+struct Fp8GroupLaunch {
+  const uint8_t* QX; const uint8_t* SX; const int32_t* counts; const uint8_t* QW; const uint8_t* SW; void* Y;
+  int epi;
+  bool masked;
+  int64_t rows, cap, align, N, K;
+  int n_experts, leaves_log2;
+  int32_t* n_items; int32_t* items; uint8_t* table;   // workspace parts
+};
+inline int64_t fp8_group_table_width(int64_t rows, int n_experts, int64_t N) {
+  return (group_max_items(rows, n_experts) * 128 + int64_t(n_experts) * cdiv(N, 128) + 3) / 4 * 4;
+}
+struct Fp8GroupWs { size_t items, table, total; };
+inline Fp8GroupWs fp8_group_ws(int64_t rows, int n_experts, int64_t N, int64_t K) {
+  Fp8GroupWs w;
+  w.items = 256;
+  w.table = w.items + align256(size_t(group_max_items(rows, n_experts)) * 16);
+  w.total = w.table + align256(size_t(K / 128) * size_t(fp8_group_table_width(rows, n_experts, N)));
+  return w;
+}
+hipError_t launch_fp8_group_gemm(const Fp8GroupLaunch& p, hipStream_t stream);
 // out[r, i] = bf16(SiLU(g) * u) in FP32, g = GU[r, i], u = GU[r, I + i], one rounding.
 hipError_t launch_silu_mul(const float* GU, int64_t ldgu, uint16_t* out, int64_t ldo, int64_t rows, int64_t I,
                            hipStream_t stream);

@@ -676,6 +676,60 @@ struct LoaderF8 : Loader<2> {
   __device__ __forceinline__ void issue_all(char* stage, int kt) const {
     segs<0, GeoF8::VM_PER_STAGE>(stage, kt);
   }
+  // Byte of the tile's W scale in the dword the scale DMA brought.
+  __device__ __forceinline__ int wsel(int, int nt) const { return nt & 3; }
+};
+
+// The FP8 loader for expert work items (expert, first row, rows): A rows of
+// the item, W the expert's slice; the table's A part holds 128 entries per
+// item (item i's row scales from byte 128 i, dword-aligned), then E x nb W
+// scales (expert e, n-block nt at e nb + nt).
+struct F8GroupOperands {
+  const uint16_t* X; const uint16_t* W; const int4* items;   // E4M3 bytes as 16-bit words
+  const uint8_t* sc;
+  int64_t N, K, scw, apart, ksc, nb;
+};
+
+struct LoaderF8G : Loader<2> {
+  F8GroupOperands g;
+  __amdgpu_buffer_rsrc_t rsc;
+  uint32_t osc;
+  __device__ __forceinline__ int expert_of(int item) const {
+    return ((const CONST_AS int32_t*)g.items)[4 * item];
+  }
+  __device__ __forceinline__ void setup(int item, int nt) {
+    const CONST_AS int32_t* it = (const CONST_AS int32_t*)g.items + 4 * item;
+    const int e = it[0], row0 = it[1], rows = it[2];
+    this->op = DenseOperands{g.X + int64_t(row0) * (g.K / 2), g.K / 2, rows, g.W + int64_t(e) * g.N * (g.K / 2),
+                             g.K / 2, g.N};
+    Loader<2>::setup(0, nt);
+    const int lane = threadIdx.x & 63;
+    rsc = make_rsrc(g.sc, uint32_t(g.ksc * g.scw));
+    const int64_t w = int64_t(e) * g.nb + nt;
+    osc = lane < 32 ? uint32_t(int64_t(item) * 128 + 4 * lane)
+                    : (lane == 32 ? uint32_t(g.apart + (w & ~int64_t(3))) : OOB);
+  }
+  template <int J>
+  __device__ __forceinline__ void seg(char* stage, int kt) const {
+    if constexpr (J < GeoF8::A_SEG + 4) {
+      Loader<2>::template seg<J>(stage, kt);
+    } else {
+      const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsc, (LDS_AS void*)(stage + GeoF8::SC_OFF + wave * 256), 4, osc,
+                                               uint32_t(kt) * uint32_t(g.scw), 0, 0);
+    }
+  }
+  template <int J0, int D>
+  __device__ __forceinline__ void segs(char* stage, int kt) const {
+    if constexpr (D > 0) {
+      seg<J0>(stage, kt);
+      segs<J0 + 1, D - 1>(stage, kt);
+    }
+  }
+  __device__ __forceinline__ void issue_all(char* stage, int kt) const {
+    segs<0, GeoF8::VM_PER_STAGE>(stage, kt);
+  }
+  __device__ __forceinline__ int wsel(int item, int nt) const { return int((expert_of(item) * g.nb + nt) & 3); }
 };
 
 // Fragments of one k-step of 64: 32 bytes of a row per lane (two 16-byte
@@ -728,8 +782,8 @@ __device__ __forceinline__ void sched_step_f8() {
 // same ring discipline (constant DMA count per stage, the mid-stage wait and
 // barrier, the last k-tile re-issued past the end), two k-steps per stage,
 // fragments read one step ahead, the stage's scales read at its start.
-template <int LG, class Epi>
-__device__ __forceinline__ void leaf_tree_persistent_f8(LoaderF8& ld, int ktiles, const TileSched& ts, Epi& epi,
+template <int LG, class Ld, class Epi>
+__device__ __forceinline__ void leaf_tree_persistent_f8(Ld& ld, int ktiles, const TileSched& ts, Epi& epi,
                                                         char* smem) {
   using G = GeoF8;
   constexpr int STAGES = G::STAGES;
@@ -811,7 +865,7 @@ __device__ __forceinline__ void leaf_tree_persistent_f8(LoaderF8& ld, int ktiles
   for (int ti = 0; ti < n_my; ++ti) {
     int mt, nt;
     ts.coords(ti, mt, nt);
-    wsel = nt & 3;
+    wsel = ld.wsel(mt, nt);
     AccT<2> pend[LG > 0 ? LG : 1];
     AccT<2> cur;
 #pragma unroll 1
@@ -836,6 +890,32 @@ void fp8_tree_gemm_kernel(F8Operands f, void* __restrict__ C, int64_t ldc, int k
   ld.op = f.op;
   ld.f = f;
   leaf_tree_persistent_f8<LG>(ld, ktiles, ts, epi, smem);
+}
+
+// The scale table of an expert call: row kb = [128 entries per work item
+// (its rows' scales, 127 = 1 past them)][expert e's W scales at e nb + nt][127
+// up to scw].
+__global__ __launch_bounds__(256) void fp8_group_table_kernel(const int4* __restrict__ items,
+                                                              const int32_t* __restrict__ n_items,
+                                                              const uint8_t* __restrict__ SX,
+                                                              const uint8_t* __restrict__ SW, int64_t n_experts,
+                                                              int64_t nb, int64_t ksc, int64_t apart, int64_t scw,
+                                                              uint8_t* __restrict__ sc) {
+  const int64_t ni = *n_items;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < ksc * scw; i += int64_t(gridDim.x) * 256) {
+    const int64_t kb = i / scw, c = i % scw;
+    uint8_t v = 127;
+    if (c < apart) {
+      const int64_t item = c / 128, r = c % 128;
+      if (item < ni) {
+        const int4 it = items[item];
+        if (r < it.z) v = SX[(int64_t(it.y) + r) * ksc + kb];
+      }
+    } else if (c < apart + n_experts * nb) {
+      v = SW[(c - apart) * ksc + kb];
+    }
+    sc[i] = v;
+  }
 }
 
 // The scale table of one call: row kb = [the A rows' scales (127 = 1 past M)
@@ -1577,6 +1657,19 @@ void group_tile_kernel(GroupOperands g, const int32_t* __restrict__ n_items, int
   leaf_tree_persistent<LG, MI>(ld, ktiles, ts, epi, smem);
 }
 
+template <int LG, int EPI>
+__global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fp8_group_tile_kernel(F8GroupOperands f, void* __restrict__ Y, const int32_t* __restrict__ n_items, int n_nt) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  TileSched ts;
+  ts.init(*(const CONST_AS int32_t*)n_items, n_nt);
+  LoaderF8G ld;
+  ld.g = f;
+  const GroupOperands go{nullptr, nullptr, Y, f.items, f.N, f.K};
+  GroupStoreEpi<EPI, 2> epi{go};
+  leaf_tree_persistent_f8<LG>(ld, int(f.ksc), ts, epi, smem);
+}
+
 // SiLU(g) * u between the expert GEMMs [BitRL, 4.4, condition 3]: in FP32,
 // sigmoid(g) = 1 / (1 + t) for g >= 0 and t / (1 + t) below, t = e^-|g| by
 // the hardware exp2 (so that very negative g keep their tiny values), times g,
@@ -1796,6 +1889,44 @@ __global__ __launch_bounds__(256) void fp8_quant_blocks_kernel(const uint16_t* _
   if (t == 0) S[br * ngroups + g] = uint8_t(e + 127);
 }
 
+// The activation between the expert GEMMs, then its FP8 input to the second
+// [BitRL, 4.4, condition 3]: p = bf16(SiLU(g) u) (FP32, one rounding, as
+// silu_mul_kernel), then p quantised in 1 x 128 blocks (as
+// fp8_quant_rows4_kernel).  One workgroup per row; lane l of a wave holds
+// columns 4l .. 4l+3 of a pair of 128-column groups (I % 4 == 0).
+__global__ __launch_bounds__(256) void silu_mul_fp8_kernel(const float* __restrict__ GU, int64_t ldgu,
+                                                           uint8_t* __restrict__ Q, int64_t ldq,
+                                                           uint8_t* __restrict__ S, int64_t R, int64_t I) {
+  const int64_t ngroups = (I + 127) / 128, npairs = (ngroups + 1) / 2;
+  const int lane = threadIdx.x & 63;
+  for (int64_t r = blockIdx.y; r < R; r += gridDim.y)
+  for (int64_t gp = threadIdx.x >> 6; gp < npairs; gp += 4) {
+    const int64_t c0 = gp * 256 + 4 * lane;
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (c0 < I) {
+      const float4 g = *reinterpret_cast<const float4*>(GU + r * ldgu + c0);
+      const float4 u = *reinterpret_cast<const float4*>(GU + r * ldgu + I + c0);
+      v[0] = __builtin_bit_cast(float, uint32_t(f32_to_bf16_rne(silu_f32(g.x) * u.x)) << 16);
+      v[1] = __builtin_bit_cast(float, uint32_t(f32_to_bf16_rne(silu_f32(g.y) * u.y)) << 16);
+      v[2] = __builtin_bit_cast(float, uint32_t(f32_to_bf16_rne(silu_f32(g.z) * u.z)) << 16);
+      v[3] = __builtin_bit_cast(float, uint32_t(f32_to_bf16_rne(silu_f32(g.w) * u.w)) << 16);
+    }
+    float m = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(v[0]), __builtin_fabsf(v[1])),
+                              __builtin_fmaxf(__builtin_fabsf(v[2]), __builtin_fabsf(v[3])));
+#pragma unroll
+    for (int d = 1; d < 32; d *= 2) m = __builtin_fmaxf(m, __shfl_xor(m, d));
+    const int e = fp8_block_exponent(m);
+    if (c0 < I) {
+      uint32_t q = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q |= f32_to_e4m3_rne(__builtin_ldexpf(v[i], -e)) << (8 * i);
+      *reinterpret_cast<uint32_t*>(Q + r * ldq + c0) = q;
+    }
+    const int64_t g = 2 * gp + (lane >> 5);
+    if ((lane & 31) == 0 && g < ngroups) S[r * ngroups + g] = uint8_t(e + 127);
+  }
+}
+
 // Dequantise to bf16 (exact): out[r, c] = value(Q[r, c]) * 2^e of its block
 // (block_rows rows x 128 columns).  Thread: 8 consecutive columns.
 __global__ __launch_bounds__(256) void fp8_dequant_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ S,
@@ -1956,6 +2087,32 @@ template <int LG>
 hipError_t launch_group_lg(const GroupLaunch& p, hipStream_t s) {
   if constexpr (block_m_for_log2(LG) == 192) return launch_group_mi<LG, 3>(p, s);
   else return launch_group_mi<LG, 2>(p, s);
+}
+
+template <int LG>
+hipError_t launch_fp8_group_lg(const Fp8GroupLaunch& p, hipStream_t s) {
+  hipLaunchKernelGGL(group_plan_kernel, dim3(1), dim3(GROUP_PLAN_THREADS), 0, s, p.counts, p.n_experts, p.masked,
+                     p.cap, p.align, p.rows, GeoF8::BM, reinterpret_cast<int4*>(p.items), p.n_items);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t ksc = p.K / 128, nb = cdiv(p.N, 128);
+  const int64_t max_items = group_max_items(p.rows, p.n_experts);
+  const int64_t apart = max_items * 128, scw = fp8_group_table_width(p.rows, p.n_experts, p.N);
+  const int64_t cells = ksc * scw;
+  hipLaunchKernelGGL(fp8_group_table_kernel, dim3(unsigned(cdiv(cells, 256) < 4096 ? cdiv(cells, 256) : 4096)),
+                     dim3(256), 0, s, reinterpret_cast<const int4*>(p.items), p.n_items, p.SX, p.SW,
+                     int64_t(p.n_experts), nb, ksc, apart, scw, p.table);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int n_nt = int(nb);
+  const F8GroupOperands f{reinterpret_cast<const uint16_t*>(p.QX), reinterpret_cast<const uint16_t*>(p.QW),
+                          reinterpret_cast<const int4*>(p.items), p.table, p.N, p.K, scw, apart, ksc, nb};
+  const dim3 grid(persistent_grid(max_items * n_nt));
+  if (p.epi == kEpiF32)
+    hipLaunchKernelGGL((fp8_group_tile_kernel<LG, kEpiF32>), grid, dim3(NTHREADS), 0, s, f, p.Y, p.n_items, n_nt);
+  else
+    hipLaunchKernelGGL((fp8_group_tile_kernel<LG, kEpiBF16>), grid, dim3(NTHREADS), 0, s, f, p.Y, p.n_items, n_nt);
+  return hipGetLastError();
 }
 
 template <int LG>
@@ -2509,6 +2666,18 @@ hipError_t launch_fp8_quantize(const uint16_t* X, int64_t ldx, uint8_t* Q, int64
   return hipGetLastError();
 }
 
+hipError_t launch_fp8_group_gemm(const Fp8GroupLaunch& p, hipStream_t s) {
+  if (p.n_experts < 1 || p.n_experts > kMaxGroupExperts) return hipErrorInvalidValue;
+  switch (p.leaves_log2) {
+    case 0: return launch_fp8_group_lg<0>(p, s);
+    case 1: return launch_fp8_group_lg<1>(p, s);
+    case 2: return launch_fp8_group_lg<2>(p, s);
+    case 3: return launch_fp8_group_lg<3>(p, s);
+    case 4: return launch_fp8_group_lg<4>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_fp8_gemm(const Fp8GemmLaunch& p, hipStream_t s) {
   switch (p.leaves_log2) {
     case 0: return launch_fp8_lg<0>(p, s);
@@ -2518,6 +2687,16 @@ hipError_t launch_fp8_gemm(const Fp8GemmLaunch& p, hipStream_t s) {
     case 4: return launch_fp8_lg<4>(p, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_silu_mul_fp8(const float* GU, int64_t ldgu, uint8_t* Q, int64_t ldq, uint8_t* S, int64_t R,
+                               int64_t I, hipStream_t s) {
+  if (R <= 0 || I <= 0) return hipSuccess;
+  if (I % 4 || ldgu % 4 || ldq % 4 || (reinterpret_cast<uintptr_t>(GU) & 15) || (reinterpret_cast<uintptr_t>(Q) & 3))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(silu_mul_fp8_kernel, dim3(1u, unsigned(R < 65535 ? R : 65535)), dim3(256), 0, s, GU, ldgu, Q,
+                     ldq, S, R, I);
+  return hipGetLastError();
 }
 
 hipError_t launch_fp8_dequant(const uint8_t* Q, const uint8_t* S, int64_t R, int64_t C, int block_rows,

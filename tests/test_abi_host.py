@@ -206,6 +206,25 @@ def test_fp8_arguments_rejected():
     assert lib.tig_fp8_dequantize(None, None, None, 4, 128, 2, None) == tig.TIG_ERR_INVALID_ARG
 
 
+def test_expert_fp8_and_silu_fp8_arguments_rejected():
+    lib = _raw()
+    n = None
+    # K/leaves not a whole number of 128-wide scale blocks; NULL pointers; nothing to do
+    assert lib.tig_expert_fp8_gemm_masked(n, n, n, n, n, n, 0, 4, 16, 128, 512, 8, n, 0, n) == tig.TIG_ERR_UNSUPPORTED
+    assert lib.tig_expert_fp8_gemm_masked(n, n, n, n, n, n, 0, 4, 16, 128, 1024, 8, n, 0, n) == \
+        tig.TIG_ERR_INVALID_ARG
+    assert lib.tig_expert_fp8_gemm_masked(n, n, n, n, n, n, 0, 4, 0, 128, 1024, 8, n, 0, n) == tig.TIG_OK
+    assert lib.tig_expert_fp8_gemm_contiguous(n, n, n, 0, n, n, n, 0, 4, 64, 128, 1024, 8, n, 0, n) == \
+        tig.TIG_ERR_INVALID_ARG                                                           # align 0
+    assert lib.tig_expert_fp8_gemm_masked(n, n, n, n, n, n, 0, 1025, 4, 128, 1024, 8, n, 0, n) == \
+        tig.TIG_ERR_UNSUPPORTED
+    # 1000 rows, 4 experts, N = 300, K = 1024: 12 items -> 256 + 256 + 8 rows of 1548 bytes (-> 12544)
+    assert tig.tig_expert_fp8_workspace_bytes(1000, 4, 300, 1024) == 256 + 256 + 12544
+    assert lib.tig_silu_mul_fp8(n, 16, n, 8, n, 4, 8, n) == tig.TIG_ERR_INVALID_ARG        # NULL
+    assert lib.tig_silu_mul_fp8(n, 12, n, 6, n, 4, 6, n) == tig.TIG_ERR_INVALID_ARG        # NULL before the
+    assert lib.tig_silu_mul_fp8(n, 16, n, 8, n, 0, 8, n) == tig.TIG_OK
+
+
 def test_null_pointers_rejected():
     lib = _raw()
     assert lib.tig_tree_gemm(None, 512, None, 512, None, 64, 0, 4, 64, 512, 8, None) == tig.TIG_ERR_INVALID_ARG
