@@ -26,12 +26,11 @@ inline int block_m_for(int64_t M, int leaves_log2) {
 // The logprob path also takes 192-row tiles at 16 leaves: it keeps the left
 // half of the leaf tree (the root of leaves 0..7) in global scratch instead
 // of registers while the right half streams (see kSpillGrid).
-// tig_tree_gemm: 64-row tiles when 128-row tiles would occupy fewer than half
-// of the 256 CUs (small grids are latency-bound per tile), else block_m_for.
-inline int tree_gemm_block_m(int64_t M, int64_t N, int leaves_log2) {
-  if (((M + 127) / 128) * ((N + 127) / 128) < 128) return 64;   // 128: the n-tile width
-  return block_m_for(M, leaves_log2);
-}
+// tig_tree_gemm's tile height: 64, 128 or (up to 8 leaves) 192 rows, whichever
+// lets the busiest workgroup of the persistent grid finish first: the number
+// of tiles it runs under the schedule's deal over this device's CUs, times the
+// measured time of one tile of that height relative to a 128-row tile.
+int tree_gemm_block_m(int64_t M, int64_t N, int leaves_log2);
 inline int logprob_block_m_for(int64_t M, int leaves_log2) {
   (void)leaves_log2;
   return (M + 191) / 192 < (M + 127) / 128 ? 192 : 128;

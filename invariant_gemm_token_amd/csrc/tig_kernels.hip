@@ -1943,9 +1943,8 @@ __global__ __launch_bounds__(256) void fp8_dequant_kernel(const uint8_t* __restr
   }
 }
 
-// Persistent grid: one workgroup per CU (multiple of 8 for the XCD deal), or
-// one per tile when there are fewer tiles.  Only the schedule depends on it.
-int persistent_grid(int64_t n_tiles) {
+// Compute units of the current device (cached per device).
+int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -1955,9 +1954,43 @@ int persistent_grid(int64_t n_tiles) {
       n = 256;
     cus[dev] = n;
   }
-  const int64_t full = int64_t(cus[dev] / 8) * 8 > 0 ? int64_t(cus[dev] / 8) * 8 : 8;
+  return cus[dev];
+}
+
+// Persistent grid: one workgroup per CU (multiple of 8 for the XCD deal), or
+// one per tile when there are fewer tiles.  Only the schedule depends on it.
+int persistent_grid(int64_t n_tiles) {
+  const int cus = device_cus();
+  const int64_t full = int64_t(cus / 8) * 8 > 0 ? int64_t(cus / 8) * 8 : 8;
   const int64_t want = ((n_tiles + 7) / 8) * 8;
   return int(want < full ? want : full);
+}
+
+// Tiles the busiest workgroup runs: TileSched's deal of n_mt x n_nt tiles over
+// a persistent grid (n-slices per XCD with at least 4 groups of n-tiles, else
+// an even split of the logical order), slots workgroups per XCD.
+int64_t busiest_tiles(int64_t n_mt, int64_t n_nt) {
+  const int64_t slots = persistent_grid(n_mt * n_nt) / 8;
+  const int64_t per_xcd = n_nt >= 4 * GROUP_N ? cdiv(n_nt, 8) * n_mt : cdiv(n_mt * n_nt, 8);
+  return cdiv(per_xcd, slots);
+}
+
+int choose_tree_gemm_block_m(int64_t M, int64_t N, int leaves_log2) {
+  // Time of one tile relative to a 128-row tile (x100), from event timings of
+  // 4096-deep contractions at 8 leaves: rows 64 / 128 / 192 -> 70 / 100 / 138.
+  const int heights[3] = {64, 128, 192}, cost[3] = {70, 100, 138};
+  const int n_h = block_m_for_log2(leaves_log2) == 192 ? 3 : 2;
+  const int64_t n_nt = cdiv(N, BN);
+  int best = 64;
+  int64_t best_t = -1;
+  for (int i = 0; i < n_h; ++i) {
+    const int64_t t = busiest_tiles(cdiv(M, heights[i]), n_nt) * cost[i];
+    if (best_t < 0 || t < best_t) {
+      best_t = t;
+      best = heights[i];
+    }
+  }
+  return best;
 }
 
 template <int LG, int MI>
@@ -1978,9 +2011,10 @@ hipError_t launch_tree_gemm_mi(const TreeGemmLaunch& p, hipStream_t s) {
 
 template <int LG>
 hipError_t launch_tree_gemm_lg(const TreeGemmLaunch& p, hipStream_t s) {
-  if (tree_gemm_block_m(p.M, p.N, LG) == 64) return launch_tree_gemm_mi<LG, 1>(p, s);
+  const int bm = tree_gemm_block_m(p.M, p.N, LG);
+  if (bm == 64) return launch_tree_gemm_mi<LG, 1>(p, s);
   if constexpr (block_m_for_log2(LG) == 192) {
-    if (block_m_for(p.M, LG) == 192) return launch_tree_gemm_mi<LG, 3>(p, s);
+    if (bm == 192) return launch_tree_gemm_mi<LG, 3>(p, s);
   }
   return launch_tree_gemm_mi<LG, 2>(p, s);
 }
@@ -2137,6 +2171,10 @@ hipError_t launch_fp8_lg(const Fp8GemmLaunch& p, hipStream_t s) {
 }
 
 }  // namespace
+
+int tree_gemm_block_m(int64_t M, int64_t N, int leaves_log2) {
+  return choose_tree_gemm_block_m(M, N, leaves_log2);
+}
 
 hipError_t launch_tree_gemm(const TreeGemmLaunch& p, hipStream_t s) {
   switch (p.leaves_log2) {

@@ -1,8 +1,8 @@
 """Schedule freedom on the GPU: tile height, leaf visiting order, sampled-logit pass.
 
 The dense kernels use 192-row tiles where that needs fewer tiles than 128-row
-ones (and 128 rows otherwise; tree_gemm also 64 rows when 128-row tiles would
-fill fewer than 128 CUs, and always 128 at 16 leaves, while the logprob
+ones (and 128 rows otherwise; tree_gemm takes 64, 128 or 192 rows, whichever
+lets its busiest workgroup finish first, and at most 128 at 16 leaves, while the logprob
 path then keeps the left half of each tile's leaf tree in scratch and adds it
 to the right half's root at the end), and a workgroup that runs several tiles
 visits the leaves of every other tile last to first.  Only the schedule may
@@ -27,16 +27,31 @@ from gpu_util import assert_bitwise, dev_bf16, say
 pytestmark = pytest.mark.gpu
 
 
+def _busiest(n_mt, n_nt, cus):
+    """Tiles of the busiest workgroup under the persistent deal (one workgroup
+    per CU in groups of 8 XCDs; n-slices per XCD from 32 n-tiles up)."""
+    tiles = n_mt * n_nt
+    slots = min(-(-tiles // 8) * 8, max(cus // 8 * 8, 8)) // 8
+    per_xcd = -(-n_nt // 8) * n_mt if n_nt >= 32 else -(-tiles // 8)
+    return -(-per_xcd // slots)
+
+
 def _block_m(M, L, logprob=False, N=None):
-    if not logprob and -(-M // 128) * -(-N // 128) < 128:
-        return 64                                   # tree_gemm on small grids
-    tall = 192 if L <= 8 or logprob else 128
-    return 192 if tall == 192 and -(-M // 192) < -(-M // 128) else 128
+    if logprob:
+        return 192 if -(-M // 192) < -(-M // 128) else 128
+    # tree_gemm: the height whose busiest workgroup finishes first, by the
+    # relative tile times 70 / 100 / 138 of 64 / 128 / 192 rows.
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    heights = (64, 128, 192) if L <= 8 else (64, 128)
+    cost = {64: 70, 128: 100, 192: 138}
+    return min(heights, key=lambda h: _busiest(-(-M // h), -(-N // 128), cus) * cost[h])
 
 
-# (start, stop) slices of a 577-row batch: 128-row tiles (M <= 128, M = 256)
-# and 192-row tiles (129, 177, 577) at different row offsets.
-SLICES = [(0, 1), (0, 128), (100, 229), (400, 577), (33, 289), (0, 577)]
+# (start, stop) slices of a 577-row batch at different row offsets.  logprob:
+# 128-row tiles for M <= 128 and M = 256, 192-row tiles for 129, 177, 512 and
+# 577 rows; tree_gemm over 64 n-tiles: 64-row tiles up to 256 rows, 128-row
+# tiles for 512 rows, 192 rows for 577 up to 8 leaves (128 at 16).
+SLICES = [(0, 1), (0, 128), (100, 229), (400, 577), (33, 289), (40, 552), (0, 577)]
 
 
 @pytest.mark.parametrize("L", [1, 8, 16])
@@ -59,10 +74,9 @@ def test_logprob_rows_identical_across_tile_heights(gpu_lib, L):
 
 @pytest.mark.parametrize("L", [2, 8, 16])
 def test_tree_gemm_rows_identical_across_tile_heights(gpu_lib, L):
-    """64 columns of n-tiles: a slice of 128 rows or fewer runs on 64-row tiles
-    (fewer than 128 tiles of 128 rows), longer slices on 128- or 192-row tiles;
-    the last columns (N = 8187) leave a ragged n-tile; a narrow W (300 columns)
-    puts the whole batch on 64-row tiles."""
+    """64 columns of n-tiles: the slices run on 64-, 128- and 192-row tiles
+    (only 64 and 128 at 16 leaves); the last columns (N = 8187) leave a ragged
+    n-tile; a narrow W (300 columns) puts the whole batch on 64-row tiles."""
     K, N, M = 1024, 8187, 577
     rng = np.random.default_rng(777 + L)
     A = dev_bf16(wl.normal_bf16(rng, (M, K), 1.0))
