@@ -337,7 +337,7 @@ typedef struct {
   int32_t version;     /* policy version */
   int32_t leaves;      /* L */
   int32_t leaf_len;    /* K / L */
-  int32_t block_m;     /* rows of the dense kernels' tallest tile (192; 128 at 16 leaves); 128-row tiles are used where they need no more tiles */
+  int32_t block_m;     /* rows of the dense kernels' tallest tile (192; 128 at 16 leaves); shorter tiles (128, and 64 in tig_tree_gemm) are a per-call schedule choice that never changes a bit */
   int32_t block_n;     /* columns per workgroup tile = vocabulary tile width */
   int32_t block_k;     /* k columns staged per LDS step (does not change bits) */
   int32_t mfma_m, mfma_n, mfma_k; /* 32, 32, 16 */
