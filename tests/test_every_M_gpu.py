@@ -1,0 +1,79 @@
+"""GPU: every batch size gives every row the same bits.
+
+[BitRL, section 2 and 4.1]: one accumulation order for every M, so a row's
+result may not depend on how many rows share its call.  The linear layer
+(4096 x 4096, 8 leaves) is called with every M from 1 to 4097 rows, each
+result compared bit for bit with the first M rows of the 4097-row call; the
+calls cover every tile height the schedule picks (64, 128 and 192 rows), every
+ragged last m-tile and grids from one workgroup to several tiles per
+workgroup.  The fused logprob is swept the same way over M = 1 .. 600 at a
+smaller LM head (K = 1024, V = 5000, 8 leaves): single row-of-tiles calls up
+to 128 rows, 128- and 192-row tiles above.  Comparisons run on the device.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_util import dev_bf16, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _first_mismatch(a: torch.Tensor, b: torch.Tensor):
+    ne = (a.view(torch.int32) != b.view(torch.int32))
+    if not bool(ne.any()):
+        return None
+    return tuple(int(i) for i in ne.nonzero()[0])
+
+
+def test_linear_every_M_1_to_4097(gpu_lib):
+    cfg = wl.CONFIGS["linear"]
+    s = wl.streams(cfg.seed)
+    Mmax = 4097
+    A = dev_bf16(wl.normal_bf16(s["H"], (Mmax, cfg.K), 1.0))
+    W = dev_bf16(wl.normal_bf16(s["W"], (cfg.N, cfg.K), 0.02))
+    full = torch.empty(Mmax, cfg.N, dtype=torch.float32, device="cuda:0")
+    gpu_lib.tig_tree_gemm(A, W, full, cfg.leaves)
+    out = torch.empty_like(full)
+    bad = []
+    for M in range(1, Mmax + 1):
+        if M % 512 == 1:
+            say(f"linear every M: M = {M} ..")
+        C = out[:M]
+        gpu_lib.tig_tree_gemm(A[:M], W, C, cfg.leaves)
+        where = _first_mismatch(C, full[:M])
+        if where is not None:
+            bad.append((M, where))
+            if len(bad) >= 5:
+                break
+    torch.cuda.synchronize()
+    assert not bad, f"rows differ from the 4097-row call at (M, (row, col)): {bad}"
+
+
+def test_logprob_every_M_1_to_600(gpu_lib):
+    K, V, L, Mmax = 1024, 5000, 8, 600
+    rng = np.random.default_rng(20241)
+    H = dev_bf16(wl.normal_bf16(rng, (Mmax, K), 1.0))
+    W = dev_bf16(wl.normal_bf16(rng, (V, K), 0.03))
+    ids = torch.from_numpy(rng.integers(0, V, size=Mmax)).to("cuda:0")
+    ws = torch.empty(gpu_lib.tig_logprob_workspace_bytes(Mmax, K, V, L), dtype=torch.uint8, device="cuda:0")
+    full_lp = torch.empty(Mmax, dtype=torch.float32, device="cuda:0")
+    full_lse = torch.empty_like(full_lp)
+    gpu_lib.tig_logprob_gather(H, W, ids, full_lp, full_lse, L, ws)
+    lp = torch.empty_like(full_lp)
+    lse = torch.empty_like(full_lp)
+    bad = []
+    for M in range(1, Mmax + 1):
+        if M % 100 == 1:
+            say(f"logprob every M: M = {M} ..")
+        gpu_lib.tig_logprob_gather(H[:M], W, ids[:M], lp[:M], lse[:M], L, ws)
+        for name, got, ref in (("logprob", lp[:M], full_lp[:M]), ("lse", lse[:M], full_lse[:M])):
+            where = _first_mismatch(got, ref)
+            if where is not None:
+                bad.append((name, M, where))
+        if len(bad) >= 5:
+            break
+    torch.cuda.synchronize()
+    assert not bad, f"rows differ from the 600-row call: {bad}"
