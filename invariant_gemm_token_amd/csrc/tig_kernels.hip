@@ -1067,18 +1067,29 @@ __device__ __forceinline__ void LogprobEpi<MI, SPLIT>::operator()(AccT<MI>& acc,
   lds_sync();   // the partner's slots are read before the buffer is refilled
 }
 
+__device__ __forceinline__ void pick_item(const uint16_t* __restrict__ H, const uint16_t* __restrict__ W,
+                                          const int64_t* __restrict__ ids, float* __restrict__ xleaf,
+                                          int64_t M, int64_t K, int64_t V, int group, int leaf, int leaves);
+
 // SPLIT (16 leaves with 192-row tiles): the left half of the tree waits in
 // `scratch` instead of registers.
 template <int LG, int MI, int WAUX, bool SPLIT>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void logprob_tile_kernel(DenseOperands op, int ktiles, int n_mt, int n_nt, float2* __restrict__ part,
-                         float* __restrict__ scratch) {
+                         float* __restrict__ scratch, const int64_t* __restrict__ ids, float* __restrict__ xleaf,
+                         int n_pick) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   TileSched ts;
   ts.init(n_mt, n_nt);
   LogprobEpi<MI, SPLIT> epi{part, op.M, op.N, n_nt, scratch};
   Loader<MI, WAUX> ld{op};
   leaf_tree_persistent<LG, MI>(ld, ktiles, ts, epi, smem);
+  // With one row of tiles the last round of tiles leaves workgroups idle: the
+  // highest-numbered ones, which run the fewest tiles, also run the n_pick
+  // items of the sampled-logit pass (one per wave; none when n_pick is 0).
+  const int j = (int(gridDim.x) - 1 - int(blockIdx.x)) * (NTHREADS / 64) + int(threadIdx.x >> 6);
+  if (j < n_pick)
+    pick_item(op.A, op.W, ids, xleaf, op.M, int64_t(ktiles) * BK, op.N, j >> LG, j & ((1 << LG) - 1), 1 << LG);
 }
 
 // ---------------------------------------------------------------------------
@@ -1094,13 +1105,14 @@ void logprob_tile_kernel(DenseOperands op, int ktiles, int n_mt, int n_nt, float
 // ---------------------------------------------------------------------------
 constexpr int PICK_U = 32;   // k-steps loaded at once (a whole leaf of 512)
 
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void logprob_pick_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ W,
-                         const int64_t* __restrict__ ids, float* __restrict__ xleaf, int64_t M,
-                         int64_t K, int64_t V) {
-  const int lane = threadIdx.x, leaf = blockIdx.y, leaves = gridDim.y;
+// One work item of the sampled-logit pass, run by one wave: rows
+// 32 group .. 32 group + 31 and one leaf.
+__device__ __forceinline__ void pick_item(const uint16_t* __restrict__ H, const uint16_t* __restrict__ W,
+                                          const int64_t* __restrict__ ids, float* __restrict__ xleaf,
+                                          int64_t M, int64_t K, int64_t V, int group, int leaf, int leaves) {
+  const int lane = threadIdx.x & 63;
   const int i = lane & 31, half = lane >> 5;
-  const int64_t row0 = int64_t(blockIdx.x) * 32;
+  const int64_t row0 = int64_t(group) * 32;
   const int64_t row = row0 + i < M ? row0 + i : M - 1;
   int64_t id = ids[row];
   if (id < 0 || id >= V) id = 0;
@@ -1130,6 +1142,13 @@ void logprob_pick_kernel(const uint16_t* __restrict__ H, const uint16_t* __restr
       if (v == vsel) d = c[v];
     xleaf[(row0 + i) * leaves + leaf] = d;
   }
+}
+
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void logprob_pick_kernel(const uint16_t* __restrict__ H, const uint16_t* __restrict__ W,
+                         const int64_t* __restrict__ ids, float* __restrict__ xleaf, int64_t M,
+                         int64_t K, int64_t V) {
+  pick_item(H, W, ids, xleaf, M, K, V, int(blockIdx.x), int(blockIdx.y), int(gridDim.y));
 }
 
 // ---------------------------------------------------------------------------
@@ -2025,11 +2044,6 @@ hipError_t launch_logprob_mi(const LogprobLaunch& p, hipStream_t s) {
   const DenseOperands op{static_cast<const uint16_t*>(p.H), p.K, p.M,
                          static_cast<const uint16_t*>(p.W), p.K, p.V};
   float2* part = static_cast<float2*>(p.partials);
-  hipLaunchKernelGGL(logprob_pick_kernel, dim3(unsigned(cdiv(p.M, 32)), 1u << LG), dim3(64), 0, s,
-                     static_cast<const uint16_t*>(p.H), static_cast<const uint16_t*>(p.W), p.ids,
-                     p.xleaf, p.M, p.K, p.V);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
   // One row of tiles (decode-sized batches): each W tile is read once, so its
   // loads bypass the caches' retention (non-temporal).  The split tree's
   // scratch holds kSpillGrid workgroups.
@@ -2037,13 +2051,24 @@ hipError_t launch_logprob_mi(const LogprobLaunch& p, hipStream_t s) {
   int grid = persistent_grid(int64_t(n_mt) * n_vt);
   if (SPLIT && grid > kSpillGrid) grid = kSpillGrid;
   if (SPLIT && !p.spill) return hipErrorInvalidValue;
+  // The sampled-logit pass: inside the tile kernel's last round when there is
+  // one row of tiles and a wave of the grid for each item, else its own kernel.
+  const int64_t items = cdiv(p.M, 32) << LG;
+  const int n_pick = n_mt == 1 && items <= int64_t(grid) * (NTHREADS / 64) ? int(items) : 0;
+  if (n_pick == 0) {
+    hipLaunchKernelGGL(logprob_pick_kernel, dim3(unsigned(cdiv(p.M, 32)), 1u << LG), dim3(64), 0, s,
+                       static_cast<const uint16_t*>(p.H), static_cast<const uint16_t*>(p.W), p.ids,
+                       p.xleaf, p.M, p.K, p.V);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (n_mt == 1)
     hipLaunchKernelGGL((logprob_tile_kernel<LG, MI, 2, SPLIT>), dim3(grid), dim3(NTHREADS), 0, s, op,
-                       int(p.K / BK), n_mt, n_vt, part, p.spill);
+                       int(p.K / BK), n_mt, n_vt, part, p.spill, p.ids, p.xleaf, n_pick);
   else
     hipLaunchKernelGGL((logprob_tile_kernel<LG, MI, 0, SPLIT>), dim3(grid), dim3(NTHREADS), 0, s, op,
-                       int(p.K / BK), n_mt, n_vt, part, p.spill);
-  err = hipGetLastError();
+                       int(p.K / BK), n_mt, n_vt, part, p.spill, p.ids, p.xleaf, 0);
+  hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   int q = 0;
   while ((256 << q) < n_vt) ++q;
