@@ -1087,9 +1087,16 @@ void logprob_tile_kernel(DenseOperands op, int ktiles, int n_mt, int n_nt, float
   // With one row of tiles the last round of tiles leaves workgroups idle: the
   // highest-numbered ones, which run the fewest tiles, also run the n_pick
   // items of the sampled-logit pass (one per wave; none when n_pick is 0).
-  const int j = (int(gridDim.x) - 1 - int(blockIdx.x)) * (NTHREADS / 64) + int(threadIdx.x >> 6);
-  if (j < n_pick)
-    pick_item(op.A, op.W, ids, xleaf, op.M, int64_t(ktiles) * BK, op.N, j >> LG, j & ((1 << LG) - 1), 1 << LG);
+  // (Compiled into the single-row instances only: WAUX == 2.)
+  if constexpr (WAUX == 2) {
+    const int j = (int(gridDim.x) - 1 - int(blockIdx.x)) * (NTHREADS / 64) + int(threadIdx.x >> 6);
+    if (j < n_pick)
+      pick_item(op.A, op.W, ids, xleaf, op.M, int64_t(ktiles) * BK, op.N, j >> LG, j & ((1 << LG) - 1), 1 << LG);
+  } else {
+    (void)ids;
+    (void)xleaf;
+    (void)n_pick;
+  }
 }
 
 // ---------------------------------------------------------------------------
