@@ -82,7 +82,9 @@ typedef enum { TIG_OUT_F32 = 0, TIG_OUT_BF16 = 1 } tig_out_dtype;
  *   C     [M, N], row stride ldc (elements, >= N); FP32 tree output, or that
  *         value rounded once to bf16 (nearest even) when out_dtype is BF16
  *   leaves  power of two in [1, 64]; K % leaves == 0
- * Implemented: leaves <= 16 and K/leaves a multiple of 64 (else UNSUPPORTED).
+ * Implemented: leaves <= 16 and K/leaves a multiple of 64; A and W 16-byte
+ * aligned with row strides a multiple of 8; 192 rows of A (128 at 16 leaves)
+ * and 128 rows of W each spanning less than 2 GiB (else UNSUPPORTED).
  * M == 0 or N == 0 is TIG_OK and launches nothing.  C must not overlap A or W.
  */
 tig_status tig_tree_gemm(const void* A, int64_t lda, const void* W, int64_t ldw,

@@ -197,7 +197,8 @@ tig_status tig_tree_gemm(const void* A, int64_t lda, const void* W, int64_t ldw,
     return fail(TIG_ERR_UNSUPPORTED, "A and W must be 16-byte aligned with row strides a multiple of 8");
   if (!aligned(C, out_dtype == TIG_OUT_F32 ? 4 : 2))
     return fail(TIG_ERR_INVALID_ARG, "C is misaligned for its dtype");
-  const int bm = tig::tree_gemm_block_m(M, N, log2i(leaves));
+  // The tallest tile bounds the span, whatever height this call runs on.
+  const int bm = tig::block_m_for_log2(log2i(leaves));
   if ((s = check_span("A tile", bm, lda)) != TIG_OK) return s;
   if ((s = check_span("W tile", tig::kBlockN, ldw)) != TIG_OK) return s;
   if (tig::cdiv(M, bm) * tig::cdiv(N, tig::kBlockN) >= (int64_t(1) << 31) - 8)

@@ -247,6 +247,12 @@ def test_alignment_and_workspace_errors_with_fake_pointers():
     # misaligned A, odd row stride
     assert lib.tig_tree_gemm(F + 2, 512, F, 512, F, 64, 0, 4, 64, 512, 8, None) == tig.TIG_ERR_UNSUPPORTED
     assert lib.tig_tree_gemm(F, 516, F, 512, F, 64, 0, 4, 64, 512, 8, None) == tig.TIG_ERR_UNSUPPORTED
+    # 192 rows of A spanning 2 GiB: rejected at every M, whatever tile height the call would run on
+    big = (1 << 31) // (192 * 2) // 8 * 8 + 8
+    for M in (1, 100, 5000):
+        assert lib.tig_tree_gemm(F, big, F, 512, F, 64, 0, M, 64, 512, 8, None) == tig.TIG_ERR_UNSUPPORTED
+    assert lib.tig_tree_gemm(F, 512, F, (1 << 31) // 256 // 8 * 8 + 8, F, 64, 0, 4, 64, 512, 8,
+                             None) == tig.TIG_ERR_UNSUPPORTED
     # workspace missing / too small / misaligned
     need = tig.tig_logprob_workspace_bytes(4, 512, 64, 8)
     assert lib.tig_logprob_gather(F, F, F, F, None, 4, 512, 64, 8, None, 0, None) == tig.TIG_ERR_WORKSPACE
