@@ -81,6 +81,33 @@ def test_equal_logits_closed_form(gpu_lib, V):
     assert np.max(np.abs(lse.cpu().double().numpy() - (X + math.log(V)))) < 1e-5
 
 
+@pytest.mark.parametrize("V,M", [(151936, 100), (151936, 300), (4097, 130), (129, 64)])
+def test_one_distinct_logit_closed_form(gpu_lib, V, M):
+    """One vocabulary row gives logit a, every other row 0: logprob = a - ln(e^a + V - 1)
+    for the sampled id of that row and -ln(e^a + V - 1) for any other (a closed form,
+    independent of the oracle), through the single-row-of-tiles path (M <= 128) and
+    the multi-row one, with the distinct row in a middle tile and ids on both sides."""
+    K, L = 1024, 8
+    rng = np.random.default_rng(V + M)
+    j = V // 2 + 3 if V > 8 else 0
+    H = np.zeros((M, K), dtype=np.float32)
+    Wf = np.zeros((V, K), dtype=np.float32)
+    a_vals = np.array([0.5, 1.0, 2.0, 3.0, 5.5, 7.25, -1.5, 0.0])   # a = h * w, exact in bf16 and FP32
+    h = a_vals[np.arange(M) % len(a_vals)]
+    H[:, 17] = h                       # row m: logit a_m at column j, 0 elsewhere
+    Wf[j, 17] = 1.0
+    ids = np.where(np.arange(M) % 2 == 0, j, rng.integers(0, V, size=M))
+    lp, lse = gpu_lib.logprob_gather(dev_bf16(wl.f32_to_bf16_bits(H)), dev_bf16(wl.f32_to_bf16_bits(Wf)),
+                                     torch.from_numpy(ids).cuda(), L)
+    lp = lp.cpu().double().numpy()
+    lse = lse.cpu().double().numpy()
+    exp_lse = np.log(np.exp(h) + (V - 1))
+    exp_lp = np.where(ids == j, h, 0.0) - exp_lse
+    say(f"one distinct logit V={V} M={M}: max |dlogprob| {np.max(np.abs(lp - exp_lp)):.2e}")
+    assert np.max(np.abs(lse - exp_lse)) < 1e-5
+    assert np.max(np.abs(lp - exp_lp)) < 1e-5
+
+
 def test_vocab_of_one(gpu_lib):
     """V = 1: lse is the single logit bit for bit and the logprob is exactly 0."""
     rng = np.random.default_rng(1)
