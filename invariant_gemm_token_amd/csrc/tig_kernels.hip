@@ -1196,9 +1196,30 @@ __global__ __launch_bounds__(256) void logprob_combine_kernel(
   const int c = 1 << q;
   const int t0 = tid * c;
 
+  // Thread 0's operands of the final step, loaded while the tiles are reduced.
+  float x[16];
+  int64_t id = 0;
+  if (tid == 0) {
+    id = ids[row];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) x[j] = j < leaves ? xleaf[row * leaves + j] : 0.0f;
+  }
+  // Up to 8 tiles per thread (vocabularies up to 262144) stay in registers
+  // between the max and the sum; more are read again.
+  constexpr int CACHE = 8;
+  float2 v[CACHE];
+#pragma unroll
+  for (int i = 0; i < CACHE; ++i) v[i] = i < c && t0 + i < n_vt ? pr[t0 + i] : make_float2(-__builtin_inff(), 0.0f);
+
   float g = -__builtin_inff();
-  for (int i = 0; i < c; ++i)
-    if (t0 + i < n_vt) g = fmaxf(g, pr[t0 + i].x);
+  if (c <= CACHE) {
+#pragma unroll
+    for (int i = 0; i < CACHE; ++i)
+      if (i < c && t0 + i < n_vt) g = fmaxf(g, v[i].x);
+  } else {
+    for (int i = 0; i < c; ++i)
+      if (t0 + i < n_vt) g = fmaxf(g, pr[t0 + i].x);
+  }
 #pragma unroll
   for (int m = 1; m < 64; m *= 2) g = fmaxf(g, __shfl_xor(g, m));
   if (lane == 0) red[wave] = g;
@@ -1208,14 +1229,26 @@ __global__ __launch_bounds__(256) void logprob_combine_kernel(
 
   float pend[MAX_Q];
   float cur = 0.0f;
-  for (int i = 0; i < c; ++i) {
-    float term = 0.0f;
-    if (t0 + i < n_vt) {
-      const float2 p = pr[t0 + i];
-      term = p.y * __builtin_amdgcn_exp2f((p.x - g) * LOG2E);
+  if (c <= CACHE) {
+#pragma unroll
+    for (int i = 0; i < CACHE; ++i) {
+      if (i < c) {
+        float term = 0.0f;
+        if (t0 + i < n_vt) term = v[i].y * __builtin_amdgcn_exp2f((v[i].x - g) * LOG2E);
+        cur = term;
+        scalar_fold<0>(pend, cur, i, q);
+      }
     }
-    cur = term;
-    scalar_fold<0>(pend, cur, i, q);
+  } else {
+    for (int i = 0; i < c; ++i) {
+      float term = 0.0f;
+      if (t0 + i < n_vt) {
+        const float2 p = pr[t0 + i];
+        term = p.y * __builtin_amdgcn_exp2f((p.x - g) * LOG2E);
+      }
+      cur = term;
+      scalar_fold<0>(pend, cur, i, q);
+    }
   }
   float S = cur;
 #pragma unroll
@@ -1228,15 +1261,11 @@ __global__ __launch_bounds__(256) void logprob_combine_kernel(
   if (tid == 0) {
     S = (red[0] + red[1]) + (red[2] + red[3]);
     const float l = g + __builtin_amdgcn_logf(S) * LN2;
-    float x[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) x[j] = j < leaves ? xleaf[row * leaves + j] : 0.0f;
 #pragma unroll
     for (int w = 1; w < 16; w *= 2)
 #pragma unroll
       for (int j = 0; j + w < 16; j += 2 * w)
         if (j + w < leaves) x[j] = x[j] + x[j + w];
-    const int64_t id = ids[row];
     const bool ok = id >= 0 && id < V;
     logprob[row] = ok ? x[0] - l : __builtin_nanf("");
     if (lse) lse[row] = l;
