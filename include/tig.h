@@ -124,6 +124,29 @@ tig_status tig_logprob_workspace_bytes(int64_t M, int64_t K, int64_t n_vocab,
                                        int32_t leaves, size_t* bytes);
 
 /*
+ * tig_logprob_gather with no workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation).  The same kernels, so the same bits, as
+ * tig_logprob_gather on the same arguments.  The intermediate data lives in a
+ * fixed device array of TIG_NOALLOC_SCRATCH_BYTES that the library holds on
+ * every GPU it runs on until the process ends; its address is looked up once
+ * per device, on the first call there.  No call allocates or frees memory.
+ *   Limit: calls whose tig_logprob_workspace_bytes() exceeds
+ *   TIG_NOALLOC_SCRATCH_BYTES return TIG_ERR_UNSUPPORTED (for a 151936-token
+ *   vocabulary at 8 leaves: more than about 3500 rows).
+ *   Every call on one GPU uses that GPU's one array: calls that may overlap on
+ *   a GPU (other streams, other host threads) race, and the caller must order
+ *   them.  Nothing in the array has to start at zero; it keeps the last call's
+ *   contents.
+ * Other arguments, limits and errors: as tig_logprob_gather.
+ */
+#define TIG_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+tig_status tig_logprob_gather_noalloc(const void* H, const void* W, const int64_t* ids,
+                                      float* logprob_out, float* lse_out,
+                                      int64_t M, int64_t K, int64_t n_vocab, int32_t leaves,
+                                      hipStream_t stream);
+
+/*
  * MoE-shaped contraction with a fixed-order FP32 combine.
  * [BitRL, 4.4] per-row expert result independent of layout; [BitRL, 4.5] and
  * [IsoExec, Parallelism-invariant kernels] expert outputs combined in a fixed

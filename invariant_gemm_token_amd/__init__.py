@@ -19,7 +19,7 @@ import os
 
 __all__ = [
     "TigError", "load", "lib_path",
-    "tig_tree_gemm", "tig_logprob_gather", "tig_logprob_workspace_bytes",
+    "tig_tree_gemm", "tig_logprob_gather", "tig_logprob_workspace_bytes", "tig_logprob_gather_noalloc",
     "tig_moe_tree_gemm_combine", "tig_moe_workspace_bytes", "tig_moe_route", "tig_topk_positions",
     "tig_expert_gemm_masked", "tig_expert_gemm_contiguous", "tig_expert_workspace_bytes", "tig_silu_mul",
     "tig_fp8_quantize", "tig_fp8_tree_gemm", "tig_fp8_gemm_workspace_bytes", "tig_fp8_dequantize",
@@ -66,6 +66,7 @@ _SIGNATURES = {
     "tig_tree_gemm": (_i32, [_vp, _i64, _vp, _i64, _vp, _i64, _i32, _i64, _i64, _i64, _i32, _vp]),
     "tig_logprob_gather": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
     "tig_logprob_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, ctypes.POINTER(_sz)]),
+    "tig_logprob_gather_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i32, _vp]),
     "tig_moe_tree_gemm_combine": (_i32, [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _i64, _i64, _i64,
                                          _i32, _vp, _sz, _vp]),
     "tig_moe_workspace_bytes": (_i32, [_i64, _i64, _i64, _i32, _i32, ctypes.POINTER(_sz)]),
@@ -225,6 +226,31 @@ def tig_logprob_gather(H, W, ids, logprob_out, lse_out, leaves: int, workspace, 
                                    int(leaves), workspace.data_ptr(), workspace.numel(),
                                    _stream(stream))
     _check(st, "tig_logprob_gather")
+
+
+def tig_logprob_gather_noalloc(H, W, ids, logprob_out, lse_out, leaves: int, stream=None) -> None:
+    """tig_logprob_gather on the library's fixed device array instead of a workspace; see include/tig.h."""
+    torch = _torch()
+    _need(H, "H", torch.bfloat16, 2)
+    _need(W, "W", torch.bfloat16, 2)
+    _need(ids, "ids", torch.int64, 1)
+    _need(logprob_out, "logprob_out", torch.float32, 1)
+    if lse_out is not None:
+        _need(lse_out, "lse_out", torch.float32, 1)
+    _same_device(H, W, ids, logprob_out, lse_out)
+    for t, n in ((H, "H"), (W, "W"), (ids, "ids"), (logprob_out, "logprob_out")):
+        _contig(t, n)
+    if lse_out is not None:
+        _contig(lse_out, "lse_out")
+    M, K = H.shape
+    V = W.shape[0]
+    if W.shape[1] != K or ids.shape[0] != M or logprob_out.shape[0] != M or (
+            lse_out is not None and lse_out.shape[0] != M):
+        raise ValueError("shapes do not match")
+    st = load().tig_logprob_gather_noalloc(H.data_ptr(), W.data_ptr(), ids.data_ptr(), logprob_out.data_ptr(),
+                                           lse_out.data_ptr() if lse_out is not None else None, M, K, V,
+                                           int(leaves), _stream(stream))
+    _check(st, "tig_logprob_gather_noalloc")
 
 
 def tig_moe_workspace_bytes(T: int, N: int, K: int, n_experts: int, topk: int) -> int:

@@ -258,6 +258,28 @@ tig_status tig_logprob_gather(const void* H, const void* W, const int64_t* ids, 
   return ok();
 }
 
+static_assert(tig::kNoAllocScratchBytes == TIG_NOALLOC_SCRATCH_BYTES, "tig.h and the device array disagree");
+
+tig_status tig_logprob_gather_noalloc(const void* H, const void* W, const int64_t* ids,
+                                      float* logprob_out, float* lse_out, int64_t M, int64_t K,
+                                      int64_t n_vocab, int32_t leaves, hipStream_t stream) {
+  size_t need = 0;
+  tig_status s = tig_logprob_workspace_bytes(M, K, n_vocab, leaves, &need);
+  if (s != TIG_OK) return s;
+  if (M == 0) return ok();
+  if (need > tig::kNoAllocScratchBytes)
+    return fail(TIG_ERR_UNSUPPORTED,
+                "tig_logprob_gather_noalloc: %lld rows need %zu bytes of intermediate data, above its fixed "
+                "%zu-byte device array; call tig_logprob_gather with a workspace",
+                (long long)M, need, tig::kNoAllocScratchBytes);
+  void* ws = nullptr;
+  const hipError_t e = tig::noalloc_scratch(&ws);
+  if (e != hipSuccess)
+    return fail(TIG_ERR_HIP, "tig_logprob_gather_noalloc: device array lookup failed: %s", hipGetErrorString(e));
+  return tig_logprob_gather(H, W, ids, logprob_out, lse_out, M, K, n_vocab, leaves, ws,
+                            tig::kNoAllocScratchBytes, stream);
+}
+
 tig_status tig_moe_workspace_bytes(int64_t T, int64_t N, int64_t K, int32_t n_experts,
                                    int32_t topk, size_t* bytes) {
   if (!bytes) return fail(TIG_ERR_INVALID_ARG, "bytes is NULL");

@@ -40,6 +40,11 @@ inline int logprob_block_m_for(int64_t M, int leaves_log2) {
 constexpr int kSpillGrid = 256;
 constexpr size_t kSpillBytesPerGroup = 256 * 96 * 4;
 constexpr int kBlockN = 128;   // also the vocabulary tile of the log-softmax
+// Device array behind tig_logprob_gather_noalloc (callers that cannot allocate):
+// one copy on every GPU the library runs on, held until the process ends.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+// Its address on the current device, looked up once per device.
+hipError_t noalloc_scratch(void** ptr);
 constexpr int kBlockK = 64;
 constexpr int kMfmaM = 32, kMfmaN = 32, kMfmaK = 16;
 constexpr int kMaxLeavesLog2 = 4;  // leaves <= 16 implemented

@@ -20,11 +20,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "tig_internal.h"
 
 #pragma clang fp contract(off)
+
+// Intermediate data of tig_logprob_gather_noalloc, for callers that cannot
+// allocate device memory: kNoAllocScratchBytes on every GPU the library runs
+// on, for the life of the process, shared by every such call on that GPU.
+static __device__ __align__(256) char scratch[tig::kNoAllocScratchBytes];
 
 namespace tig {
 namespace {
@@ -460,7 +466,7 @@ __device__ __forceinline__ void leaf_tree_persistent(Ld& ld, int ktiles, const T
 
   // With Epi::kSplitTop the top level of the tree is not held in registers:
   // each half of the positions is folded on its own, the first half's root
-  // goes to the epilogue's scratch (epi.spill) and the epilogue adds it to
+  // goes to the epilogue's spill area (epi.spill) and the epilogue adds it to
   // the second half's root, the same last addition of the same tree.
   constexpr bool SPLIT = Epi::kSplitTop && LG > 0;
   constexpr int PLG = SPLIT ? LG - 1 : LG;   // tree levels held in registers
@@ -504,13 +510,13 @@ struct LogprobEpi {
   static_assert(64 * BN * 4 <= Geo<MI>::STAGE, "the transpose pass must fit one ring buffer");
   static constexpr bool kSplitTop = SPLIT;
   float2* part; int64_t M, V; int n_vt;
-  float* scratch;   // SPLIT: this launch's spill area, kSpillBytesPerGroup bytes per workgroup
+  float* spill_base;   // SPLIT: this launch's spill area, kSpillBytesPerGroup bytes per workgroup
   __device__ __forceinline__ void operator()(AccT<MI>& acc, int mt, int nt, char* region) const;
   // The left half's root waits in the workgroup's area in the accumulator
   // layout: 16-byte chunk q of block (i, j) of thread t at byte
   // (((i 2 + j) 4 + q) 256 + t) 16.
   __device__ __forceinline__ float* area() const {
-    return scratch + size_t(blockIdx.x) * (kSpillBytesPerGroup / 4);
+    return spill_base + size_t(blockIdx.x) * (kSpillBytesPerGroup / 4);
   }
   // One VGPR of lane offset for all 24 stores, the chunk offset in soffset
   // (always inside the area).
@@ -1072,16 +1078,16 @@ __device__ __forceinline__ void pick_item(const uint16_t* __restrict__ H, const 
                                           int64_t M, int64_t K, int64_t V, int group, int leaf, int leaves);
 
 // SPLIT (16 leaves with 192-row tiles): the left half of the tree waits in
-// `scratch` instead of registers.
+// `spill_base` instead of registers.
 template <int LG, int MI, int WAUX, bool SPLIT>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void logprob_tile_kernel(DenseOperands op, int ktiles, int n_mt, int n_nt, float2* __restrict__ part,
-                         float* __restrict__ scratch, const int64_t* __restrict__ ids, float* __restrict__ xleaf,
+                         float* __restrict__ spill_base, const int64_t* __restrict__ ids, float* __restrict__ xleaf,
                          int n_pick) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   TileSched ts;
   ts.init(n_mt, n_nt);
-  LogprobEpi<MI, SPLIT> epi{part, op.M, op.N, n_nt, scratch};
+  LogprobEpi<MI, SPLIT> epi{part, op.M, op.N, n_nt, spill_base};
   Loader<MI, WAUX> ld{op};
   leaf_tree_persistent<LG, MI>(ld, ktiles, ts, epi, smem);
   // With one row of tiles the last round of tiles leaves workgroups idle: the
@@ -2246,6 +2252,30 @@ hipError_t launch_tree_gemm(const TreeGemmLaunch& p, hipStream_t s) {
     case 4: return launch_tree_gemm_lg<4>(p, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+// The no-allocation entry point's intermediate data (tile partials, picked
+// logit leaves and, at 16 leaves on 192-row tiles, the parked half trees) lives
+// in the file-scope array `scratch`.  Host code never passes the array's name
+// to a kernel (in host code it is only a stand-in for the symbol): the first
+// call on a device looks up that device's copy with hipGetSymbolAddress, with
+// the device current, and every later call on it reuses that address.
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static void* addr[kMaxDevices];
+  static hipError_t status[kMaxDevices];
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev] {
+    status[dev] = hipGetSymbolAddress(&addr[dev], HIP_SYMBOL(scratch));
+    if (status[dev] == hipSuccess && addr[dev] == nullptr) status[dev] = hipErrorInvalidSymbol;
+  });
+  if (status[dev] != hipSuccess) return status[dev];
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_logprob(const LogprobLaunch& p, hipStream_t s) {

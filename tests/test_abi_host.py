@@ -126,6 +126,24 @@ def test_zero_rows_is_a_noop_even_with_null_pointers():
     assert lib.tig_topk_positions(None, 65536, None, 0, 2048, None, None) == tig.TIG_OK
 
 
+def test_noalloc_logprob_limits_checked_before_any_device_call():
+    lib = _raw()
+    # M == 0: no-op even with NULL pointers; the device array is not looked up
+    assert lib.tig_logprob_gather_noalloc(None, None, None, None, None, 0, 4096, 151936, 8, None) == tig.TIG_OK
+    # argument errors as tig_logprob_gather
+    assert lib.tig_logprob_gather_noalloc(None, None, None, None, None, -1, 4096, 151936, 8, None) == \
+        tig.TIG_ERR_INVALID_ARG
+    assert lib.tig_logprob_gather_noalloc(None, None, None, None, None, 4, 4096, 151936, 3, None) == \
+        tig.TIG_ERR_INVALID_ARG
+    # above the fixed array: rejected with a message naming the limit
+    need = tig.tig_logprob_workspace_bytes(4000, 4096, 151936, 8)
+    assert need > 32 << 20
+    assert lib.tig_logprob_gather_noalloc(None, None, None, None, None, 4000, 4096, 151936, 8, None) == \
+        tig.TIG_ERR_UNSUPPORTED
+    assert "device array" in tig.tig_last_error()
+    assert tig.tig_logprob_workspace_bytes(3000, 4096, 151936, 8) <= 32 << 20
+
+
 def test_route_arguments_rejected_before_any_launch():
     lib = _raw()
     # topk outside [1, n_experts]
