@@ -22,6 +22,7 @@
 
 #include <mutex>
 #include <type_traits>
+#include <utility>
 
 #include "tig_internal.h"
 
@@ -324,7 +325,33 @@ struct FragAddr {
     f.b0 = *reinterpret_cast<const bf16x8*>(st + w0 + ch);
     f.b1 = *reinterpret_cast<const bf16x8*>(st + w1 + ch);
   }
+  // Fragment IDX of k-step s alone: A block IDX (IDX < MI), else W block IDX - MI.
+  template <int IDX>
+  __device__ __forceinline__ void read_one(Frags<MI>& f, const char* st, int s) const {
+    const uint32_t ch = uint32_t(((2 * s + fk) ^ ((fr >> 1) & 7)) << 4);
+    if constexpr (IDX < MI)
+      f.a[IDX] = *reinterpret_cast<const bf16x8*>(st + a0 + IDX * 32 * 128 + ch);
+    else if constexpr (IDX == MI)
+      f.b0 = *reinterpret_cast<const bf16x8*>(st + w0 + ch);
+    else
+      f.b1 = *reinterpret_cast<const bf16x8*>(st + w1 + ch);
+  }
 };
+
+// f(integral_constant<int, K>) for K = 0 .. N-1, in order.
+template <class F, int... K>
+__device__ __forceinline__ void for_each_index(std::integer_sequence<int, K...>, F&& f) {
+  (f(std::integral_constant<int, K>{}), ...);
+}
+
+// The k-step's fragment set by index (compile time).
+template <int S, class T>
+__device__ __forceinline__ T& pick4(T& f0, T& f1, T& f2, T& f3) {
+  if constexpr (S == 0) return f0;
+  else if constexpr (S == 1) return f1;
+  else if constexpr (S == 2) return f2;
+  else return f3;
+}
 
 // One k-step of 16 on the wave tile.  The first k-step of a leaf takes the
 // constant +0 as accumulator input.
@@ -431,34 +458,67 @@ __device__ __forceinline__ void leaf_tree_persistent(Ld& ld, int ktiles, const T
   fa.read(F0, smem, 0);
   fa.read(F1, smem, 1);
 
-  // DMA instructions per k-step: the stage's VM_PER_STAGE spread over its 4 steps.
+  // One stage is 8 MI MFMAs (4 k-steps of 2 MI), issued one per section in a
+  // fixed order; hard scheduling fences between sections pin the other
+  // instructions of the stage beside them, so the matrix core gets a new
+  // instruction every section instead of waiting behind clumps of LDS reads
+  // and DMA issues:
+  //   first half  (k-steps 0, 1): the reads of this stage's k-steps 2 and 3,
+  //               spread over its first sections, and half of the stage's DMA;
+  //   mid-stage:  wait for the DMA of stage q+1 and for this wave's reads of
+  //               stage q, then the barrier: stage q+1 has landed everywhere
+  //               and stage q's buffer is no longer read;
+  //   second half (k-steps 2, 3): the reads of the next stage's k-steps 0 and
+  //               1 and the rest of the DMA.
+  // The reads of a half stop four MFMAs before its end, so that they have
+  // returned when the mid-stage wait or the next stage's first MFMA needs them.
   constexpr int VM = G::VM_PER_STAGE;
-  constexpr int D0 = VM / 4, D1 = VM / 2 - VM / 4, D2 = (3 * VM) / 4 - VM / 2, D3 = VM - (3 * VM) / 4;
+  constexpr int NM = 8 * MI, HALF = NM / 2, NR = MI + 2;
+  constexpr int RSPAN = HALF - 4 > HALF / 2 ? HALF - 4 : HALF / 2;
+  constexpr int DH1 = VM / 2, DH2 = VM - VM / 2;
   // vmcnt once stage q+1 has landed, at the mid-stage wait of stage q: the
-  // later stages q+2 .. q+STAGES-2 and this stage's first D0 + D1 instructions.
-  constexpr int MID_WAIT = VM * (STAGES - 3) + D0 + D1;
+  // later stages q+2 .. q+STAGES-2 and this stage's first DH1 instructions.
+  constexpr int MID_WAIT = VM * (STAGES - 3) + DH1;
   auto stage = [&](AccT<MI>& cur, auto first) {
     const char* st = smem + off_q;
     char* pb = smem + off_pf;
     const uint32_t off_n = off_q + G::STAGE == RING ? 0u : off_q + uint32_t(G::STAGE);
-    fa.read(F2, st, 2);
-    mfma_step<decltype(first)::value>(cur, F0);
-    ld.template segs<0, D0>(pb, kt);
-    sched_step<MI, D0>();
-    fa.read(F3, st, 3);
-    mfma_step<false>(cur, F1);
-    ld.template segs<D0, D1>(pb, kt);
-    sched_step<MI, D1>();
-    wait_vmcnt_lgkm0<MID_WAIT>();   // stage q+1 landed; this wave's reads of stage q returned
-    bar();                          // every wave is done with stage q's buffer
-    fa.read(F0, smem + off_n, 0);
-    mfma_step<false>(cur, F2);
-    ld.template segs<D0 + D1, D2>(pb, kt);
-    sched_step<MI, D2>();
-    fa.read(F1, smem + off_n, 1);
-    mfma_step<false>(cur, F3);
-    ld.template segs<D0 + D1 + D2, D3>(pb, kt);
-    sched_step<MI, D3>();
+    const char* sn = smem + off_n;
+    for_each_index(std::make_integer_sequence<int, NM>{}, [&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      constexpr int ks = k / (2 * MI), t = k % (2 * MI), i = t >> 1, j = t & 1;
+      constexpr bool second = k >= HALF;
+      constexpr int hk = second ? k - HALF : k;
+      {
+        const Frags<MI>& F = pick4<ks>(F0, F1, F2, F3);
+        const f32x16 z = {};
+        cur.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F.a[i], j ? F.b1 : F.b0,
+                                                              (decltype(first)::value && ks == 0) ? z : cur.c[i][j],
+                                                              0, 0, 0);
+      }
+      // LDS reads of this section: read r of the half goes to section r RSPAN / (2 NR).
+      for_each_index(std::make_integer_sequence<int, 2 * NR>{}, [&](auto rc) {
+        constexpr int r = decltype(rc)::value;
+        if constexpr ((r * RSPAN) / (2 * NR) == hk) {
+          constexpr int step = second ? r / NR : 2 + r / NR;   // this stage's 2, 3 / the next one's 0, 1
+          Frags<MI>& D = pick4<step>(F0, F1, F2, F3);
+          fa.template read_one<r % NR>(D, second ? sn : st, step);
+        }
+      });
+      // DMA of this section: instruction d of a half goes to section (2 d + 1) HALF / (2 D).
+      for_each_index(std::make_integer_sequence<int, (DH1 > DH2 ? DH1 : DH2)>{}, [&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        if constexpr (!second && d < DH1 && ((2 * d + 1) * HALF) / (2 * DH1) == hk)
+          ld.template seg<d>(pb, kt);
+        if constexpr (second && d < DH2 && ((2 * d + 1) * HALF) / (2 * DH2) == hk)
+          ld.template seg<DH1 + d>(pb, kt);
+      });
+      if constexpr (k == HALF - 1) {
+        wait_vmcnt_lgkm0<MID_WAIT>();   // stage q+1 landed; this wave's reads of stage q returned
+        bar();                          // every wave is done with stage q's buffer
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
     advance();
     off_pf = off_q;
     off_q = off_n;
