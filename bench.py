@@ -11,7 +11,11 @@ line carries:
   size; achieved = 2 M K V flops per call / the event-timed duration of one
   call, against the bf16 dense peak; traffic = HBM-side bytes per launch from
   the committed counter summary, when it was taken on this kernel source;
-* tree_gemm: the same contraction rate as TFLOP/s and fraction of the peak;
+* tree_gemm: the leaf-tree contraction entry point alone at the same shape
+  (8192 x 4096 x 151936, 8 leaves; FP32 and bf16 output), TFLOP/s and
+  fraction of the peak;
+* clock: the GFX clock and board power sampled while the prefill runs in a
+  loop, and the matrix-core peak at that clock (256 CUs x 4096 flop/clock);
 * decode: one 128-row decode step of the same LM head (bound by streaming the
   1.245 GB weight from HBM), tokens/s and fraction of 8 TB/s;
 * linear, moe, large: the other workloads of the path, each with its own
@@ -20,7 +24,8 @@ line carries:
   tokens, matrix cores), and the hidden-7168 / vocabulary-129280 LM head at
   16 leaves (16384-row prefill: matrix cores; 256-row decode: both);
 * cpu_baseline: the fp64 CPU oracle timed on a bounded sample of rows of the
-  headline workload, on this host's cores (skipped with --no-cpu-baseline).
+  headline workload, on this host's cores, plus the same oracle on every other
+  workload (rows/s and fp64 GFLOP/s; skipped with --no-cpu-baseline).
 
 Inputs are seeded and synthetic (workloads: bf16 N(0,1) activations,
 N(0,0.02) weights, uniform sampled ids, top-8 routing of N(0,1) router
@@ -87,7 +92,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=8192)
+    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--cpu-rows-large", type=int, default=256)
     ap.add_argument("--no-extra", action="store_true", help="skip the linear / moe / large lines")
     ap.add_argument("--phase", choices=("all", "prefill", "decode"), default="all",
                     help="time only one LM-head configuration (for per-kernel profiles)")
@@ -143,6 +149,45 @@ def main():
         gbs = nbytes / (ms / 1e3) / 1e9
         return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS}
 
+    def sample_clock(fn, seconds):
+        """Run fn in a loop for about `seconds` while sampling the GFX clocks and board power."""
+        import subprocess
+        import threading
+        samples, stop = [], [False]
+
+        def poll():
+            while not stop[0]:
+                try:
+                    r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                                       timeout=10)
+                    d = json.loads(r.stdout)
+                    g = (d["gpu_data"] if isinstance(d, dict) else d)[0]
+                    clk = [v["clk"]["value"] for k, v in g["clock"].items()
+                           if k.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict)
+                           and isinstance(v["clk"].get("value"), (int, float))]
+                    pw = g["power"]["socket_power"]["value"]
+                    if clk and isinstance(pw, (int, float)):
+                        samples.append((float(np.mean(clk)), float(pw)))
+                except Exception:
+                    pass
+                time.sleep(0.2)
+
+        th = threading.Thread(target=poll)
+        th.start()
+        t0 = time.time()
+        while time.time() - t0 < seconds:
+            fn()
+            torch.cuda.synchronize()
+        stop[0] = True
+        th.join()
+        # drop the first samples (clock still ramping)
+        use = samples[2:] if len(samples) > 4 else samples
+        if not use:
+            return None
+        mhz = float(np.median([c for c, _ in use]))
+        return {"gfx_mhz_median": mhz, "power_w_median": float(np.median([p for _, p in use])), "samples": len(use),
+                "peak_bf16_tflops_at_clock": 256 * 4096 * mhz * 1e6 / 1e12}
+
     # ---------------- headline: LM-head prefill ----------------
     cfg = wl.CONFIGS["lmhead"]
     M, K, V, L = cfg.n_seq * cfg.n_pos, cfg.K, cfg.N, cfg.leaves
@@ -188,6 +233,26 @@ def main():
         log(f"prefill: {ms_step:.3f} ms/step, {tok_s:.4g} tok/s, {tflops:.1f} TFLOP/s "
             f"(min {min(per_call):.3f} ms, max {max(per_call):.3f} ms)")
 
+    clock = None
+    tree = None
+    if args.phase == "all":
+        clock = sample_clock(lambda: tig.tig_logprob_gather(Hd, Wd, idd, lp, lse, L, ws), 3.0)
+        if clock is not None and tflops is not None:
+            clock["prefill_frac_of_peak_at_clock"] = tflops / clock["peak_bf16_tflops_at_clock"]
+            log(f"clock while the prefill runs: {clock['gfx_mhz_median']:.0f} MHz, {clock['power_w_median']:.0f} W; "
+                f"peak at that clock {clock['peak_bf16_tflops_at_clock']:.0f} TFLOP/s")
+        # The leaf-tree contraction entry point alone at the headline shape.
+        tree = {"shape": f"M={M} K={K} N={V} leaves={L}"}
+        for name, dt in (("fp32_out", torch.float32), ("bf16_out", torch.bfloat16)):
+            Ct = torch.empty(M, V, dtype=dt, device=dev)
+            ms_t, per_t = timed(lambda: tig.tig_tree_gemm(Hd, Wd, Ct, L), 5, 1, per_call=True)
+            line = mfma_line(flops, ms_t)
+            tree[name] = {"ms": ms_t, "min_ms": float(np.min(per_t)), "tflops": line["achieved"],
+                          "mfma_frac": line["frac"], "roofline": line,
+                          "output_bytes": float(Ct.numel() * Ct.element_size())}
+            log(f"tree_gemm {name}: {ms_t:.3f} ms, {line['achieved']:.0f} TFLOP/s")
+            del Ct
+
     decode = None
     if args.phase in ("all", "decode"):
         Md = cfg.n_seq
@@ -224,7 +289,8 @@ def main():
         del QW8, SW8, QA8, SA8, C8, ws8
 
     cpu = None
-    if not args.no_cpu_baseline and args.phase == "all":
+    do_cpu = not args.no_cpu_baseline and args.phase == "all"
+    if do_cpu:
         import oracle
         try:
             from threadpoolctl import threadpool_info
@@ -238,8 +304,24 @@ def main():
         dt = time.perf_counter() - t0
         cpu = {"value": args.cpu_rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
                "sample": f"first {args.cpu_rows} of the {M} prefill rows, full vocabulary {V}, "
-                         f"fp64 numpy (includes converting W to fp64), {dt:.1f}s"}
-        log(f"cpu oracle: {cpu['value']:.3g} tok/s on {threads} threads")
+                         f"fp64 numpy (includes converting W to fp64), {dt:.1f}s",
+               "host_cores": os.cpu_count(), "blas_threads": int(threads),
+               "configs": {"lmhead": {"rows": args.cpu_rows, "s": dt, "rows_per_s": args.cpu_rows / dt,
+                                      "fp64_gflops": 2.0 * args.cpu_rows * K * V / dt / 1e9}}}
+        log(f"cpu oracle: {cpu['value']:.3g} tok/s on {threads} threads ({os.cpu_count()} host cores)")
+
+        def cpu_line(name, nrows, flop, fn):
+            t1 = time.perf_counter()
+            fn()
+            d = time.perf_counter() - t1
+            cpu["configs"][name] = {"rows": nrows, "s": d, "rows_per_s": nrows / d, "fp64_gflops": flop / d / 1e9}
+            log(f"cpu oracle {name}: {nrows / d:.3g} rows/s, {flop / d / 1e9:.1f} fp64 GFLOP/s ({d:.1f}s)")
+
+        c = wl.CONFIGS["tiny"]
+        st = wl.streams(c.seed)
+        Ht, Wt = wl.normal_bf16(st["H"], (64, c.K), 1.0), wl.normal_bf16(st["W"], (c.N, c.K), 0.02)
+        it = wl.uniform_ids(st["ids"], 64, c.N)
+        cpu_line("tiny", 64, 2.0 * 64 * c.K * c.N, lambda: oracle.logprob_ref(Ht, Wt, it))
     del H, W
     del Hd, Wd, idd, ws
 
@@ -248,8 +330,11 @@ def main():
     if not args.no_extra and args.phase == "all":
         c = wl.CONFIGS["linear"]
         sl = wl.streams(c.seed)
-        A = to_dev(wl.normal_bf16(sl["H"], (4097, c.K), 1.0))
-        Wl = to_dev(wl.normal_bf16(sl["W"], (c.N, c.K), 0.02))
+        Ah, Wlh = wl.normal_bf16(sl["H"], (4097, c.K), 1.0), wl.normal_bf16(sl["W"], (c.N, c.K), 0.02)
+        A, Wl = to_dev(Ah), to_dev(Wlh)
+        if do_cpu:
+            cpu_line("linear", 4097, 2.0 * 4097 * c.K * c.N, lambda: oracle.contraction_ref(Ah, Wlh))
+        del Ah, Wlh
         linear = {}
         for Mr in (4096, 4097):
             Ar = A[:Mr]
@@ -278,9 +363,12 @@ def main():
 
         c = wl.CONFIGS["moe"]
         sm = wl.streams(c.seed)
-        Hm = to_dev(wl.normal_bf16(sm["H"], (c.tokens, c.K), 1.0))
-        We = to_dev(wl.normal_bf16(sm["W"], (c.experts, c.N, c.K), 0.02))
-        tid, tw = wl.route_topk(sm["route"], c.tokens, c.experts, c.topk)
+        Hmh, Weh = wl.normal_bf16(sm["H"], (c.tokens, c.K), 1.0), wl.normal_bf16(sm["W"], (c.experts, c.N, c.K), 0.02)
+        Hm, We = to_dev(Hmh), to_dev(Weh)
+        tid, tw = wl.routing_input(sm["route"], c.tokens, c.experts, c.topk)
+        if do_cpu:
+            cpu_line("moe", c.tokens, 2.0 * c.tokens * c.topk * c.K * c.N, lambda: oracle.moe_ref(Hmh, Weh, tid, tw))
+        del Hmh, Weh
         tid, tw = torch.from_numpy(tid).to(dev), torch.from_numpy(tw).to(dev)
         out = torch.empty(c.tokens, c.N, dtype=torch.float32, device=dev)
         wsm = torch.empty(tig.tig_moe_workspace_bytes(c.tokens, c.N, c.K, c.experts, c.topk),
@@ -388,9 +476,14 @@ def main():
         c = wl.CONFIGS["large"]
         sg = wl.streams(c.seed)
         Mg = c.n_seq * c.n_pos
-        Hg = to_dev(wl.normal_bf16(sg["H"], (Mg, c.K), 1.0))
-        Wg = to_dev(wl.normal_bf16(sg["W"], (c.N, c.K), 0.02))
-        ig = torch.from_numpy(wl.uniform_ids(sg["ids"], Mg, c.N)).to(dev)
+        Hgh, Wgh = wl.normal_bf16(sg["H"], (Mg, c.K), 1.0), wl.normal_bf16(sg["W"], (c.N, c.K), 0.02)
+        igh = wl.uniform_ids(sg["ids"], Mg, c.N)
+        Hg, Wg = to_dev(Hgh), to_dev(Wgh)
+        ig = torch.from_numpy(igh).to(dev)
+        if do_cpu:
+            nr = args.cpu_rows_large
+            cpu_line("large", nr, 2.0 * nr * c.K * c.N, lambda: oracle.logprob_ref(Hgh[:nr], Wgh, igh[:nr]))
+        del Hgh, Wgh
         large = {}
         for name, Mr, steps in (("prefill", Mg, 3), ("decode", c.n_seq, 20)):
             Hr, ir = Hg[:Mr].contiguous(), ig[:Mr].contiguous()
@@ -417,9 +510,9 @@ def main():
         "roofline": None if tflops is None else {
             "bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
             "frac": tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic("lmhead_prefill")},
-        "tree_gemm": None if tflops is None else {
-            "tflops": tflops, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
-            "shape": f"M={M} K={K} N={V} leaves={L}", "spread": spread},
+        "prefill_spread": spread,
+        "tree_gemm": tree,
+        "clock": clock,
         "device_copy_GBs": copy_gbs,
         "decode": decode,
         "linear": linear,

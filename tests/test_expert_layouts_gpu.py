@@ -237,7 +237,7 @@ def test_expert_gemm_moe_config(gpu_lib):
     s = wl.streams(cfg.seed)
     H = wl.normal_bf16(s["H"], (cfg.tokens, cfg.K), 1.0)
     We = wl.normal_bf16(s["W"], (cfg.experts, cfg.N, cfg.K), 0.02)
-    ids, _ = wl.route_topk(s["route"], cfg.tokens, cfg.experts, cfg.topk)
+    ids, _ = wl.routing_input(s["route"], cfg.tokens, cfg.experts, cfg.topk)
     rows_e = [H[np.nonzero((ids == e).any(axis=1))[0]] for e in range(cfg.experts)]
     cap = int(-(-max(r.shape[0] for r in rows_e) // 64) * 64)
     counts, Xm, Xc, starts = _layouts(s["extra"], rows_e, cfg.K, cap, 128)

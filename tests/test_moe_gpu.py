@@ -23,7 +23,7 @@ def moe():
     s = wl.streams(cfg.seed)
     H = wl.normal_bf16(s["H"], (cfg.tokens, cfg.K), 1.0)
     We = wl.normal_bf16(s["W"], (cfg.experts, cfg.N, cfg.K), 0.02)
-    ids, w = wl.route_topk(s["route"], cfg.tokens, cfg.experts, cfg.topk)
+    ids, w = wl.routing_input(s["route"], cfg.tokens, cfg.experts, cfg.topk)
     return cfg, H, We, ids, w, s["perm"]
 
 

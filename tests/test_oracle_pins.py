@@ -309,7 +309,7 @@ def test_moe_ref_brute_force():
     T, E, N, K, topk = 4, 5, 3, 8, 2
     H = wl.normal_bf16(rng, (T, K))
     We = wl.normal_bf16(rng, (E, N, K), 0.5)
-    ids, w = wl.route_topk(rng, T, E, topk)
+    ids, w = wl.routing_input(rng, T, E, topk)
     got = oracle.moe_ref(H, We, ids, w)
     for t in range(T):
         for n in range(N):
@@ -347,12 +347,14 @@ def test_moe_combine_closed_forms(row):
 
 def test_routing_input_is_valid():
     rng = np.random.default_rng(13)
-    ids, w = wl.route_topk(rng, 100, 64, 8)
-    assert ids.shape == (100, 8) and ids.dtype == np.int32
+    ids, w = wl.routing_input(rng, 2000, 64, 8)
+    assert ids.shape == (2000, 8) and ids.dtype == np.int32 and w.dtype == np.float32
     for r in ids:
-        assert len(set(r.tolist())) == 8
-    assert np.allclose(w.sum(axis=1), 1.0, atol=1e-6)
-    assert np.all(np.diff(w, axis=1) <= 0)  # descending-logit slot order
+        assert len(set(r.tolist())) == 8 and r.min() >= 0 and r.max() < 64
+    assert np.all(w > 0) and np.allclose(w.sum(axis=1), 1.0, atol=1e-6)
+    # every expert is used about equally (16000 pairs over 64 experts: 250 each)
+    cnt = np.bincount(ids.reshape(-1), minlength=64)
+    assert cnt.min() > 150 and cnt.max() < 350
 
 
 # ---------------------------------------------------------------------------

@@ -19,9 +19,10 @@ the separate streams, so changing one stream never shifts another):
   chunk is sequence-major, decode step ``t`` holds position ``t`` of every
   sequence (shuffled with a seeded permutation where a config asks for mixed
   sequence origins);
-* MoE routing: router logits N(0, 1) in float64, the top-k experts by logit
-  (ties go to the lower expert id), gate weights are the softmax over the k
-  selected logits, stored as float32;
+* MoE routing inputs for the expert combine: ``topk`` distinct experts per
+  token drawn uniformly and flat-Dirichlet gate weights (float32); no router
+  arithmetic (the router is a separate entry point checked against the
+  oracle);
 * indexer scores for the Top-K of positions: float32 N(0, 1) draws, by default
   rounded to bf16 values so that equal scores are common; request lengths
   uniform in a stated range.
@@ -41,7 +42,7 @@ __all__ = [
     "streams",
     "uniform_ids",
     "gumbel",
-    "route_topk",
+    "routing_input",
     "prefill_decode_rows",
     "integer_bf16",
     "indexer_scores",
@@ -162,19 +163,21 @@ def gumbel(rng: np.random.Generator, shape) -> np.ndarray:
     return -np.log(-np.log(u))
 
 
-def route_topk(rng: np.random.Generator, T: int, E: int, topk: int):
+def routing_input(rng: np.random.Generator, T: int, E: int, topk: int):
     """MoE routing input: ``(topk_ids int32 [T, topk], topk_w float32 [T, topk])``.
 
-    Router logits are N(0, 1) in float64.  The selected experts are the ``topk``
-    largest logits, ties to the lower expert id, in descending-logit slot order.
-    Gate weights are the softmax over the selected logits.
+    A plain sample with the structure of a top-k routing, not a router: each
+    token gets ``topk`` distinct experts drawn uniformly (the first ``topk`` of a
+    random permutation of the experts), and gate weights drawn from the flat
+    Dirichlet distribution (independent unit exponentials divided by their
+    sum: positive, summing to 1), stored as float32.  The router itself (top-k
+    of the router logits and a softmax over them) is the GPU path's
+    ``tig_moe_route`` and the oracle's routing functions, not this module.
     """
-    logits = rng.standard_normal((T, E))
-    order = np.argsort(-logits, axis=1, kind="stable")[:, :topk]
-    sel = np.take_along_axis(logits, order, axis=1)
-    z = np.exp(sel - sel.max(axis=1, keepdims=True))
-    w = z / z.sum(axis=1, keepdims=True)
-    return order.astype(np.int32), w.astype(np.float32)
+    ids = np.argsort(rng.random((T, E)), axis=1, kind="stable")[:, :topk]
+    g = rng.exponential(size=(T, topk))
+    w = g / g.sum(axis=1, keepdims=True)
+    return ids.astype(np.int32), w.astype(np.float32)
 
 
 def prefill_decode_rows(n_seq: int, n_pos: int, rng: np.random.Generator | None = None):
