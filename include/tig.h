@@ -105,7 +105,9 @@ tig_status tig_tree_gemm(const void* A, int64_t lda, const void* W, int64_t ldw,
  *   lse_out      float [M] log-sum-exp of the row's logits, or NULL to skip
  *   workspace    device scratch of at least tig_logprob_workspace_bytes()
  *                bytes, 256-byte aligned; contents on entry are ignored
- * Implemented: leaves <= 16, K/leaves a multiple of 64, n_vocab <= 2^23.
+ * Implemented: leaves <= 16, K/leaves a multiple of 64, n_vocab <= 2^23, and
+ * 192 rows of H spanning less than 2 GiB (K < 5592406), at every M (else
+ * UNSUPPORTED, whatever the batch size).
  * M == 0 is TIG_OK and launches nothing.
  */
 tig_status tig_logprob_gather(const void* H, const void* W, const int64_t* ids,

@@ -243,8 +243,10 @@ tig_status tig_logprob_gather(const void* H, const void* W, const int64_t* ids, 
     return fail(TIG_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need,
                 workspace ? workspace_bytes : size_t(0));
   if (!aligned(workspace, 256)) return fail(TIG_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  // The tallest tile bounds the span at every M, so that whether a row is
+  // accepted never depends on the batch it arrives in.
   const int bm = tig::logprob_block_m_for(M, log2i(leaves));
-  if ((s = check_span("H tile", bm, K)) != TIG_OK) return s;
+  if ((s = check_span("H tile", tig::kLogprobMaxBlockM, K)) != TIG_OK) return s;
   if (tig::cdiv(M, bm) * tig::cdiv(n_vocab, tig::kBlockN) >= (int64_t(1) << 31) - 8)
     return fail(TIG_ERR_UNSUPPORTED, "too many output tiles");
   char* ws = static_cast<char*>(workspace);

@@ -31,6 +31,7 @@ inline int block_m_for(int64_t M, int leaves_log2) {
 // of tiles it runs under the schedule's deal over this device's CUs, times the
 // measured time of one tile of that height relative to a 128-row tile.
 int tree_gemm_block_m(int64_t M, int64_t N, int leaves_log2);
+constexpr int kLogprobMaxBlockM = 192;   // tallest tile of the logprob path, at every leaf count
 inline int logprob_block_m_for(int64_t M, int leaves_log2) {
   (void)leaves_log2;
   return (M + 191) / 192 < (M + 127) / 128 ? 192 : 128;

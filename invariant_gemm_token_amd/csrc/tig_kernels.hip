@@ -1275,7 +1275,12 @@ __global__ __launch_bounds__(256) void logprob_combine_kernel(
   constexpr int CACHE = 8;
   float2 v[CACHE];
 #pragma unroll
-  for (int i = 0; i < CACHE; ++i) v[i] = i < c && t0 + i < n_vt ? pr[t0 + i] : make_float2(-__builtin_inff(), 0.0f);
+  for (int i = 0; i < CACHE; ++i) v[i] = make_float2(-__builtin_inff(), 0.0f);
+  if (c <= CACHE) {
+#pragma unroll
+    for (int i = 0; i < CACHE; ++i)
+      if (i < c && t0 + i < n_vt) v[i] = pr[t0 + i];
+  }
 
   float g = -__builtin_inff();
   if (c <= CACHE) {

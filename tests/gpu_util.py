@@ -6,10 +6,25 @@ which is checked on the raw bits; on failure the first differing index and
 value pair are reported.
 """
 
+import os
 import sys
 
 import numpy as np
 import torch
+
+
+# Every comparison made through these helpers during a test session, written
+# as JSON at the end of the session (tests/conftest.py): the bitwise checks
+# with their diff statistics (max, mean, std of |delta| and the k3 KL of the
+# bit-consistent RL post, section 3.2, all exactly 0 when they pass) and the
+# largest deviations from the fp64 oracle.
+REPORT: list = []
+
+
+def record(kind: str, what: str, **fields):
+    """Add one comparison to the session report, tagged with the running test."""
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    REPORT.append(dict(test=test, kind=kind, what=what, **fields))
 
 
 def say(*a):
@@ -39,6 +54,10 @@ def host_bits(t: torch.Tensor) -> np.ndarray:
 def assert_bitwise(a: torch.Tensor, b: torch.Tensor, what: str):
     ba, bb = host_bits(a), host_bits(b)
     assert ba.shape == bb.shape, f"{what}: shapes {ba.shape} vs {bb.shape}"
+    fields = {"elements": int(ba.size), "differing": int(np.count_nonzero(ba != bb))}
+    if a.dtype == torch.float32 and a.dim() == 1:
+        fields.update(diff_stats(a.detach().cpu().double().numpy(), b.detach().cpu().double().numpy()))
+    record("bitwise", what, **fields)
     if not np.array_equal(ba, bb):
         idx = np.argwhere(ba != bb)
         i = tuple(idx[0])
@@ -64,8 +83,10 @@ def assert_gemm_close(got: np.ndarray, ref: np.ndarray, rel: float = 2e-3, what:
     rms = float(np.sqrt(np.mean(ref * ref))) if ref.size else 0.0
     bound = rel * np.maximum(np.abs(ref), rms)
     bad = np.abs(got - ref) > bound
+    worst = float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), rms))) if ref.size else 0.0
+    record("oracle_gemm", what, elements=int(ref.size), max_rel=worst, bound=rel, outside=int(bad.sum()))
     if bad.any():
         i = tuple(np.argwhere(bad)[0])
         raise AssertionError(f"{what}: {int(bad.sum())} outside tolerance; first {i}: "
                              f"got {got[i]!r} ref {ref[i]!r} bound {bound[i]!r}")
-    return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), rms))) if ref.size else 0.0
+    return worst

@@ -271,6 +271,14 @@ def test_alignment_and_workspace_errors_with_fake_pointers():
         assert lib.tig_tree_gemm(F, big, F, 512, F, 64, 0, M, 64, 512, 8, None) == tig.TIG_ERR_UNSUPPORTED
     assert lib.tig_tree_gemm(F, 512, F, (1 << 31) // 256 // 8 * 8 + 8, F, 64, 0, 4, 64, 512, 8,
                              None) == tig.TIG_ERR_UNSUPPORTED
+    # logprob: 192 rows of H spanning 2 GiB are rejected at every M, including the
+    # batch sizes that would run on 128-row tiles (K = 5592576 = 10923 x 512)
+    Kbig = 10923 * 512
+    assert 128 * Kbig * 2 < (1 << 31) <= 192 * Kbig * 2
+    for M in (1, 128, 300):
+        wsb = tig.tig_logprob_workspace_bytes(M, Kbig, 64, 8)
+        assert lib.tig_logprob_gather(F, F, F, F, None, M, Kbig, 64, 8, F, wsb, None) == tig.TIG_ERR_UNSUPPORTED
+        assert "spans" in tig.tig_last_error()
     # workspace missing / too small / misaligned
     need = tig.tig_logprob_workspace_bytes(4, 512, 64, 8)
     assert lib.tig_logprob_gather(F, F, F, F, None, 4, 512, 64, 8, None, 0, None) == tig.TIG_ERR_WORKSPACE

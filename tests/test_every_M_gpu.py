@@ -6,9 +6,15 @@ result may not depend on how many rows share its call.  The linear layer
 result compared bit for bit with the first M rows of the 4097-row call; the
 calls cover every tile height the schedule picks (64, 128 and 192 rows), every
 ragged last m-tile and grids from one workgroup to several tiles per
-workgroup.  The fused logprob is swept the same way over M = 1 .. 600 at a
-smaller LM head (K = 1024, V = 5000, 8 leaves): single row-of-tiles calls up
-to 128 rows, 128- and 192-row tiles above.  Comparisons run on the device.
+workgroup.  The fused logprob is swept the same way over M = 1 .. 600 on
+smaller LM heads: K = 1024, V = 5000 at 8 and at 16 leaves (64-column leaves),
+K = 2048, V = 5000 at 16 leaves, and the full 151936-token vocabulary at
+K = 512, 8 leaves.  Up to 192 rows a call has a single row of tiles (the sampled
+logit picked inside the tile kernel); above, 128- and 192-row tiles alternate
+as M grows, and at 16 leaves the 192-row tiles park the first half of the leaf
+tree outside registers.  The 16-leaf contraction (K = 2048, N = 1024) is swept
+over every M from 1 to 1024 (64- and 128-row tiles).  Comparisons run on the
+device.
 """
 
 import numpy as np
@@ -52,9 +58,10 @@ def test_linear_every_M_1_to_4097(gpu_lib):
     assert not bad, f"rows differ from the 4097-row call at (M, (row, col)): {bad}"
 
 
-def test_logprob_every_M_1_to_600(gpu_lib):
-    K, V, L, Mmax = 1024, 5000, 8, 600
-    rng = np.random.default_rng(20241)
+@pytest.mark.parametrize("K,V,L", [(1024, 5000, 8), (1024, 5000, 16), (2048, 5000, 16), (512, 151936, 8)])
+def test_logprob_every_M_1_to_600(gpu_lib, K, V, L):
+    Mmax = 600
+    rng = np.random.default_rng(20241 + K + V + L)
     H = dev_bf16(wl.normal_bf16(rng, (Mmax, K), 1.0))
     W = dev_bf16(wl.normal_bf16(rng, (V, K), 0.03))
     ids = torch.from_numpy(rng.integers(0, V, size=Mmax)).to("cuda:0")
@@ -67,7 +74,7 @@ def test_logprob_every_M_1_to_600(gpu_lib):
     bad = []
     for M in range(1, Mmax + 1):
         if M % 100 == 1:
-            say(f"logprob every M: M = {M} ..")
+            say(f"logprob every M (K={K} V={V} L={L}): M = {M} ..")
         gpu_lib.tig_logprob_gather(H[:M], W, ids[:M], lp[:M], lse[:M], L, ws)
         for name, got, ref in (("logprob", lp[:M], full_lp[:M]), ("lse", lse[:M], full_lse[:M])):
             where = _first_mismatch(got, ref)
@@ -76,4 +83,28 @@ def test_logprob_every_M_1_to_600(gpu_lib):
         if len(bad) >= 5:
             break
     torch.cuda.synchronize()
+    assert bool(torch.isfinite(full_lp).all())
     assert not bad, f"rows differ from the 600-row call: {bad}"
+
+
+def test_tree_gemm_16_leaves_every_M_1_to_1024(gpu_lib):
+    K, N, L, Mmax = 2048, 1024, 16, 1024
+    rng = np.random.default_rng(77)
+    A = dev_bf16(wl.normal_bf16(rng, (Mmax, K), 1.0))
+    W = dev_bf16(wl.normal_bf16(rng, (N, K), 0.02))
+    full = torch.empty(Mmax, N, dtype=torch.float32, device="cuda:0")
+    gpu_lib.tig_tree_gemm(A, W, full, L)
+    out = torch.empty_like(full)
+    bad = []
+    for M in range(1, Mmax + 1):
+        if M % 256 == 1:
+            say(f"16-leaf contraction every M: M = {M} ..")
+        C = out[:M]
+        gpu_lib.tig_tree_gemm(A[:M], W, C, L)
+        where = _first_mismatch(C, full[:M])
+        if where is not None:
+            bad.append((M, where))
+            if len(bad) >= 5:
+                break
+    torch.cuda.synchronize()
+    assert not bad, f"rows differ from the 1024-row call at (M, (row, col)): {bad}"

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import workloads as wl
-from gpu_util import assert_bitwise, dev_bf16, diff_stats, say
+from gpu_util import assert_bitwise, dev_bf16, diff_stats, record, say
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-3
@@ -26,6 +26,7 @@ def _parity(lp, lse, ref_lp, ref_lse, what):
     e1 = np.max(np.abs(lp - ref_lp))
     e2 = np.max(np.abs(lse - ref_lse))
     say(f"{what}: max |dlogprob| {e1:.3e}  max |dlse| {e2:.3e}")
+    record("oracle_logprob", what, rows=int(lp.size), max_abs_logprob=float(e1), max_abs_lse=float(e2), bound=TOL)
     assert e1 <= TOL and e2 <= TOL, what
     return e1
 
@@ -81,12 +82,14 @@ def test_equal_logits_closed_form(gpu_lib, V):
     assert np.max(np.abs(lse.cpu().double().numpy() - (X + math.log(V)))) < 1e-5
 
 
-@pytest.mark.parametrize("V,M", [(151936, 100), (151936, 300), (4097, 130), (129, 64)])
+@pytest.mark.parametrize("V,M", [(151936, 100), (151936, 300), (4097, 130), (129, 64), (4097, 200),
+                                 (129, 400)])
 def test_one_distinct_logit_closed_form(gpu_lib, V, M):
     """One vocabulary row gives logit a, every other row 0: logprob = a - ln(e^a + V - 1)
     for the sampled id of that row and -ln(e^a + V - 1) for any other (a closed form,
-    independent of the oracle), through the single-row-of-tiles path (M <= 128) and
-    the multi-row one, with the distinct row in a middle tile and ids on both sides."""
+    independent of the oracle), through the single-row-of-tiles path (up to 192 rows)
+    and the multi-row one (at the full vocabulary and at ragged ones), with the
+    distinct row in a middle tile and ids on both sides."""
     K, L = 1024, 8
     rng = np.random.default_rng(V + M)
     j = V // 2 + 3 if V > 8 else 0
@@ -106,6 +109,49 @@ def test_one_distinct_logit_closed_form(gpu_lib, V, M):
     say(f"one distinct logit V={V} M={M}: max |dlogprob| {np.max(np.abs(lp - exp_lp)):.2e}")
     assert np.max(np.abs(lse - exp_lse)) < 1e-5
     assert np.max(np.abs(lp - exp_lp)) < 1e-5
+
+
+# Vocabularies above 256 x 8 x 128 = 262144 tokens give the combine pass more
+# than 8 vocabulary tiles per thread: it reads each row's tile partials twice
+# (once for the max, once for the sum) instead of keeping them in registers.
+@pytest.mark.parametrize("V", [262145, 1000003, 1 << 23])
+def test_large_vocab_equal_logits_closed_form(gpu_lib, V):
+    """All W rows equal: logprob = -ln V and lse = logit + ln V (the tile sums are
+    exact, V < 2^24), and each row the same bits at every M."""
+    K, L, Mmax = 512, 8, 37
+    rng = np.random.default_rng(V)
+    H = dev_bf16(wl.normal_bf16(rng, (Mmax, K), 1.0))
+    row = dev_bf16(wl.normal_bf16(rng, (1, K), 0.05))
+    W = row.expand(V, K).contiguous()
+    ids = torch.from_numpy(rng.integers(0, V, size=Mmax)).cuda()
+    say(f"equal logits V={V}")
+    lp, lse = gpu_lib.logprob_gather(H, W, ids, L)
+    x = gpu_lib.tree_gemm(H, row, L)[:, 0].double()
+    assert float((lp.double() + math.log(V)).abs().max()) < 2e-5
+    assert float((lse.double() - (x + math.log(V))).abs().max()) < 2e-5
+    for M in (1, 2, 5, 36):
+        a, b = gpu_lib.logprob_gather(H[:M], W, ids[:M], L)
+        assert_bitwise(a, lp[:M], f"V={V} logprob M={M}")
+        assert_bitwise(b, lse[:M], f"V={V} lse M={M}")
+
+
+def test_large_vocab_parity(gpu_lib):
+    """Random weights at a vocabulary of 1000003 (7813 tiles: the combine's
+    re-read path, a last tile of 3 columns) against the fp64 oracle, and each
+    row's bits independent of M."""
+    K, V, L, M = 512, 1000003, 8, 6
+    rng = np.random.default_rng(99)
+    H = wl.normal_bf16(rng, (M, K), 1.0)
+    W = wl.normal_bf16(rng, (V, K), 0.05)
+    ids = rng.integers(0, V, size=M)
+    ids[0], ids[1] = V - 1, 0
+    Hd, Wd, idd = dev_bf16(H), dev_bf16(W), torch.from_numpy(ids).cuda()
+    lp, lse = gpu_lib.logprob_gather(Hd, Wd, idd, L)
+    ref_lp, ref_lse = oracle.logprob_ref(H, W, ids)
+    _parity(lp, lse, ref_lp, ref_lse, f"V={V} M={M}")
+    a, b = gpu_lib.logprob_gather(Hd[:1], Wd, idd[:1], L)
+    assert_bitwise(a, lp[:1], "V=1000003 logprob M=1")
+    assert_bitwise(b, lse[:1], "V=1000003 lse M=1")
 
 
 def test_vocab_of_one(gpu_lib):
