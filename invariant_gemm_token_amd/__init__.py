@@ -42,7 +42,9 @@ _LIB = None
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "libtig.so")
+    """The in-tree ``libtig.so``, or the library named by ``$TIG_LIB`` (for example a
+    sanitizer build of the host code used by the CPU tests)."""
+    return os.environ.get("TIG_LIB") or os.path.join(_HERE, "libtig.so")
 
 
 class TigError(RuntimeError):
