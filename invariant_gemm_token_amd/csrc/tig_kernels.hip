@@ -605,22 +605,22 @@ struct LogprobEpi {
   // Block (i, j) of the right half's root becomes left + right, the tree's
   // last addition.  The loads are asm blocks of two, each ending in its own
   // wait (device scope: read from L2), so that the compiler neither hoists
-  // them nor keeps more than 8 extra registers live.  Each block starts with
-  // five wait states: the scalar base may have just been written by a VALU
-  // instruction (a v_readlane reloading a spilled SGPR), and a VMEM
-  // instruction reading that SGPR needs them; the compiler does not insert
-  // them in front of inline asm.
+  // them nor keeps more than 8 extra registers live.  Their addresses are
+  // per-lane 64-bit VGPR pointers: the blocks read no SGPR, so no scalar base
+  // reloaded by a vector instruction (a spilled SGPR brought back with
+  // v_readlane) can reach them without its wait states.
   __device__ __forceinline__ void join(int i, int j, f32x16& c) const {
-    const float* b = area() + ((i * 2 + j) * 4) * NTHREADS * 4;   // uniform: scalar base
-    const uint32_t voff = uint32_t(opaque_tid()) * 16;
+    const float* b = area() + (size_t((i * 2 + j) * 4) * NTHREADS + size_t(opaque_tid())) * 4;
 #pragma unroll
     for (int q = 0; q < 4; q += 2) {
+      const float* p0 = b + size_t(q) * NTHREADS * 4;
+      const float* p1 = p0 + NTHREADS * 4;
       float4 l0, l1;
       asm volatile(
-          "s_nop 4\n global_load_dwordx4 %0, %2, %3 sc1\n global_load_dwordx4 %1, %2, %4 sc1\n"
+          "global_load_dwordx4 %0, %2, off sc1\n global_load_dwordx4 %1, %3, off sc1\n"
           "s_waitcnt vmcnt(0)"
           : "=&v"(l0), "=&v"(l1)
-          : "v"(voff), "s"(b + q * NTHREADS * 4), "s"(b + (q + 1) * NTHREADS * 4)
+          : "v"(p0), "v"(p1)
           : "memory");
       c[4 * q + 0] = l0.x + c[4 * q + 0];
       c[4 * q + 1] = l0.y + c[4 * q + 1];
