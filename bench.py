@@ -16,6 +16,10 @@ line carries:
   fraction of the peak;
 * clock: the GFX clock and board power sampled while the prefill runs in a
   loop, and the matrix-core peak at that clock (256 CUs x 4096 flop/clock);
+* vendor_plain_gemm_context: torch.matmul (the vendor library's plain bf16
+  GEMM, no leaf tree, no log-softmax) at the same shape, timed on the same
+  box with its clock and power: context for what the board sustains, not
+  part of the path;
 * decode: one 128-row decode step of the same LM head (bound by streaming the
   1.245 GB weight from HBM), tokens/s and fraction of 8 TB/s;
 * linear, moe, large: the other workloads of the path, each with its own
@@ -95,7 +99,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--cpu-rows-large", type=int, default=256)
     ap.add_argument("--no-extra", action="store_true", help="skip the linear / moe / large lines")
-    ap.add_argument("--phase", choices=("all", "prefill", "decode"), default="all",
+    ap.add_argument("--phase", choices=("all", "prefill", "decode", "tree"), default="all",
                     help="time only one LM-head configuration (for per-kernel profiles)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device-to-device copy (counter calibration)")
@@ -235,18 +239,36 @@ def main():
 
     clock = None
     tree = None
+    vendor = None
     if args.phase == "all":
         clock = sample_clock(lambda: tig.tig_logprob_gather(Hd, Wd, idd, lp, lse, L, ws), 3.0)
         if clock is not None and tflops is not None:
             clock["prefill_frac_of_peak_at_clock"] = tflops / clock["peak_bf16_tflops_at_clock"]
             log(f"clock while the prefill runs: {clock['gfx_mhz_median']:.0f} MHz, {clock['power_w_median']:.0f} W; "
                 f"peak at that clock {clock['peak_bf16_tflops_at_clock']:.0f} TFLOP/s")
+        # Context, not the product path: the vendor's plain bf16 GEMM of the same shape (torch.matmul, no
+        # leaf tree, no log-softmax, bf16 output), with the clock and power it runs at on this machine.
+        try:
+            Wt = Wd.t()
+            Cb = torch.empty(M, V, dtype=torch.bfloat16, device=dev)
+            ms_ref, _ = timed(lambda: torch.matmul(Hd, Wt, out=Cb), 5, 2)
+            ref_clock = sample_clock(lambda: torch.matmul(Hd, Wt, out=Cb), 2.0)
+            vendor = {"ms": ms_ref, "tflops": flops / (ms_ref / 1e3) / 1e12, "what": "torch.matmul bf16 out",
+                      "clock": ref_clock}
+            log(f"vendor plain GEMM (context): {ms_ref:.3f} ms, {vendor['tflops']:.0f} TFLOP/s")
+            del Cb, Wt
+        except Exception as e:   # the context line never fails the bench
+            vendor = {"error": str(e)}
+    if args.phase in ("all", "tree"):
         # The leaf-tree contraction entry point alone at the headline shape.
         tree = {"shape": f"M={M} K={K} N={V} leaves={L}"}
         for name, dt in (("fp32_out", torch.float32), ("bf16_out", torch.bfloat16)):
+            if args.phase == "tree" and name == "bf16_out":
+                continue
             Ct = torch.empty(M, V, dtype=dt, device=dev)
             ms_t, per_t = timed(lambda: tig.tig_tree_gemm(Hd, Wd, Ct, L), 5, 1, per_call=True)
             line = mfma_line(flops, ms_t)
+            line["traffic"] = measured_traffic("tree_gemm_lmhead") if name == "fp32_out" else None
             tree[name] = {"ms": ms_t, "min_ms": float(np.min(per_t)), "tflops": line["achieved"],
                           "mfma_frac": line["frac"], "roofline": line,
                           "output_bytes": float(Ct.numel() * Ct.element_size())}
@@ -263,6 +285,7 @@ def main():
                           args.decode_steps, args.warmup)
         dec_bytes = 2.0 * K * V + 2.0 * Md * K + 8.0 * Md + 4.0 * Md
         r = hbm_line(dec_bytes, dec_ms)
+        r["traffic"] = measured_traffic("lmhead_decode")
         log(f"decode M={Md}: {dec_ms * 1e3:.1f} us/step, {r['achieved']:.0f} GB/s")
         decode = {"tokens": Md, "us_per_step": dec_ms * 1e3, "tokens_per_s": Md / (dec_ms / 1e3),
                   "achieved_GBs": r["achieved"], "peak_GBs": PEAK_HBM_GBS, "hbm_frac": r["frac"],
@@ -513,6 +536,7 @@ def main():
         "prefill_spread": spread,
         "tree_gemm": tree,
         "clock": clock,
+        "vendor_plain_gemm_context": vendor,
         "device_copy_GBs": copy_gbs,
         "decode": decode,
         "linear": linear,

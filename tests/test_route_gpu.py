@@ -77,6 +77,12 @@ def test_route_moe_config_parity_and_order(gpu_lib):
     ref_logits, ref_ids, ref_w = oracle.route_ref(H, Wr, cfg.topk)
     assert_gemm_close(lg, ref_logits, what="router logits")
     _valid_order(lg, ids_np)
+    # The selection is an integer decision on FP32 logits: taken by the oracle's
+    # rule on the kernel's own FP32 logits (exact in fp64), it is the kernel's,
+    # on every row; so are the gates, within the exp2 / division tolerance.
+    lg64 = lg.astype(np.float64)
+    assert np.array_equal(ids_np, oracle.route_select(lg64, cfg.topk))
+    assert np.max(np.abs(w_np - oracle.route_gates_ref(lg64, ids_np))) <= GATE_ATOL
     # Where the oracle's ranking has a clear margin, the selection is the oracle's.
     srt = -np.sort(-ref_logits, axis=1)
     gaps = np.abs(np.diff(srt[:, :cfg.topk + 1], axis=1)).min(axis=1)
