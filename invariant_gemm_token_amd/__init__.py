@@ -135,8 +135,14 @@ def _torch():
 
 def _stream(stream) -> int:
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
-    return int(s.cuda_stream)
+    if stream is not None:
+        return int(stream.cuda_stream)
+    # The current stream's handle without building a Stream object (which costs
+    # a few microseconds per call); the public route where that getter is absent.
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    if raw is not None:
+        return int(raw(torch._C._cuda_getDevice()))
+    return int(torch.cuda.current_stream().cuda_stream)
 
 
 def _need(t, name, dtype, ndim):
