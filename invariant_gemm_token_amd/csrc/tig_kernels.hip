@@ -2481,6 +2481,10 @@ constexpr int kTopkGroup = 16;                       // slots loaded and tested 
 constexpr int kTopkCopies = 8;                       // histogram copies, by lane % 8
 constexpr int kTopkHistStride = 2048 + 4;            // words from one copy to the next (4 banks on)
 constexpr int kTopkBlocks = kTopkPerThread * kTopkWaves;   // 64-position blocks of the longest row
+// Keys of the first pass's threshold bin that the last two passes can take
+// from a list in LDS (the histogram copies past the first): more fall back to
+// scanning every key again.
+constexpr int kTopkListCap = (kTopkCopies - 1) * kTopkHistStride;
 
 // f(integral_constant<I>), f(integral_constant<I+1>), ..., below N.
 template <int I, int N, class F>
@@ -2584,7 +2588,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
   __shared__ __attribute__((aligned(16))) uint32_t hist[kTopkCopies * kTopkHistStride];
   __shared__ __attribute__((aligned(16))) uint32_t masks[kTopkBlocks * 4];   // per block: gt lo, hi, eq lo, hi
   __shared__ __attribute__((aligned(16))) int red[4 * kTopkWaves];   // two halves, alternated by pass; scans
-  __shared__ int found[2][2];
+  __shared__ int found[2][3];   // per pass parity: digit, keys still wanted, keys in the digit's bin
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int n = lengths[r];
@@ -2637,26 +2641,109 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
     for (int i = tid; i < kTopkCopies * kTopkHistStride / 4; i += kTopkThreads)
       reinterpret_cast<uint4*>(hist)[i] = make_uint4(0u, 0u, 0u, 0u);
     __syncthreads();
-    uint32_t prefix = 0;
-    int rem = take;
+    // One pass's histogram (NCOP copies) to the digit at which the count from
+    // the top reaches `want`: thread t owns bins 4t..4t+3 and clears them as it
+    // reads them; `above` counts the bins of the threads after it, i.e. the
+    // larger digits.  Ends with a barrier; `par` alternates the scan's area.
+    auto scan_find = [&](auto ncop, int par, int want, int& digit, int& left, int& bin_n) {
+      constexpr int NCOP = decltype(ncop)::value;
+      int h[4] = {0, 0, 0, 0};
 #pragma unroll
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-      const uint32_t dmask = pass == 2 ? 1023u : 2047u;
-      const int pshift = pass == 1 ? 21 : 10;        // bits below the digits already found
+      for (int c = 0; c < NCOP; ++c) {
+        uint4* const w = reinterpret_cast<uint4*>(&hist[c * kTopkHistStride + 4 * tid]);
+        const uint4 q = *w;
+        *w = make_uint4(0u, 0u, 0u, 0u);
+        h[0] += int(q.x);
+        h[1] += int(q.y);
+        h[2] += int(q.z);
+        h[3] += int(q.w);
+      }
+      const int mine = h[0] + h[1] + h[2] + h[3];
+      int total;
+      const int incl = block_scan1_topk(mine, red + par * kTopkWaves, total);
+      int above = total - incl;
+      if (above < want && above + mine >= want) {
 #pragma unroll
-      for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g) {
-        if (g < groups) {
-          if (pass == 0 && g != groups - 1) {        // full groups: every slot counts
+        for (int b = 3; b >= 0; --b) {
+          if (above < want && above + h[b] >= want) {
+            found[par][0] = 4 * tid + b;
+            found[par][1] = want - above;
+            found[par][2] = h[b];
+          }
+          above += h[b];
+        }
+      }
+      __syncthreads();
+      digit = found[par][0];
+      left = found[par][1];
+      bin_n = found[par][2];
+    };
+    int d0, rem, c0;
+    // Pass 0 over every key: top 11 bits.
 #pragma unroll
-            for (int i = 0; i < kTopkGroup; ++i) atomicAdd(&hcopy[key[kTopkGroup * g + i] >> 21], 1u);
-          } else if (pass == 0) {                   // the last group: slots past the row have key 0
+    for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g) {
+      if (g < groups) {
+        if (g != groups - 1) {                       // full groups: every slot counts
 #pragma unroll
-            for (int i = 0; i < kTopkGroup; ++i) {
-              const uint32_t kv = key[kTopkGroup * g + i];
-              if (kv != 0u) atomicAdd(&hcopy[kv >> 21], 1u);
-            }
-          } else {
+          for (int i = 0; i < kTopkGroup; ++i) atomicAdd(&hcopy[key[kTopkGroup * g + i] >> 21], 1u);
+        } else {                                     // the last group: slots past the row have key 0
+#pragma unroll
+          for (int i = 0; i < kTopkGroup; ++i) {
+            const uint32_t kv = key[kTopkGroup * g + i];
+            if (kv != 0u) atomicAdd(&hcopy[kv >> 21], 1u);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    scan_find(std::integral_constant<int, kTopkCopies>{}, 0, take, d0, rem, c0);
+    uint32_t prefix = uint32_t(d0);
+    if (c0 <= kTopkListCap) {
+      // The keys of bin d0 (c0 of them, slots past the row excluded) into a
+      // list in the histogram copies past the first, at offsets from a scan of
+      // the per-thread counts; passes 1 and 2 then read the list and count into
+      // copy 0 alone.  The order of the list does not reach T or `need`.
+      uint32_t* const list = hist + kTopkHistStride;
+      int cnt = 0;
+#pragma unroll
+      for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g)
+        if (g < groups)
+#pragma unroll
+          for (int i = 0; i < kTopkGroup; ++i) {
+            const uint32_t kv = key[kTopkGroup * g + i];
+            cnt += (kv != 0u && (kv >> 21) == prefix) ? 1 : 0;
+          }
+      int c_all;
+      int at = block_scan1_topk(cnt, red + kTopkWaves, c_all) - cnt;
+#pragma unroll
+      for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g)
+        if (g < groups)
+#pragma unroll
+          for (int i = 0; i < kTopkGroup; ++i) {
+            const uint32_t kv = key[kTopkGroup * g + i];
+            if (kv != 0u && (kv >> 21) == prefix) list[at++] = kv;
+          }
+      __syncthreads();
+      int d1, d2, n1, n2;
+      for (int i = tid; i < c0; i += kTopkThreads) atomicAdd(&hist[(list[i] >> 10) & 2047u], 1u);
+      __syncthreads();
+      scan_find(std::integral_constant<int, 1>{}, 0, rem, d1, rem, n1);
+      prefix = (prefix << 11) | uint32_t(d1);
+      for (int i = tid; i < c0; i += kTopkThreads)
+        if ((list[i] >> 10) == prefix) atomicAdd(&hist[list[i] & 1023u], 1u);
+      __syncthreads();
+      scan_find(std::integral_constant<int, 1>{}, 1, rem, d2, rem, n2);
+      prefix = (prefix << 10) | uint32_t(d2);
+    } else {
+      // Passes 1 and 2 over every key again.
+#pragma unroll
+      for (int pass = 1; pass < 3; ++pass) {
+        const int shift = pass == 1 ? 10 : 0;
+        const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+        const int pshift = pass == 1 ? 21 : 10;      // bits below the digits already found
+#pragma unroll
+        for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g) {
+          if (g < groups) {
             // Four slots per test: a wave with no match in any of them skips
             // the four (the common case in the last pass).
 #pragma unroll
@@ -2672,38 +2759,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
             }
           }
         }
+        __syncthreads();
+        int d, nb;
+        scan_find(std::integral_constant<int, kTopkCopies>{}, pass & 1, rem, d, rem, nb);
+        prefix = (prefix << (pass == 2 ? 10 : 11)) | uint32_t(d);
       }
-      __syncthreads();
-      // Thread t owns bins 4t..4t+3; `above` counts the bins of the threads
-      // after it, i.e. the larger digits.
-      int h[4] = {0, 0, 0, 0};
-#pragma unroll
-      for (int c = 0; c < kTopkCopies; ++c) {
-        uint4* const w = reinterpret_cast<uint4*>(&hist[c * kTopkHistStride + 4 * tid]);
-        const uint4 q = *w;
-        *w = make_uint4(0u, 0u, 0u, 0u);
-        h[0] += int(q.x);
-        h[1] += int(q.y);
-        h[2] += int(q.z);
-        h[3] += int(q.w);
-      }
-      const int mine = h[0] + h[1] + h[2] + h[3];
-      int total;
-      const int incl = block_scan1_topk(mine, red + (pass & 1) * kTopkWaves, total);
-      int above = total - incl;
-      if (above < rem && above + mine >= rem) {
-#pragma unroll
-        for (int b = 3; b >= 0; --b) {
-          if (above < rem && above + h[b] >= rem) {
-            found[pass & 1][0] = 4 * tid + b;
-            found[pass & 1][1] = rem - above;
-          }
-          above += h[b];
-        }
-      }
-      __syncthreads();
-      prefix = (prefix << (pass == 2 ? 10 : 11)) | uint32_t(found[pass & 1][0]);
-      rem = found[pass & 1][1];
     }
     const uint32_t T = prefix;
     const int need = rem;                            // keys equal to T to take, largest positions first
