@@ -316,10 +316,15 @@ tig_status tig_moe_route(const void* H, const void* Wr, float* logits, int32_t* 
     return fail(TIG_ERR_INVALID_ARG, "logits, topk_ids or topk_w misaligned");
   if (T * int64_t(n_experts) >= (int64_t(1) << 40))
     return fail(TIG_ERR_UNSUPPORTED, "T * n_experts too large");
-  // The logits: the leaf-tree contraction with FP32 output, as tig_tree_gemm.
-  s = tig_tree_gemm(H, K, Wr, K, logits, n_experts, TIG_OUT_F32, T, n_experts, K, leaves, stream);
-  if (s != TIG_OK) return s;
-  const hipError_t e = tig::launch_moe_route(logits, T, n_experts, topk, topk_ids, topk_w, stream);
+  // Byte offsets inside the 64 router rows of a block are 32-bit.
+  if (64 * K * 2 >= (int64_t(1) << 32)) return fail(TIG_ERR_UNSUPPORTED, "K (%lld) too large", (long long)K);
+  // The logits: the leaf-tree contraction with FP32 output (the bits of tig_tree_gemm),
+  // on 32-token blocks.
+  int lg = 0;
+  while ((1 << lg) < leaves) ++lg;
+  hipError_t e = tig::launch_router_logits(H, Wr, logits, T, K, n_experts, lg, stream);
+  if (e != hipSuccess) return fail(TIG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+  e = tig::launch_moe_route(logits, T, n_experts, topk, topk_ids, topk_w, stream);
   if (e != hipSuccess) return fail(TIG_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
   return ok();
 }

@@ -223,6 +223,10 @@ hipError_t launch_topk_positions(const float* scores, int64_t ld, const int32_t*
 // Router, after its logits are computed: per token the topk largest logits
 // and their softmax gates.
 constexpr int kMaxRouteExperts = 1024;
+// The router's logits (FP32 leaf-tree contraction of H [T, K] and Wr [n_experts, K],
+// the same bits as the tree GEMM), on 32-token x 64-expert blocks.
+hipError_t launch_router_logits(const void* H, const void* Wr, float* logits, int64_t T, int64_t K,
+                                int n_experts, int leaves_log2, hipStream_t s);
 hipError_t launch_moe_route(const float* logits, int64_t T, int n_experts, int topk, int32_t* topk_ids,
                             float* topk_w, hipStream_t stream);
 

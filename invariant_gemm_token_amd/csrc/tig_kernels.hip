@@ -2374,6 +2374,52 @@ __device__ __forceinline__ int route_key(float v) {
 }
 
 // PER = candidates per lane: ceil(E / 64) rounded up to a power of two (<= 16).
+// Max of a 64-bit value over the wave, on every lane: rotations inside the
+// 16-lane rows (DPP), then rows 0 / 1 and 2 / 3 swapped (v_permlane16_swap)
+// and the wave halves swapped (v_permlane32_swap); the two 32-bit halves move
+// together.  No LDS.
+__device__ __forceinline__ int64_t wave_max_i64(int64_t x) {
+  auto halves_of = [](int64_t v, int& lo, int& hi) {
+    lo = int(uint32_t(uint64_t(v)));
+    hi = int(uint32_t(uint64_t(v) >> 32));
+  };
+  auto join = [](int lo, int hi) { return int64_t((uint64_t(uint32_t(hi)) << 32) | uint32_t(lo)); };
+  auto rot = [&](auto ctrl) {
+    int lo, hi;
+    halves_of(x, lo, hi);
+    constexpr int C = decltype(ctrl)::value;
+    const int64_t o = join(__builtin_amdgcn_mov_dpp(lo, C, 0xf, 0xf, true), __builtin_amdgcn_mov_dpp(hi, C, 0xf, 0xf, true));
+    x = o > x ? o : x;
+  };
+  rot(std::integral_constant<int, 0x121>{});   // row_ror:1
+  rot(std::integral_constant<int, 0x122>{});   // row_ror:2
+  rot(std::integral_constant<int, 0x124>{});   // row_ror:4
+  rot(std::integral_constant<int, 0x128>{});   // row_ror:8
+  auto swap = [&](auto wide) {
+    int lo, hi;
+    halves_of(x, lo, hi);
+    unsigned lo2 = unsigned(lo), hi2 = unsigned(hi);
+    // Second operands the compiler cannot equate with the first: with two equal
+    // operands it folds the swap away, although it exchanges rows.
+    asm volatile("" : "+v"(lo2), "+v"(hi2));
+    unsigned l0, l1, h0, h1;
+    if constexpr (decltype(wide)::value) {
+      const auto sl = __builtin_amdgcn_permlane32_swap(unsigned(lo), lo2, false, false);
+      const auto sh = __builtin_amdgcn_permlane32_swap(unsigned(hi), hi2, false, false);
+      l0 = sl[0]; l1 = sl[1]; h0 = sh[0]; h1 = sh[1];   // elements through scalars (see halves())
+    } else {
+      const auto sl = __builtin_amdgcn_permlane16_swap(unsigned(lo), lo2, false, false);
+      const auto sh = __builtin_amdgcn_permlane16_swap(unsigned(hi), hi2, false, false);
+      l0 = sl[0]; l1 = sl[1]; h0 = sh[0]; h1 = sh[1];
+    }
+    const int64_t a = join(int(l0), int(h0)), b = join(int(l1), int(h1));
+    x = a > b ? a : b;
+  };
+  swap(std::false_type{});
+  swap(std::true_type{});
+  return x;
+}
+
 template <int PER>
 __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict__ logits, int64_t T, int E,
                                                         int topk, int32_t* __restrict__ ids,
@@ -2399,17 +2445,14 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
     int64_t best = INT64_MIN;
 #pragma unroll
     for (int c = 0; c < ROUTE_PER_LANE; ++c) best = cand[c] > best ? cand[c] : best;
-#pragma unroll
-    for (int d = 1; d < 64; d *= 2) {
-      const int64_t o = __shfl_xor(best, d);
-      best = o > best ? o : best;
-    }
-    const int e = int(~uint32_t(uint64_t(best)));   // every lane: the winner
+    best = wave_max_i64(best);
+    // Every lane: the winner (uniform, so its lane is read with readlane).
+    const int e = __builtin_amdgcn_readfirstlane(int(~uint32_t(uint64_t(best))));
     float mine = 0.0f;
 #pragma unroll
     for (int c = 0; c < ROUTE_PER_LANE; ++c)
       if (c == (e >> 6)) mine = v[c];
-    const float ve = __shfl(mine, e & 63);
+    const float ve = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mine), e & 63));
     if (lane == (e & 63)) {
 #pragma unroll
       for (int c = 0; c < ROUTE_PER_LANE; ++c)
@@ -2433,7 +2476,148 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
   }
 }
 
+// Router logits, the leaf-tree contraction with FP32 output for the router's
+// shape (few experts): one workgroup per 32 tokens x 64 experts, so that
+// T / 32 workgroups share the work instead of T / 64 tiles of the persistent
+// kernel.  Wave w accumulates leaves w, w + 4, ...: the same
+// v_mfma_f32_32x32x16_bf16 k-steps, ascending from +0, with the same operand
+// layout (lane l: row l % 32, columns 8 (l / 32) .. +7 of the k-step) as the
+// tile kernels, so each leaf is the same FP32 block.  Each wave streams its
+// leaf through two 12 KiB stages of its own in LDS (64 columns of the 32
+// token rows and 64 expert rows; direct-to-LDS DMA of 8 rows x 128 bytes per
+// instruction, chunk c of row r at chunk c ^ ((r >> 1) & 7) as in the tile
+// kernels; rows past T or the expert count read as zero).  The leaves' blocks
+// stay in registers until every wave is done, then meet in LDS and fold by the
+// balanced adjacent-pair tree, left + right, as in the tile kernels.
+constexpr int kRouterStage = (32 + 64) * 128;   // bytes of one stage of one wave
+
+template <int LG>
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ H,
+                                                            const uint16_t* __restrict__ Wr,
+                                                            float* __restrict__ logits, int64_t T, int64_t K,
+                                                            int E) {
+  constexpr int L = 1 << LG;
+  constexpr int NL = L < 4 ? 1 : L / 4;   // leaves per wave (waves past L have none)
+  constexpr int STAGE_BYTES = 4 * 2 * kRouterStage;
+  constexpr int PART_BYTES = L * 32 * 64 * 4;
+  __shared__ __attribute__((aligned(1024))) char smem[STAGE_BYTES > PART_BYTES ? STAGE_BYTES : PART_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t t0 = int64_t(blockIdx.x) * 32;
+  const int e0 = int(blockIdx.y) * 64;
+  const int64_t trows = T - t0 < 32 ? T - t0 : 32;
+  const int erows = E - e0 < 64 ? E - e0 : 64;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(H + t0 * K, uint32_t(trows * K * 2));
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(Wr + int64_t(e0) * K, uint32_t(int64_t(erows) * K * 2));
+  // DMA lane offsets: instruction g loads rows 8 g .. 8 g + 7; lane i fills LDS
+  // chunk i % 8 of row 8 g + i / 8 with logical chunk (i % 8) ^ ((row >> 1) & 7).
+  // (row >> 1) & 7 = 4 (g & 1) + i / 16, so two offsets per operand cover every g.
+  const int rs = lane >> 3;
+  const uint32_t c0 = uint32_t(((lane & 7) ^ (rs >> 1)) << 4), c1 = c0 ^ 64u;
+  const uint32_t lo0 = uint32_t(int64_t(rs) * K * 2) + c0, lo1 = uint32_t(int64_t(rs) * K * 2) + c1;
+  const uint32_t gstride = uint32_t(8 * K * 2);   // 8 rows
+  // Fragment reads: row fr = lane % 32 of the operand, logical chunk 2 s + fk.
+  const int fr = lane & 31, fk = lane >> 5;
+  char* const mine = smem + wave * 2 * kRouterStage;
+  const int64_t kl = K >> LG;            // columns per leaf, a multiple of 64
+  const int nst = int(kl / 64);          // stages per leaf
+  const f32x16 z = {};
+  f32x16 acc[NL][2];
+  auto issue = [&](int buf, uint32_t kb) {   // one stage: 4 DMA of token rows, 8 of expert rows
+    char* const st = mine + buf * kRouterStage;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LDS_AS void*)(st + g * 1024), 16,
+                                               ((g & 1) ? lo1 : lo0) + uint32_t(g) * gstride, kb, 0, 0);
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LDS_AS void*)(st + 4096 + g * 1024), 16,
+                                               ((g & 1) ? lo1 : lo0) + uint32_t(g) * gstride, kb, 0, 0);
+  };
+#pragma unroll
+  for (int li = 0; li < NL; ++li) {
+    const int l = wave + 4 * li;
+    acc[li][0] = z;
+    acc[li][1] = z;
+    if (l < L) {
+      const uint32_t kb0 = uint32_t(int64_t(l) * kl * 2);
+      issue(0, kb0);
+      for (int st = 0; st < nst; ++st) {
+        const int buf = st & 1;
+        if (st + 1 < nst) {
+          issue(buf ^ 1, kb0 + uint32_t(st + 1) * 128);
+          wait_vmcnt<12>();   // stage st has landed (the 12 loads of stage st + 1 may be in flight)
+        } else {
+          wait_vmcnt<0>();
+        }
+        asm volatile("" ::: "memory");
+        const char* const sp = mine + buf * kRouterStage;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t ch = uint32_t(((2 * s + fk) ^ ((fr >> 1) & 7)) << 4);
+          const bf16x8 av = *reinterpret_cast<const bf16x8*>(sp + fr * 128 + ch);
+          const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(sp + 4096 + fr * 128 + ch);
+          const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(sp + 4096 + (32 + fr) * 128 + ch);
+          acc[li][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b0, acc[li][0], 0, 0, 0);
+          acc[li][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, b1, acc[li][1], 0, 0, 0);
+        }
+        // Every fragment read of this buffer has returned before its next DMA is issued.
+        wait_lgkm0();
+        asm volatile("" ::: "memory");
+      }
+    }
+  }
+  __syncthreads();   // every wave is done with its stages: the area takes the leaf blocks
+  float* const part = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int li = 0; li < NL; ++li) {
+    const int l = wave + 4 * li;
+    if (l < L) {
+      float* const pl = part + l * 32 * 64;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = (v >> 2) * 8 + fk * 4 + (v & 3);
+        const float x0 = acc[li][0][v], x1 = acc[li][1][v];
+        pl[row * 64 + fr] = x0;
+        pl[row * 64 + 32 + fr] = x1;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int o = tid + 256 * q, row = o >> 6, col = o & 63;
+    float p[L];
+#pragma unroll
+    for (int l = 0; l < L; ++l) p[l] = part[l * 32 * 64 + o];
+#pragma unroll
+    for (int w = 1; w < L; w *= 2)
+#pragma unroll
+      for (int j = 0; j + w < L; j += 2 * w) p[j] = p[j] + p[j + w];
+    if (t0 + row < T && e0 + col < E) logits[(t0 + row) * int64_t(E) + e0 + col] = p[0];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_router_logits(const void* H, const void* Wr, float* logits, int64_t T, int64_t K,
+                                int n_experts, int leaves_log2, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (n_experts < 1 || K < 64 || leaves_log2 < 0 || leaves_log2 > 4 || (K >> leaves_log2) % 64 != 0 ||
+      cdiv(T, 32) > 0x7FFFFFFF || 64 * K * 2 >= (int64_t(1) << 32))
+    return hipErrorInvalidValue;
+  const dim3 grid(unsigned(cdiv(T, 32)), unsigned(cdiv(n_experts, 64))), block(256);
+  const uint16_t* h = static_cast<const uint16_t*>(H);
+  const uint16_t* w = static_cast<const uint16_t*>(Wr);
+  switch (leaves_log2) {
+    case 0: hipLaunchKernelGGL(router_logits_kernel<0>, grid, block, 0, s, h, w, logits, T, K, n_experts); break;
+    case 1: hipLaunchKernelGGL(router_logits_kernel<1>, grid, block, 0, s, h, w, logits, T, K, n_experts); break;
+    case 2: hipLaunchKernelGGL(router_logits_kernel<2>, grid, block, 0, s, h, w, logits, T, K, n_experts); break;
+    case 3: hipLaunchKernelGGL(router_logits_kernel<3>, grid, block, 0, s, h, w, logits, T, K, n_experts); break;
+    default: hipLaunchKernelGGL(router_logits_kernel<4>, grid, block, 0, s, h, w, logits, T, K, n_experts); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_moe_route(const float* logits, int64_t T, int n_experts, int topk, int32_t* topk_ids,
                             float* topk_w, hipStream_t s) {

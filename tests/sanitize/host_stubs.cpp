@@ -28,6 +28,9 @@ hipError_t launch_silu_mul(const float*, int64_t, uint16_t*, int64_t, int64_t, i
 hipError_t launch_topk_positions(const float*, int64_t, const int32_t*, int64_t, int, int32_t*, hipStream_t) {
   return hipErrorNotSupported;
 }
+hipError_t launch_router_logits(const void*, const void*, float*, int64_t, int64_t, int, int, hipStream_t) {
+  return hipErrorNotSupported;
+}
 hipError_t launch_moe_route(const float*, int64_t, int, int, int32_t*, float*, hipStream_t) {
   return hipErrorNotSupported;
 }

@@ -124,3 +124,18 @@ def test_routed_moe_is_batch_invariant(gpu_lib):
     full = run(H)
     parts = torch.cat([run(H[i:i + 64].contiguous()) for i in range(0, T, 64)])
     assert_bitwise(parts, full, "router + MoE, 8 x 64 vs 512 tokens")
+
+
+@pytest.mark.parametrize("T,E,K,L", [(333, 16, 512, 1), (4096, 64, 2048, 8), (1000, 100, 1024, 2),
+                                     (77, 1024, 2048, 16), (4096, 64, 2048, 4), (50, 64, 4096, 8),
+                                     (129, 130, 768, 4)])
+def test_route_logits_equal_tree_gemm(gpu_lib, T, E, K, L):
+    """The router's logits are the leaf-tree contraction with FP32 output: bit for bit
+    what tig_tree_gemm gives for the same H and Wr (ragged T and E, 1 .. 16 leaves)."""
+    rng = np.random.default_rng(4242 + T + E + K + L)
+    H = dev_bf16(wl.normal_bf16(rng, (T, K), 1.0))
+    Wr = dev_bf16(wl.normal_bf16(rng, (E, K), 0.02))
+    logits, _, _ = gpu_lib.moe_route(H, Wr, min(8, E), L)
+    C = torch.empty(T, E, dtype=torch.float32, device="cuda:0")
+    gpu_lib.tig_tree_gemm(H, Wr, C, L)
+    assert_bitwise(logits, C, f"router logits vs tree GEMM T={T} E={E} K={K} L={L}")
