@@ -551,7 +551,7 @@ __device__ __forceinline__ void leaf_tree_persistent(Ld& ld, int ktiles, const T
   wait_vmcnt<0>();   // no LDS DMA may still be landing when the workgroup ends
 }
 
-// Epilogue: store the tile (FP32, or bf16 by RNE).
+// Epilogue: store the tile (FP32, or bf16 by RNE), with non-temporal stores.
 template <int EPI, int MI>
 struct StoreEpi {
   static constexpr bool kSplitTop = false;
@@ -654,10 +654,12 @@ __device__ __forceinline__ void StoreEpi<EPI, MI>::operator()(const AccT<MI>& ac
       for (int v = 0; v < 16; ++v) {
         const int64_t row = m0 + acc_row<MI>(wm, i, v, lane);
         if (row >= M) continue;
+        // Non-temporal: the output streams past the L2, where the operand
+        // tiles the workgroups of an XCD share stay resident.
         if (EPI == kEpiF32)
-          static_cast<float*>(C)[row * ldc + col] = acc.c[i][j][v];
+          __builtin_nontemporal_store(acc.c[i][j][v], &static_cast<float*>(C)[row * ldc + col]);
         else
-          static_cast<uint16_t*>(C)[row * ldc + col] = f32_to_bf16_rne(acc.c[i][j][v]);
+          __builtin_nontemporal_store(f32_to_bf16_rne(acc.c[i][j][v]), &static_cast<uint16_t*>(C)[row * ldc + col]);
       }
     }
 }
@@ -1592,7 +1594,7 @@ struct MoeStoreEpi {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int row = acc_row<MI>(wm, i, v, lane);
-          if (row < rows) C[int64_t(row) * op.N + col] = acc.c[i][j][v];
+          if (row < rows) __builtin_nontemporal_store(acc.c[i][j][v], &C[int64_t(row) * op.N + col]);   // as StoreEpi
         }
       }
   }
