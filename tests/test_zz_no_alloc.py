@@ -5,7 +5,8 @@ device array instead of a caller's workspace, so its outputs must be the same
 bits.  Two calls in a row, the second on fewer rows, check that the array's
 leftover contents from the first call do not leak into the second.  The
 16-leaf case with more than 128 rows takes the split-tree path, whose parked
-half trees also live in the array.
+half trees also live in the array.  The call is also captured in a graph and
+replayed, the use it exists for.
 """
 
 import numpy as np
@@ -56,3 +57,39 @@ def test_noalloc_rejects_calls_above_its_array(gpu_lib):
     with pytest.raises(tig.TigError) as e:
         tig.tig_logprob_gather_noalloc(big_H, big_W, big_ids, lp, None, 8)
     assert e.value.status == tig.TIG_ERR_UNSUPPORTED
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("K,V,leaves,M", [
+    (1024, 5000, 8, 300),       # several m-tiles, the sampled logit by its own kernel
+    (2048, 4097, 16, 150),      # 192-row tiles at 16 leaves: parked half trees in the array
+    (1024, 151936, 8, 128),     # one row of tiles: the sampled logit inside the tile kernel
+])
+def test_noalloc_graph_replays_match_eager(gpu_lib, K, V, leaves, M):
+    """The no-allocation call captured in a graph and replayed four times, with
+    eager work between the replays (the buffers cleared, and an eager call on
+    other rows that leaves its own data in the device array): every replay gives
+    the eager call's bits."""
+    tig = gpu_lib
+    say(f"noalloc graph K={K} V={V} leaves={leaves} M={M}")
+    H, W, ids = _inputs(5151 + leaves, 2 * M, K, V)
+    Hm, idm = H[:M].contiguous(), ids[:M].contiguous()
+    ref_lp = torch.empty(M, dtype=torch.float32, device="cuda:0")
+    ref_lse = torch.empty_like(ref_lp)
+    tig.tig_logprob_gather_noalloc(Hm, W, idm, ref_lp, ref_lse, leaves)   # first call on the device: eager
+    torch.cuda.synchronize()
+    lp = torch.empty_like(ref_lp)
+    lse = torch.empty_like(ref_lp)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        tig.tig_logprob_gather_noalloc(Hm, W, idm, lp, lse, leaves)
+    other_lp = torch.empty(M, dtype=torch.float32, device="cuda:0")
+    for rep in range(4):
+        lp.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        tig.tig_logprob_gather_noalloc(H[M:].contiguous(), W, ids[M:].contiguous(), other_lp, None, leaves)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_bitwise(lp, ref_lp, f"graph replay {rep} logprob")
+        assert_bitwise(lse, ref_lse, f"graph replay {rep} lse")
