@@ -13,8 +13,11 @@ K = 512, 8 leaves.  Up to 192 rows a call has a single row of tiles (the sampled
 logit picked inside the tile kernel); above, 128- and 192-row tiles alternate
 as M grows, and at 16 leaves the 192-row tiles park the first half of the leaf
 tree outside registers.  The 16-leaf contraction (K = 2048, N = 1024) is swept
-over every M from 1 to 1024 (64- and 128-row tiles).  Comparisons run on the
-device.
+over every M from 1 to 1024 (64- and 128-row tiles).  The block-FP8 path
+(per-token quantisation of the first M rows, then the W8A8 contraction, FP32
+and bf16 outputs), the MoE contraction + combine and the router (logits,
+chosen experts, gates) are swept over every batch size up to 600 or 300 rows.
+Comparisons run on the device.
 """
 
 import numpy as np
@@ -108,3 +111,82 @@ def test_tree_gemm_16_leaves_every_M_1_to_1024(gpu_lib):
                 break
     torch.cuda.synchronize()
     assert not bad, f"rows differ from the 1024-row call at (M, (row, col)): {bad}"
+
+
+@pytest.mark.parametrize("K,N,L,bf16", [(2048, 640, 8, False), (2048, 400, 16, True)])
+def test_fp8_every_M_1_to_600(gpu_lib, K, N, L, bf16):
+    """Quantise + W8A8 contraction of the first M rows, every M: the per-token
+    activation blocks and the per-call scale table (sized by M) may not change
+    a row's bits."""
+    Mmax = 600
+    rng = np.random.default_rng(31000 + N + L)
+    A = dev_bf16(wl.normal_bf16(rng, (Mmax, K), 1.0))
+    QW, SW = gpu_lib.fp8_quantize(dev_bf16(wl.normal_bf16(rng, (N, K), 0.02)), 128)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    QA, SA = gpu_lib.fp8_quantize(A, 1)
+    full = gpu_lib.fp8_tree_gemm(QA, SA, QW, SW, L, out_dtype=dt)
+    view = torch.int16 if bf16 else torch.int32
+    bad = []
+    for M in range(1, Mmax + 1):
+        if M % 100 == 1:
+            say(f"fp8 every M (K={K} N={N} L={L} bf16={bf16}): M = {M} ..")
+        qa, sa = gpu_lib.fp8_quantize(A[:M], 1)
+        C = gpu_lib.fp8_tree_gemm(qa, sa, QW, SW, L, out_dtype=dt)
+        ne = C.view(view) != full[:M].view(view)
+        if bool(ne.any()):
+            bad.append((M, tuple(int(i) for i in ne.nonzero()[0])))
+            if len(bad) >= 5:
+                break
+    torch.cuda.synchronize()
+    assert not bad, f"rows differ from the 600-row call at (M, (row, col)): {bad}"
+
+
+def test_moe_every_T_1_to_300(gpu_lib):
+    """The MoE contraction + combine of the first T tokens, every T: a token's
+    output may not depend on how many tokens (and so how many rows per expert)
+    share the call."""
+    T, E, N, K, topk, L = 300, 16, 384, 1024, 4, 8
+    rng = np.random.default_rng(32000)
+    H = dev_bf16(wl.normal_bf16(rng, (T, K), 1.0))
+    We = dev_bf16(wl.normal_bf16(rng, (E, N, K), 0.02))
+    ids, w = wl.routing_input(rng, T, E, topk)
+    ids, w = torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda()
+    full = gpu_lib.moe_tree_gemm_combine(H, We, ids, w, L)
+    ws = torch.empty(gpu_lib.tig_moe_workspace_bytes(T, N, K, E, topk), dtype=torch.uint8, device="cuda:0")
+    out = torch.empty_like(full)
+    bad = []
+    for t in range(1, T + 1):
+        if t % 50 == 1:
+            say(f"moe every T: T = {t} ..")
+        gpu_lib.tig_moe_tree_gemm_combine(H[:t], We, ids[:t], w[:t], out[:t], L, ws)
+        where = _first_mismatch(out[:t], full[:t])
+        if where is not None:
+            bad.append((t, where))
+            if len(bad) >= 5:
+                break
+    torch.cuda.synchronize()
+    assert not bad, f"tokens differ from the 300-token call at (T, (token, col)): {bad}"
+
+
+@pytest.mark.parametrize("E,topk", [(64, 8), (100, 6)])
+def test_router_every_T_1_to_300(gpu_lib, E, topk):
+    """Router logits, chosen experts and gates of the first T tokens, every T."""
+    T, K, L = 300, 2048, 8
+    rng = np.random.default_rng(33000 + E)
+    H = dev_bf16(wl.normal_bf16(rng, (T, K), 1.0))
+    Wr = dev_bf16(wl.normal_bf16(rng, (E, K), 0.02))
+    f_lg, f_ids, f_w = gpu_lib.moe_route(H, Wr, topk, L)
+    bad = []
+    for t in range(1, T + 1):
+        if t % 50 == 1:
+            say(f"router every T (E={E} top-{topk}): T = {t} ..")
+        lg, ids, w = gpu_lib.moe_route(H[:t], Wr, topk, L)
+        for name, got, ref in (("logits", lg.view(torch.int32), f_lg[:t].view(torch.int32)),
+                               ("ids", ids, f_ids[:t]), ("gates", w.view(torch.int32), f_w[:t].view(torch.int32))):
+            ne = got != ref
+            if bool(ne.any()):
+                bad.append((name, t, tuple(int(i) for i in ne.nonzero()[0])))
+        if len(bad) >= 5:
+            break
+    torch.cuda.synchronize()
+    assert not bad, f"tokens differ from the 300-token call: {bad}"
