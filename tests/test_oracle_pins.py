@@ -94,6 +94,19 @@ def test_bf16_rounding_of_generator_is_nearest_even():
     assert [int(v) for v in got] == exp
 
 
+def test_sign_generator_gives_signed_powers_of_two():
+    rng = np.random.default_rng(8)
+    for e in (0, -12, 5):
+        v = oracle.bf16_bits_to_f64(wl.sign_bf16(rng, (3, 700), e, chunk=257))
+        assert np.all(np.abs(v) == 2.0 ** e)
+        frac = np.mean(v > 0)
+        assert 0.4 < frac < 0.6
+    # the stream does not depend on the chunk size
+    a = wl.sign_bf16(np.random.default_rng(9), (1000,), 0, chunk=1 << 24)
+    b = wl.sign_bf16(np.random.default_rng(9), (1000,), 0, chunk=130)
+    assert np.array_equal(a, b)
+
+
 # ---------------------------------------------------------------------------
 # P1: brute force on tiny inputs with exact rational arithmetic
 # ---------------------------------------------------------------------------

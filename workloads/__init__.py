@@ -103,6 +103,28 @@ def integer_bf16(rng: np.random.Generator, shape, lo: int, hi: int) -> np.ndarra
     return f32_to_bf16_bits(v)
 
 
+def sign_bf16(rng: np.random.Generator, shape, exp2: int = 0, chunk: int = 1 << 24) -> np.ndarray:
+    """Uniform random signs times ``2**exp2`` as bf16 bit patterns (uint16).
+
+    Element i takes its sign from bit i (least significant first) of the raw
+    64-bit outputs of ``rng``'s bit generator, so the values do not depend on
+    the chunk size, which only bounds memory (rounded up to a multiple of 64).
+    """
+    if not -126 <= exp2 <= 127:
+        raise ValueError("exp2 must give a normal bf16 power of two")
+    n = int(np.prod(shape))
+    chunk = -(-max(int(chunk), 64) // 64) * 64
+    out = np.empty(n, dtype=np.uint16)
+    mag = np.uint16((exp2 + 127) << 7)
+    for i in range(0, n, chunk):
+        j = min(n, i + chunk)
+        words = rng.bit_generator.random_raw(-(-(j - i) // 64)).astype("<u8")
+        bits = np.unpackbits(words.view(np.uint8), bitorder="little")[:j - i]
+        out[i:j] = bits.astype(np.uint16) << 15
+        out[i:j] |= mag
+    return out.reshape(shape)
+
+
 @dataclass(frozen=True)
 class Config:
     """One workload: sizes, leaf count and seed."""
