@@ -34,6 +34,11 @@ line carries:
 Inputs are seeded and synthetic (workloads: bf16 N(0,1) activations,
 N(0,0.02) weights, uniform sampled ids, top-8 routing of N(0,1) router
 logits); a kernel's cost does not depend on the values.
+
+The headline runs exactly --warmup untimed steps before its --steps timed ones.
+Every other line first calls its kernel back to back for at least 200 ms, so
+that it is not timed while the GPU clock comes back from an idle spell (input
+generation, the CPU baseline).
 """
 
 from __future__ import annotations
@@ -50,6 +55,7 @@ if ROOT not in sys.path:
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+AUX_WARM_MS = 200.0         # back-to-back calls before each line other than the headline
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix-core peak
 
 
@@ -126,12 +132,29 @@ def main():
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    def timed(fn, steps, warmup, per_call=False):
+    def settle(fn, warm_ms):
+        """Call fn back to back for at least warm_ms of wall time: after an idle spell
+        (input generation, the CPU baseline) the GPU clock needs tens of ms to come back,
+        and a short line timed right away measures part of that ramp."""
+        import time
+        if warm_ms <= 0:
+            return
+        t0 = time.perf_counter()
+        while True:
+            for _ in range(8):
+                fn()
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= warm_ms:
+                return
+
+    def timed(fn, steps, warmup, per_call=False, warm_ms=AUX_WARM_MS):
         """Mean ms per call over `steps` calls (events on the launch stream), and with
         per_call the time of each call (an event between calls: fine for long calls, an
-        overhead of its own for short ones)."""
+        overhead of its own for short ones).  `warmup` calls, then at least warm_ms of
+        calls, go first."""
         for _ in range(warmup):
             fn()
+        settle(fn, warm_ms)
         torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_call else 2)]
         ev[0].record(stream)
@@ -144,7 +167,7 @@ def main():
         per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)] if per_call else []
         return ev[0].elapsed_time(ev[-1]) / steps, per
 
-    def device_timed(fn, steps, warmup):
+    def device_timed(fn, steps, warmup, warm_ms=AUX_WARM_MS):
         """Device time per call of a short call: the calls are queued behind a sleep
         kernel, so the events bracket only GPU work, not the host's time to issue each
         call through the Python binding.  Returns (ms per call, ms per call as issued
@@ -152,6 +175,7 @@ def main():
         import time
         for _ in range(warmup):
             fn()
+        settle(fn, warm_ms)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -169,7 +193,7 @@ def main():
         # The GPU never waited for the host if issuing all calls took less time than
         # the sleep plus the calls themselves took on the GPU.
         ahead = t_issue * 1e3 < s0.elapsed_time(s1) + dev_ms * steps
-        host_ms, _ = timed(fn, steps, 0)
+        host_ms, _ = timed(fn, steps, 0, warm_ms=0)
         return dev_ms, host_ms, ahead
 
     def mfma_line(flops, ms):
@@ -247,7 +271,7 @@ def main():
         # Attainable HBM rate on this machine: a 1 GiB device-to-device copy (bytes read + written).
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        copy_ms, _ = timed(lambda: dst.copy_(src), 10, 2)
+        copy_ms, _ = timed(lambda: dst.copy_(src), 10, 2, warm_ms=0)
         copy_gbs = 2.0 * (1 << 30) / (copy_ms / 1e3) / 1e9
         log(f"device copy: {copy_gbs:.0f} GB/s (read + write)")
         del src, dst
@@ -256,8 +280,9 @@ def main():
     spread = None
     flops = 2.0 * M * K * V
     if args.phase in ("all", "prefill"):
+        # The headline: exactly args.warmup untimed steps, then args.steps timed ones.
         ms_step, per_call = timed(lambda: tig.tig_logprob_gather(Hd, Wd, idd, lp, lse, L, ws),
-                                  args.steps, args.warmup, per_call=True)
+                                  args.steps, args.warmup, per_call=True, warm_ms=0)
         tok_s = M / (ms_step / 1e3)
         tflops = flops / (float(np.mean(per_call)) / 1e3) / 1e12
         spread = {"min_ms": float(np.min(per_call)), "median_ms": float(np.median(per_call)),
