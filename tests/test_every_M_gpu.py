@@ -16,8 +16,9 @@ tree outside registers.  The 16-leaf contraction (K = 2048, N = 1024) is swept
 over every M from 1 to 1024 (64- and 128-row tiles).  The block-FP8 path
 (per-token quantisation of the first M rows, then the W8A8 contraction, FP32
 and bf16 outputs), the MoE contraction + combine and the router (logits,
-chosen experts, gates) are swept over every batch size up to 600 or 300 rows.
-Comparisons run on the device.
+chosen experts, gates) are swept over every batch size up to 600 or 300 rows,
+and the expert GEMMs over every row count 1 .. 400 of one expert, in both
+layouts.  Comparisons run on the device.
 """
 
 import numpy as np
@@ -141,12 +142,13 @@ def test_fp8_every_M_1_to_600(gpu_lib, K, N, L, bf16):
     assert not bad, f"rows differ from the 600-row call at (M, (row, col)): {bad}"
 
 
-def test_moe_every_T_1_to_300(gpu_lib):
+@pytest.mark.parametrize("L", [8, 16])
+def test_moe_every_T_1_to_300(gpu_lib, L):
     """The MoE contraction + combine of the first T tokens, every T: a token's
     output may not depend on how many tokens (and so how many rows per expert)
     share the call."""
-    T, E, N, K, topk, L = 300, 16, 384, 1024, 4, 8
-    rng = np.random.default_rng(32000)
+    T, E, N, K, topk = 300, 16, 384, 1024, 4
+    rng = np.random.default_rng(32000 + L)
     H = dev_bf16(wl.normal_bf16(rng, (T, K), 1.0))
     We = dev_bf16(wl.normal_bf16(rng, (E, N, K), 0.02))
     ids, w = wl.routing_input(rng, T, E, topk)
@@ -157,7 +159,7 @@ def test_moe_every_T_1_to_300(gpu_lib):
     bad = []
     for t in range(1, T + 1):
         if t % 50 == 1:
-            say(f"moe every T: T = {t} ..")
+            say(f"moe every T ({L} leaves): T = {t} ..")
         gpu_lib.tig_moe_tree_gemm_combine(H[:t], We, ids[:t], w[:t], out[:t], L, ws)
         where = _first_mismatch(out[:t], full[:t])
         if where is not None:
@@ -168,18 +170,18 @@ def test_moe_every_T_1_to_300(gpu_lib):
     assert not bad, f"tokens differ from the 300-token call at (T, (token, col)): {bad}"
 
 
-@pytest.mark.parametrize("E,topk", [(64, 8), (100, 6)])
-def test_router_every_T_1_to_300(gpu_lib, E, topk):
+@pytest.mark.parametrize("E,topk,L", [(64, 8, 8), (100, 6, 8), (64, 8, 16)])
+def test_router_every_T_1_to_300(gpu_lib, E, topk, L):
     """Router logits, chosen experts and gates of the first T tokens, every T."""
-    T, K, L = 300, 2048, 8
-    rng = np.random.default_rng(33000 + E)
+    T, K = 300, 2048
+    rng = np.random.default_rng(33000 + E + L)
     H = dev_bf16(wl.normal_bf16(rng, (T, K), 1.0))
     Wr = dev_bf16(wl.normal_bf16(rng, (E, K), 0.02))
     f_lg, f_ids, f_w = gpu_lib.moe_route(H, Wr, topk, L)
     bad = []
     for t in range(1, T + 1):
         if t % 50 == 1:
-            say(f"router every T (E={E} top-{topk}): T = {t} ..")
+            say(f"router every T (E={E} top-{topk}, {L} leaves): T = {t} ..")
         lg, ids, w = gpu_lib.moe_route(H[:t], Wr, topk, L)
         for name, got, ref in (("logits", lg.view(torch.int32), f_lg[:t].view(torch.int32)),
                                ("ids", ids, f_ids[:t]), ("gates", w.view(torch.int32), f_w[:t].view(torch.int32))):
@@ -190,3 +192,45 @@ def test_router_every_T_1_to_300(gpu_lib, E, topk):
             break
     torch.cuda.synchronize()
     assert not bad, f"tokens differ from the 300-token call: {bad}"
+
+
+@pytest.mark.parametrize("L", [8, 16])
+def test_expert_gemm_every_count_1_to_400(gpu_lib, L):
+    """Expert GEMMs with expert 1 holding c rows, every c: its rows keep their bits
+    as c grows (one tile row, several, ragged last tiles), in the masked layout and
+    in the contiguous one (where expert 2's block moves with c), and experts 0 and
+    2 are unchanged."""
+    E, K, N, cap, align = 3, 1024, 320, 400, 128
+    rng = np.random.default_rng(34000 + L)
+    X = dev_bf16(wl.normal_bf16(rng, (E, cap, K), 1.0))
+    W = dev_bf16(wl.normal_bf16(rng, (E, N, K), 0.02))
+    fixed = (37, 150)
+    full = gpu_lib.expert_gemm_masked(X, torch.tensor([fixed[0], cap, fixed[1]], dtype=torch.int32,
+                                                       device="cuda:0"), W, L)
+    up = lambda n: -(-n // align) * align
+    bad = []
+    for c in range(1, cap + 1):
+        if c % 100 == 1:
+            say(f"expert gemm every count ({L} leaves): c = {c} ..")
+        counts = torch.tensor([fixed[0], c, fixed[1]], dtype=torch.int32, device="cuda:0")
+        Ym = gpu_lib.expert_gemm_masked(X, counts, W, L)
+        s1 = up(fixed[0])
+        s2 = s1 + up(c)
+        Xc = torch.zeros(s2 + fixed[1] + 5, K, dtype=torch.bfloat16, device="cuda:0")
+        Xc[:fixed[0]] = X[0, :fixed[0]]
+        Xc[s1:s1 + c] = X[1, :c]
+        Xc[s2:s2 + fixed[1]] = X[2, :fixed[1]]
+        Yc = gpu_lib.expert_gemm_contiguous(Xc, counts, W, align, L)
+        pieces = (("masked expert 1", Ym[1, :c], full[1, :c]),
+                  ("masked expert 0", Ym[0, :fixed[0]], full[0, :fixed[0]]),
+                  ("masked expert 2", Ym[2, :fixed[1]], full[2, :fixed[1]]),
+                  ("contiguous expert 1", Yc[s1:s1 + c], full[1, :c]),
+                  ("contiguous expert 2", Yc[s2:s2 + fixed[1]], full[2, :fixed[1]]))
+        for name, got, ref in pieces:
+            where = _first_mismatch(got, ref)
+            if where is not None:
+                bad.append((name, c, where))
+        if len(bad) >= 5:
+            break
+    torch.cuda.synchronize()
+    assert not bad, f"rows differ from the full-count call: {bad}"
