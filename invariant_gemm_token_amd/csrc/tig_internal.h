@@ -216,7 +216,7 @@ hipError_t launch_silu_mul(const float* GU, int64_t ldgu, uint16_t* out, int64_t
                            hipStream_t stream);
 // Deterministic Top-K of positions: one workgroup of kTopkThreads per row,
 // kTopkPerThread scores per thread in registers.
-constexpr int kTopkThreads = 512, kTopkPerThread = 128;
+constexpr int kTopkThreads = 1024, kTopkPerThread = 64;
 constexpr int64_t kTopkMaxLen = int64_t(kTopkThreads) * kTopkPerThread;
 hipError_t launch_topk_positions(const float* scores, int64_t ld, const int32_t* lengths, int64_t R, int k,
                                  int32_t* out, hipStream_t stream);

@@ -2647,8 +2647,10 @@ hipError_t launch_moe_route(const float* logits, int64_t T, int n_experts, int t
 // scores go to the larger position; +0 equals -0, NaN below every number.
 // The selected positions are written by descending position, then -1.
 //
-// One workgroup of 512 threads per row.  Slot j of thread t holds position
-// n-1-(512j+t): each load instruction of a wave reads 64 consecutive scores,
+// One workgroup of 1024 threads per row (four waves per SIMD: the per-key
+// phases are chains of dependent vector instructions, which more waves
+// overlap).  Slot j of thread t holds position n-1-(1024j+t): each load
+// instruction of a wave reads 64 consecutive scores,
 // and (slot, wave, lane) order is descending position order.  The threshold
 // T, the take-th largest 32-bit score key, is found by a radix select over
 // LDS histograms of 11, 11 and 10 bits: each pass counts the keys that share
@@ -2667,6 +2669,8 @@ constexpr int kTopkGroup = 16;                       // slots loaded and tested 
 constexpr int kTopkCopies = 8;                       // histogram copies, by lane % 8
 constexpr int kTopkHistStride = 2048 + 4;            // words from one copy to the next (4 banks on)
 constexpr int kTopkBlocks = kTopkPerThread * kTopkWaves;   // 64-position blocks of the longest row
+static_assert(kTopkThreads * 4 >= 2048, "every bin of an 11-bit histogram has an owner in the scan");
+static_assert(2 * kTopkThreads * 8 <= kTopkCopies * kTopkHistStride * 4, "the blocks' offsets fit the histograms");
 // Keys of the first pass's threshold bin that the last two passes can take
 // from a list in LDS (the histogram copies past the first): more fall back to
 // scanning every key again.
@@ -2834,15 +2838,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
     auto scan_find = [&](auto ncop, int par, int want, int& digit, int& left, int& bin_n) {
       constexpr int NCOP = decltype(ncop)::value;
       int h[4] = {0, 0, 0, 0};
+      if (tid < 2048 / 4) {                          // the 2048 bins' owners; the other threads add 0
 #pragma unroll
-      for (int c = 0; c < NCOP; ++c) {
-        uint4* const w = reinterpret_cast<uint4*>(&hist[c * kTopkHistStride + 4 * tid]);
-        const uint4 q = *w;
-        *w = make_uint4(0u, 0u, 0u, 0u);
-        h[0] += int(q.x);
-        h[1] += int(q.y);
-        h[2] += int(q.z);
-        h[3] += int(q.w);
+        for (int c = 0; c < NCOP; ++c) {
+          uint4* const w = reinterpret_cast<uint4*>(&hist[c * kTopkHistStride + 4 * tid]);
+          const uint4 q = *w;
+          *w = make_uint4(0u, 0u, 0u, 0u);
+          h[0] += int(q.x);
+          h[1] += int(q.y);
+          h[2] += int(q.z);
+          h[3] += int(q.w);
+        }
       }
       const int mine = h[0] + h[1] + h[2] + h[3];
       int total;
@@ -2971,8 +2977,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
       }
     }
     __syncthreads();
-    // Blocks e = slot * 8 + wave (64 positions each, descending) in order;
-    // thread t scans blocks 2t and 2t+1.  Blocks of groups past the row are 0.
+    // Blocks e = slot * waves + wave (64 positions each, descending) in order;
+    // thread t scans blocks 2t and 2t+1.  Blocks past the row's groups count 0.
     const int used = groups * kTopkGroup * kTopkWaves;
     int pg[2], pq[2];
 #pragma unroll
@@ -2996,7 +3002,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
     // Output: a selected position's offset is the number of selected positions
     // above it, = (keys > T above it) + min(need, ties above it).  Quarter
     // u = 4e + c holds positions 16c .. 16c+15 of block e; thread t writes the
-    // quarters t, t + 512, ...  The stores go through a buffer over the row's
+    // quarters t, t + 1024, ...  The stores go through a buffer over the row's
     // k outputs, so even an offset out of range could not write outside them.
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(o, uint32_t(k) * 4u);
     uint4 mu[kTopkPerThread / 16];
