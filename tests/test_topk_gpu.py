@@ -138,16 +138,17 @@ def test_topk_indexer_config(gpu_lib):
 
 
 def test_topk_threshold_bin_beyond_the_list(gpu_lib):
-    """Rows whose threshold lies in one 11-bit key bin holding more keys than the
-    LDS list of the last two passes takes (14364): they scan every key again.
-    Floats in [1, 1.25) share sign, exponent and the top two mantissa bits, so
-    every key of such a row falls in one first-pass bin; lengths straddle the
-    list's size."""
+    """Rows whose threshold lies in one first-pass key bin holding more keys than
+    the LDS list of the last two passes takes (14364): they scan every key again.
+    Floats in [1, 1 + 2^-4) share sign, exponent and the top four mantissa
+    bits, so every key of such a row falls in one bin of the first digit (the
+    key's top 11 bits); lengths straddle the list's size, and reach past it by
+    10000 and more."""
     rng = np.random.default_rng(7200)
-    R, ld, k = 8, 65536, 2048
-    mant = rng.integers(0, 1 << 21, size=(R, ld)).astype(np.uint32)
+    R, ld, k = 10, 65536, 2048
+    mant = rng.integers(0, 1 << 19, size=(R, ld)).astype(np.uint32)
     scores = (np.uint32(0x3F800000) | mant).view(np.float32)
     scores[1] = 1.0                                  # one key everywhere: ties by position
     scores[2, ::2] = 2.0                             # half the row in a higher bin, all equal
-    lengths = np.array([ld, ld, ld, 20000, 14365, 14364, 30000, 65535], dtype=np.int32)
+    lengths = np.array([ld, ld, ld, 20000, 14365, 14364, 24589, 24588, 30000, 65535], dtype=np.int32)
     _check(gpu_lib, scores, lengths, k, "one dense bin")
