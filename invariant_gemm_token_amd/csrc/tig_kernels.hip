@@ -1809,25 +1809,52 @@ __device__ __forceinline__ float silu_f32(float g) {
   return g * s;
 }
 
-__global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__ GU, int64_t ldgu,
-                                                       uint16_t* __restrict__ out, int64_t ldo, int64_t rows,
-                                                       int64_t I, bool vec) {
-  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
-  const float* g = GU + r * ldgu;
-  const float* u = g + I;
-  uint16_t* o = out + r * ldo;
-  for (int64_t c = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4; c < I; c += int64_t(gridDim.x) * 1024) {
-    if (vec) {
-      const float4 gv = *reinterpret_cast<const float4*>(g + c), uv = *reinterpret_cast<const float4*>(u + c);
-      const uint32_t lo = uint32_t(f32_to_bf16_rne(silu_f32(gv.x) * uv.x)) |
-                          (uint32_t(f32_to_bf16_rne(silu_f32(gv.y) * uv.y)) << 16);
-      const uint32_t hi = uint32_t(f32_to_bf16_rne(silu_f32(gv.z) * uv.z)) |
-                          (uint32_t(f32_to_bf16_rne(silu_f32(gv.w) * uv.w)) << 16);
-      *reinterpret_cast<uint2*>(o + c) = make_uint2(lo, hi);
-    } else {
-      for (int64_t j = c; j < c + 4 && j < I; ++j) o[j] = f32_to_bf16_rne(silu_f32(g[j]) * u[j]);
+// Vectorised path: the (row, 4-column chunk) pairs of the call in one flat
+// range, four per thread per round (loads of all four first), so that a
+// workgroup streams 32 KiB instead of one row's few KiB.
+__global__ __launch_bounds__(256) void silu_mul_vec_kernel(const float* __restrict__ GU, int64_t ldgu,
+                                                           uint16_t* __restrict__ out, int64_t ldo, uint32_t rows,
+                                                           uint32_t q) {
+  constexpr int U = 4;
+  const uint32_t total = rows * q;                     // < 2^31, checked by the launcher
+  const uint32_t step = gridDim.x * 256u * U;
+  for (uint32_t base = blockIdx.x * 256u * U + threadIdx.x; base < total; base += step) {
+    float4 gv[U], uv[U];
+    uint32_t rr[U], cc[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const uint32_t idx = base + 256u * k;
+      rr[k] = idx / q;
+      cc[k] = (idx - rr[k] * q) * 4u;
+      if (idx < total) {
+        const float* g = GU + int64_t(rr[k]) * ldgu + cc[k];
+        gv[k] = *reinterpret_cast<const float4*>(g);
+        uv[k] = *reinterpret_cast<const float4*>(g + int64_t(q) * 4);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      if (base + 256u * k < total) {
+        const uint32_t lo = uint32_t(f32_to_bf16_rne(silu_f32(gv[k].x) * uv[k].x)) |
+                            (uint32_t(f32_to_bf16_rne(silu_f32(gv[k].y) * uv[k].y)) << 16);
+        const uint32_t hi = uint32_t(f32_to_bf16_rne(silu_f32(gv[k].z) * uv[k].z)) |
+                            (uint32_t(f32_to_bf16_rne(silu_f32(gv[k].w) * uv[k].w)) << 16);
+        *reinterpret_cast<uint2*>(out + int64_t(rr[k]) * ldo + cc[k]) = make_uint2(lo, hi);
+      }
     }
   }
+}
+
+// Any widths and alignments: one element at a time, rows across the grid.
+__global__ __launch_bounds__(256) void silu_mul_kernel(const float* __restrict__ GU, int64_t ldgu,
+                                                       uint16_t* __restrict__ out, int64_t ldo, int64_t rows,
+                                                       int64_t I) {
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+    const float* g = GU + r * ldgu;
+    const float* u = g + I;
+    uint16_t* o = out + r * ldo;
+    for (int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x; c < I; c += int64_t(gridDim.x) * 256)
+      o[c] = f32_to_bf16_rne(silu_f32(g[c]) * u[c]);
   }
 }
 
@@ -3159,11 +3186,17 @@ hipError_t launch_silu_mul(const float* GU, int64_t ldgu, uint16_t* out, int64_t
                            hipStream_t s) {
   if (rows <= 0 || I <= 0) return hipSuccess;
   const bool vec = I % 4 == 0 && ldgu % 4 == 0 && ldo % 4 == 0 && (reinterpret_cast<uintptr_t>(GU) & 15) == 0 &&
-                   (reinterpret_cast<uintptr_t>(out) & 7) == 0;
-  const int64_t cx = cdiv(I, 1024);
-  hipLaunchKernelGGL(silu_mul_kernel, dim3(unsigned(cx < 64 ? cx : 64), unsigned(rows < 65535 ? rows : 65535)),
-                     dim3(256), 0, s, GU, ldgu,
-                     out, ldo, rows, I, vec);
+                   (reinterpret_cast<uintptr_t>(out) & 7) == 0 && rows * (I / 4) < (int64_t(1) << 31);
+  if (vec) {
+    const int64_t total = rows * (I / 4);
+    const int64_t wgs = cdiv(total, 256 * 4);
+    hipLaunchKernelGGL(silu_mul_vec_kernel, dim3(unsigned(wgs < 65536 ? wgs : 65536)), dim3(256), 0, s, GU, ldgu,
+                       out, ldo, uint32_t(rows), uint32_t(I / 4));
+  } else {
+    const int64_t cx = cdiv(I, 256);
+    hipLaunchKernelGGL(silu_mul_kernel, dim3(unsigned(cx < 64 ? cx : 64), unsigned(rows < 65535 ? rows : 65535)),
+                       dim3(256), 0, s, GU, ldgu, out, ldo, rows, I);
+  }
   return hipGetLastError();
 }
 
