@@ -18,6 +18,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtig.so")
+# A C99 client of the ABI (tests/c_abi), linked against the library: the GPU
+# tests run it as a program of its own.
+CLIENT_SRC = os.path.join(ROOT, "tests", "c_abi", "tig_c_client.c")
+CLIENT = os.path.join(ROOT, "tests", "c_abi", "tig_c_client")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
@@ -45,7 +49,8 @@ def _run(cmd, verbose):
 
 
 def build(verbose: bool = False) -> str:
-    """Compile the kernels and the C ABI into ``invariant_gemm_token_amd/libtig.so``."""
+    """Compile the kernels and the C ABI into ``invariant_gemm_token_amd/libtig.so``, and
+    the C client of the ABI into ``tests/c_abi/tig_c_client``."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     inc = [f"-I{INCLUDE}", f"-I{CSRC}"]
     kobj = os.path.join(BUILD_DIR, "tig_kernels.o")
@@ -56,6 +61,12 @@ def build(verbose: bool = False) -> str:
     _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, kobj, hobj,
           f"-L{ROCM}/lib", "-lamdhip64", "-Wl,--no-undefined"], verbose)
     shutil.move(tmp, LIB)
+    if os.path.exists(CLIENT_SRC):
+        ctmp = CLIENT + ".tmp"
+        _run(["gcc", "-std=c99", "-O1", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__", f"-I{INCLUDE}",
+              f"-I{ROCM}/include", CLIENT_SRC, "-o", ctmp, f"-L{PKG}", "-ltig", f"-L{ROCM}/lib", "-lamdhip64",
+              "-lm", "-Wl,-rpath,$ORIGIN/../../invariant_gemm_token_amd", f"-Wl,-rpath,{ROCM}/lib"], verbose)
+        shutil.move(ctmp, CLIENT)
     return LIB
 
 
