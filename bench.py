@@ -102,7 +102,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--cpu-rows", type=int, default=8192)   # about 11 s of the fp64 oracle on 16 cores
     ap.add_argument("--cpu-rows-large", type=int, default=256)
     ap.add_argument("--no-extra", action="store_true", help="skip the linear / moe / large lines")
     ap.add_argument("--phase", choices=("all", "prefill", "decode", "tree"), default="all",
