@@ -123,7 +123,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// Persistent leaf-tree pipeline.
+// Persistent leaf-tree pipeline [IsoExec, Parallelism-invariant kernels].
 //
 // One workgroup per CU walks its tiles; the k-tiles of all its tiles form one
 // stream that an LDS ring (the whole 160 KiB) keeps several k-tiles ahead of
@@ -636,7 +636,8 @@ struct LogprobEpi {
 };
 
 // ---------------------------------------------------------------------------
-// tree_gemm: C = leaf-tree(A W^T), FP32 or bf16 out.
+// tree_gemm: C = leaf-tree(A W^T), FP32 or bf16 out [IsoExec, Parallelism-invariant
+// kernels]; the same bits for every M [BitRL, 4.1].
 // ---------------------------------------------------------------------------
 template <int EPI, int MI>
 __device__ __forceinline__ void StoreEpi<EPI, MI>::operator()(const AccT<MI>& acc, int mt, int nt,
@@ -1002,7 +1003,7 @@ __global__ __launch_bounds__(256) void fp8_scale_table_kernel(const uint8_t* __r
 }
 
 // ---------------------------------------------------------------------------
-// logprob, pass 1: per (row, 128-column vocabulary tile) the max m_t and
+// logprob, pass 1 [BitRL, 2]: per (row, 128-column vocabulary tile) the max m_t and
 // s_t = sum exp2((x - m_t) log2 e) by the balanced adjacent-pair tree over the
 // 128 columns (padded columns add +0), plus the sampled token's logit.
 // ---------------------------------------------------------------------------
@@ -1168,7 +1169,7 @@ void logprob_tile_kernel(DenseOperands op, int ktiles, int n_mt, int n_nt, float
 }
 
 // ---------------------------------------------------------------------------
-// logprob: the sampled token's logit x[row, id[row]], computed exactly as the
+// logprob [BitRL, 2]: the sampled token's logit x[row, id[row]], computed exactly as the
 // tile kernels compute that element.  One wave per (32 rows, leaf): it forms
 // the 32 x 32 block H[rows] W[ids]^T of its leaf with the same
 // v_mfma_f32_32x32x16_bf16 k-steps (ascending, from +0) and keeps the
@@ -1227,7 +1228,7 @@ void logprob_pick_kernel(const uint16_t* __restrict__ H, const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// logprob, pass 2: one workgroup of 256 per row combines the vocabulary tiles.
+// logprob, pass 2 [BitRL, 2]: one workgroup of 256 per row combines the vocabulary tiles.
 //   g = max_t m_t (exact); S = sum_t s_t exp2((m_t - g) log2 e) by the
 //   balanced adjacent-pair tree over the tiles zero-padded to P = 256 2^q
 //   (padding beyond the next power of two only adds +0 subtrees): thread t
@@ -1346,7 +1347,7 @@ __global__ __launch_bounds__(256) void logprob_combine_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// MoE: route (stable per-expert token lists), plan (work items), per-expert
+// MoE [BitRL, 4.4-4.5]: route (stable per-expert token lists), plan (work items), per-expert
 // leaf-tree GEMM on the persistent pipeline with gathered A rows, and the
 // fixed-order FP32 combine.
 // ---------------------------------------------------------------------------
@@ -2505,7 +2506,7 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
   }
 }
 
-// Router logits, the leaf-tree contraction with FP32 output for the router's
+// Router logits [BitRL, 4.1], the leaf-tree contraction with FP32 output for the router's
 // shape (few experts): one workgroup per 32 tokens x 64 experts, so that
 // T / 32 workgroups share the work instead of T / 64 tiles of the persistent
 // kernel.  Wave w accumulates leaves w, w + 4, ...: the same
@@ -2669,7 +2670,7 @@ hipError_t launch_moe_route(const float* logits, int64_t T, int n_experts, int t
 }
 
 // ---------------------------------------------------------------------------
-// Deterministic Top-K of positions: per row, the k positions of largest key,
+// Deterministic Top-K of positions [BitRL, 4.3]: per row, the k positions of largest key,
 // key = (order key of the score, position) as one 64-bit value, so equal
 // scores go to the larger position; +0 equals -0, NaN below every number.
 // The selected positions are written by descending position, then -1.
