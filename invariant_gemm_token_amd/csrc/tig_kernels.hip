@@ -2683,8 +2683,10 @@ hipError_t launch_moe_route(const float* logits, int64_t T, int n_experts, int t
 // T, the take-th largest 32-bit score key, is found by a radix select over
 // LDS histograms of 11, 11 and 10 bits: each pass counts the keys that share
 // the digits found so far and picks the digit at which the count from the
-// top reaches the number still wanted.  Keys above T are selected, and of the
-// keys equal to T the `need` at the largest positions.  The wave ballots of
+// top reaches the number still wanted.  On long rows a sample of 1024 keys
+// first bounds T from below, and when few enough keys reach the bound the
+// passes count only those, from a list in LDS.  Keys above T are selected, and
+// of the keys equal to T the `need` at the largest positions.  The wave ballots of
 // "key > T" and "key == T" per slot are, in that order, a bitmap of the row
 // by descending position; one scan over their popcounts gives each 64-position
 // block its output offset and tie rank, and the blocks' 16-position quarters,
@@ -2703,6 +2705,15 @@ static_assert(2 * kTopkThreads * 8 <= kTopkCopies * kTopkHistStride * 4, "the bl
 // from a list in LDS (the histogram copies past the first): more fall back to
 // scanning every key again.
 constexpr int kTopkListCap = (kTopkCopies - 1) * kTopkHistStride;
+// The sample that bounds T from below: slot kTopkSampleStride * w of every
+// thread of wave w, i.e. 16 runs of 64 consecutive positions spread over the
+// longest row.  A row whose sample holds fewer than kTopkMinSample positions
+// skips it.
+constexpr int kTopkSampleStride = kTopkPerThread / kTopkWaves;
+constexpr int kTopkMinSample = 256;
+// Keys at or above the sample's bound that the three passes can take from a
+// list in LDS.
+constexpr int kTopkCandCap = 8192;
 
 // f(integral_constant<I>), f(integral_constant<I+1>), ..., below N.
 template <int I, int N, class F>
@@ -2807,6 +2818,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
   __shared__ __attribute__((aligned(16))) uint32_t masks[kTopkBlocks * 4];   // per block: gt lo, hi, eq lo, hi
   __shared__ __attribute__((aligned(16))) int red[4 * kTopkWaves];   // two halves, alternated by pass; scans
   __shared__ int found[2][3];   // per pass parity: digit, keys still wanted, keys in the digit's bin
+  // The keys at or above the sample's bound, then one word per thread that
+  // takes its other keys' writes (so the list is written without branches).
+  __shared__ uint32_t cand[kTopkCandCap + kTopkThreads];
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int n = lengths[r];
@@ -2898,95 +2912,177 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
       left = found[par][1];
       bin_n = found[par][2];
     };
-    int d0, rem, c0;
-    // Pass 0 over every key: top 11 bits.
+    uint32_t T;
+    int need;                                        // keys equal to T to take, largest positions first
+    // Candidates.  The sampled keys give a lower bound P on T: the low edge of
+    // the first-digit bin that holds the sample's rs-th largest key, with rs
+    // about 1.5 times the sample's share of `take` (plus 8).  If at least
+    // `take` and at most kTopkCandCap keys are >= P, those keys are the row's
+    // largest and hold every key >= T, so the take-th largest of them is T and
+    // the number above T is the same: the three passes run over them alone,
+    // from a list in LDS.  Otherwise (a sample unlike the row, many equal
+    // keys) the passes run over every key.  P decides only how much is
+    // counted, never T or `need`.
+    uint32_t P = 0u;
+    int total = 0, cand_at = 0;                      // keys >= P; this thread's first place in the list
+    bool use_list = false;
+    {
+      int m = 0;                                     // sampled slots inside the row
 #pragma unroll
-    for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g) {
-      if (g < groups) {
-        if (g != groups - 1) {                       // full groups: every slot counts
+      for (int w = 0; w < kTopkWaves; ++w) {
+        const int v = n - (kTopkThreads * kTopkSampleStride + 64) * w;
+        m += v < 0 ? 0 : (v > 64 ? 64 : v);
+      }
+      const int rs = int(3 * int64_t(take) * m / (2 * int64_t(n))) + 8;
+      if (m >= kTopkMinSample && 4 * rs <= m) {
+        // This wave's sampled slot; slots in groups past the row are not
+        // loaded, and the last group's slots past the row hold key 0.
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        uint32_t sk = 0u;
 #pragma unroll
-          for (int i = 0; i < kTopkGroup; ++i) atomicAdd(&hcopy[key[kTopkGroup * g + i] >> 21], 1u);
-        } else {                                     // the last group: slots past the row have key 0
+        for (int w = 0; w < kTopkWaves; ++w)
+          if (w == wv && kTopkSampleStride * w < kTopkGroup * groups) sk = key[kTopkSampleStride * w];
+        if (sk != 0u) atomicAdd(&hist[sk >> 21], 1u);
+        __syncthreads();
+        int ds, unused_left, unused_n;
+        scan_find(std::integral_constant<int, 1>{}, 0, rs, ds, unused_left, unused_n);
+        // Digit 0 holds NaN and the slots past the row: no bound below it.
+        if (ds > 0) {
+          P = uint32_t(ds) << 21;
+          int cnt = 0;
 #pragma unroll
-          for (int i = 0; i < kTopkGroup; ++i) {
-            const uint32_t kv = key[kTopkGroup * g + i];
-            if (kv != 0u) atomicAdd(&hcopy[kv >> 21], 1u);
-          }
+          for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g)
+            if (g < groups)
+#pragma unroll
+              for (int i = 0; i < kTopkGroup; ++i) cnt += key[kTopkGroup * g + i] >= P ? 1 : 0;
+          cand_at = block_scan1_topk(cnt, red, total) - cnt;
+          use_list = total >= take && total <= kTopkCandCap;
         }
       }
     }
-    __syncthreads();
-    scan_find(std::integral_constant<int, kTopkCopies>{}, 0, take, d0, rem, c0);
-    uint32_t prefix = uint32_t(d0);
-    if (c0 <= kTopkListCap) {
-      // The keys of bin d0 (c0 of them, slots past the row excluded) into a
-      // list in the histogram copies past the first, at offsets from a scan of
-      // the per-thread counts; passes 1 and 2 then read the list and count into
-      // copy 0 alone.  The order of the list does not reach T or `need`.
-      uint32_t* const list = hist + kTopkHistStride;
-      int cnt = 0;
+    if (use_list) {
 #pragma unroll
       for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g)
         if (g < groups)
 #pragma unroll
           for (int i = 0; i < kTopkGroup; ++i) {
             const uint32_t kv = key[kTopkGroup * g + i];
-            cnt += (kv != 0u && (kv >> 21) == prefix) ? 1 : 0;
-          }
-      int c_all;
-      int at = block_scan1_topk(cnt, red + kTopkWaves, c_all) - cnt;
-#pragma unroll
-      for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g)
-        if (g < groups)
-#pragma unroll
-          for (int i = 0; i < kTopkGroup; ++i) {
-            const uint32_t kv = key[kTopkGroup * g + i];
-            if (kv != 0u && (kv >> 21) == prefix) list[at++] = kv;
+            const bool c = kv >= P;
+            cand[c ? cand_at : kTopkCandCap + tid] = kv;
+            cand_at += c ? 1 : 0;
           }
       __syncthreads();
-      int d1, d2, n1, n2;
-      for (int i = tid; i < c0; i += kTopkThreads) atomicAdd(&hist[(list[i] >> 10) & 2047u], 1u);
+      int d0, d1, d2, rem, c0, n1, n2;
+      for (int i = tid; i < total; i += kTopkThreads) atomicAdd(&hcopy[cand[i] >> 21], 1u);
+      __syncthreads();
+      scan_find(std::integral_constant<int, kTopkCopies>{}, 1, take, d0, rem, c0);
+      uint32_t prefix = uint32_t(d0);
+      for (int i = tid; i < total; i += kTopkThreads) {
+        const uint32_t kv = cand[i];
+        if ((kv >> 21) == prefix) atomicAdd(&hist[(kv >> 10) & 2047u], 1u);
+      }
       __syncthreads();
       scan_find(std::integral_constant<int, 1>{}, 0, rem, d1, rem, n1);
       prefix = (prefix << 11) | uint32_t(d1);
-      for (int i = tid; i < c0; i += kTopkThreads)
-        if ((list[i] >> 10) == prefix) atomicAdd(&hist[list[i] & 1023u], 1u);
+      for (int i = tid; i < total; i += kTopkThreads) {
+        const uint32_t kv = cand[i];
+        if ((kv >> 10) == prefix) atomicAdd(&hist[kv & 1023u], 1u);
+      }
       __syncthreads();
       scan_find(std::integral_constant<int, 1>{}, 1, rem, d2, rem, n2);
-      prefix = (prefix << 10) | uint32_t(d2);
+      T = (prefix << 10) | uint32_t(d2);
+      need = rem;
     } else {
-      // Passes 1 and 2 over every key again.
+      int d0, rem, c0;
+      // Pass 0 over every key: top 11 bits.
 #pragma unroll
-      for (int pass = 1; pass < 3; ++pass) {
-        const int shift = pass == 1 ? 10 : 0;
-        const uint32_t dmask = pass == 2 ? 1023u : 2047u;
-        const int pshift = pass == 1 ? 21 : 10;      // bits below the digits already found
+      for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g) {
+        if (g < groups) {
+          if (g != groups - 1) {                       // full groups: every slot counts
 #pragma unroll
-        for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g) {
-          if (g < groups) {
-            // Four slots per test: a wave with no match in any of them skips
-            // the four (the common case in the last pass).
+            for (int i = 0; i < kTopkGroup; ++i) atomicAdd(&hcopy[key[kTopkGroup * g + i] >> 21], 1u);
+          } else {                                     // the last group: slots past the row have key 0
 #pragma unroll
-            for (int i0 = 0; i0 < kTopkGroup; i0 += 4) {
-              bool m[4];
-#pragma unroll
-              for (int q = 0; q < 4; ++q) m[q] = (key[kTopkGroup * g + i0 + q] >> pshift) == prefix;
-              if (m[0] || m[1] || m[2] || m[3]) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                  if (m[q]) atomicAdd(&hcopy[(key[kTopkGroup * g + i0 + q] >> shift) & dmask], 1u);
-              }
+            for (int i = 0; i < kTopkGroup; ++i) {
+              const uint32_t kv = key[kTopkGroup * g + i];
+              if (kv != 0u) atomicAdd(&hcopy[kv >> 21], 1u);
             }
           }
         }
-        __syncthreads();
-        int d, nb;
-        scan_find(std::integral_constant<int, kTopkCopies>{}, pass & 1, rem, d, rem, nb);
-        prefix = (prefix << (pass == 2 ? 10 : 11)) | uint32_t(d);
       }
+      __syncthreads();
+      scan_find(std::integral_constant<int, kTopkCopies>{}, 0, take, d0, rem, c0);
+      uint32_t prefix = uint32_t(d0);
+      if (c0 <= kTopkListCap) {
+        // The keys of bin d0 (c0 of them, slots past the row excluded) into a
+        // list in the histogram copies past the first, at offsets from a scan of
+        // the per-thread counts; passes 1 and 2 then read the list and count into
+        // copy 0 alone.  The order of the list does not reach T or `need`.
+        uint32_t* const list = hist + kTopkHistStride;
+        int cnt = 0;
+#pragma unroll
+        for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g)
+          if (g < groups)
+#pragma unroll
+            for (int i = 0; i < kTopkGroup; ++i) {
+              const uint32_t kv = key[kTopkGroup * g + i];
+              cnt += (kv != 0u && (kv >> 21) == prefix) ? 1 : 0;
+            }
+        int c_all;
+        int at = block_scan1_topk(cnt, red + kTopkWaves, c_all) - cnt;
+#pragma unroll
+        for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g)
+          if (g < groups)
+#pragma unroll
+            for (int i = 0; i < kTopkGroup; ++i) {
+              const uint32_t kv = key[kTopkGroup * g + i];
+              if (kv != 0u && (kv >> 21) == prefix) list[at++] = kv;
+            }
+        __syncthreads();
+        int d1, d2, n1, n2;
+        for (int i = tid; i < c0; i += kTopkThreads) atomicAdd(&hist[(list[i] >> 10) & 2047u], 1u);
+        __syncthreads();
+        scan_find(std::integral_constant<int, 1>{}, 0, rem, d1, rem, n1);
+        prefix = (prefix << 11) | uint32_t(d1);
+        for (int i = tid; i < c0; i += kTopkThreads)
+          if ((list[i] >> 10) == prefix) atomicAdd(&hist[list[i] & 1023u], 1u);
+        __syncthreads();
+        scan_find(std::integral_constant<int, 1>{}, 1, rem, d2, rem, n2);
+        prefix = (prefix << 10) | uint32_t(d2);
+      } else {
+        // Passes 1 and 2 over every key again.
+#pragma unroll
+        for (int pass = 1; pass < 3; ++pass) {
+          const int shift = pass == 1 ? 10 : 0;
+          const uint32_t dmask = pass == 2 ? 1023u : 2047u;
+          const int pshift = pass == 1 ? 21 : 10;      // bits below the digits already found
+#pragma unroll
+          for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g) {
+            if (g < groups) {
+              // Four slots per test: a wave with no match in any of them skips
+              // the four (the common case in the last pass).
+#pragma unroll
+              for (int i0 = 0; i0 < kTopkGroup; i0 += 4) {
+                bool m[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) m[q] = (key[kTopkGroup * g + i0 + q] >> pshift) == prefix;
+                if (m[0] || m[1] || m[2] || m[3]) {
+#pragma unroll
+                  for (int q = 0; q < 4; ++q)
+                    if (m[q]) atomicAdd(&hcopy[(key[kTopkGroup * g + i0 + q] >> shift) & dmask], 1u);
+                }
+              }
+            }
+          }
+          __syncthreads();
+          int d, nb;
+          scan_find(std::integral_constant<int, kTopkCopies>{}, pass & 1, rem, d, rem, nb);
+          prefix = (prefix << (pass == 2 ? 10 : 11)) | uint32_t(d);
+        }
+      }
+      T = prefix;
+      need = rem;
     }
-    const uint32_t T = prefix;
-    const int need = rem;                            // keys equal to T to take, largest positions first
     // Ballots per slot, gathered 16 slots to a register (lane 4s+q holds word
     // q of slot s of the group) and stored with one write per group.
 #pragma unroll

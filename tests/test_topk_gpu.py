@@ -152,3 +152,75 @@ def test_topk_threshold_bin_beyond_the_list(gpu_lib):
     scores[2, ::2] = 2.0                             # half the row in a higher bin, all equal
     lengths = np.array([ld, ld, ld, 20000, 14365, 14364, 24589, 24588, 30000, 65535], dtype=np.int32)
     _check(gpu_lib, scores, lengths, k, "one dense bin")
+
+
+# The kernel first bounds T from below with a sample of each row (slot 4w of
+# every thread of wave w: positions n-1-(4160w + l), l < 64) and, when at most
+# 8192 keys reach that bound, runs its radix passes over those keys alone.
+# The mirror below follows that rule on the host, only to make sure that each
+# case here takes the path it is meant to take; the expected result comes from
+# the oracle alone.
+def _sampled_positions(n: int) -> np.ndarray:
+    p = np.array([n - 1 - (4160 * w + l) for w in range(16) for l in range(64)])
+    return p[p >= 0]
+
+
+def _takes_list_path(row: np.ndarray, n: int, k: int) -> bool:
+    take = min(n, k)
+    m = _sampled_positions(n).size
+    rs = 3 * take * m // (2 * n) + 8
+    if m < 256 or 4 * rs > m:
+        return False
+    x = row[:n].astype(np.float32)
+    b = (x + np.float32(0)).view(np.uint32)
+    key = b ^ (((b.view(np.int32) >> 31).view(np.uint32)) | np.uint32(0x80000000))
+    key = np.where(np.isnan(x), np.uint32(1), key).astype(np.uint32)
+    ds = int(np.sort(key[_sampled_positions(n)] >> 21)[::-1][rs - 1])
+    if ds == 0:
+        return False
+    total = int((key >= np.uint32(ds << 21)).sum())
+    return take <= total <= 8192
+
+
+def test_topk_sampled_bound_both_paths(gpu_lib):
+    """Rows built so that the sample's bound is right, too high (fewer than k
+    keys reach it), too low (more keys than the list holds), and at the list's
+    capacity exactly (all ties at T) and one past it: every row must match the
+    oracle whichever path it takes."""
+    rng = np.random.default_rng(7500)
+    ld, k = 65536, 2048
+    sp = _sampled_positions(ld)
+    rows, want = [], []
+    rows.append(rng.standard_normal(ld).astype(np.float32)); want.append(True)        # plain N(0, 1)
+    r = rng.standard_normal(ld).astype(np.float32); r[sp] = 50.0 + rng.random(sp.size, dtype=np.float32)
+    rows.append(r); want.append(False)                                              # bound too high
+    r = rng.standard_normal(ld).astype(np.float32); r[sp] = -50.0
+    rows.append(r); want.append(False)                                              # bound too low
+    for extra, w in ((8192 - sp.size, True), (8193 - sp.size, False)):              # at / past capacity
+        r = np.full(ld, -1.0, np.float32)
+        others = np.setdiff1d(np.arange(ld), sp)
+        r[sp] = 1.0
+        r[rng.choice(others, size=extra, replace=False)] = 1.0
+        rows.append(r); want.append(w)
+    r = rng.standard_normal(ld).astype(np.float32); r[::7] = np.nan                 # NaN among the keys
+    rows.append(r); want.append(True)
+    scores = np.stack(rows)
+    lengths = np.full(len(rows), ld, np.int32)
+    for i, (row, w) in enumerate(zip(rows, want)):
+        assert _takes_list_path(row, ld, k) == w, i
+    _check(gpu_lib, scores, lengths, k, "sampled bound, both paths")
+
+
+@pytest.mark.parametrize("k", [1, 64, 512, 2048])
+def test_topk_sample_size_edges(gpu_lib, k):
+    """Lengths where the sample reaches its minimum size (12544 = 3 * 4160 + 64
+    positions), just below it, and where k is too large a share of the row for
+    the bound to pay; bf16-rounded scores (many ties)."""
+    rng = np.random.default_rng(7600 + k)
+    ld = 20000
+    lens = np.array([12543, 12544, 12545, 16383, 16384, 16385, 20000, 4160 * 4 + 63, 4160 * 4 + 64], np.int32)
+    scores = wl.indexer_scores(rng, lens.size, ld, "bf16")
+    paths = [_takes_list_path(scores[i], int(n), k) for i, n in enumerate(lens)]
+    if k <= 512:
+        assert not paths[0] and paths[1] and all(paths[1:]), paths
+    _check(gpu_lib, scores, lens, k, f"sample size edges k={k}")
