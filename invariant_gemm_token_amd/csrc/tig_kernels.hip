@@ -2683,14 +2683,19 @@ hipError_t launch_moe_route(const float* logits, int64_t T, int n_experts, int t
 // T, the take-th largest 32-bit score key, is found by a radix select over
 // LDS histograms of 11, 11 and 10 bits: each pass counts the keys that share
 // the digits found so far and picks the digit at which the count from the
-// top reaches the number still wanted.  On long rows a sample of 1024 keys
-// first bounds T from below, and when few enough keys reach the bound the
-// passes count only those, from a list in LDS.  Keys above T are selected, and
-// of the keys equal to T the `need` at the largest positions.  The wave ballots of
-// "key > T" and "key == T" per slot are, in that order, a bitmap of the row
-// by descending position; one scan over their popcounts gives each 64-position
-// block its output offset and tie rank, and the blocks' 16-position quarters,
-// dealt round-robin to the threads, write the selected positions.
+// top reaches the number still wanted.  Keys above T are selected, and of the
+// keys equal to T the `need` at the largest positions.
+//
+// On long rows a sample of 1024 keys first bounds T from below.  When few
+// enough keys reach the bound, they are listed in LDS with their positions, in
+// descending position order (per-block counts from wave ballots, one scan,
+// then each lane's rank in its wave's ballot): the passes count the list, and
+// the output is read off it, each thread taking a run of entries.  Otherwise
+// the passes count every key, and the wave ballots of "key > T" and
+// "key == T" per slot give a bitmap of the row by descending position; one
+// scan over their popcounts gives each 64-position block its output offset
+// and tie rank, and the blocks' 16-position quarters, dealt round-robin to
+// the threads, write the selected positions.
 // ---------------------------------------------------------------------------
 namespace {
 
@@ -2818,9 +2823,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
   __shared__ __attribute__((aligned(16))) uint32_t masks[kTopkBlocks * 4];   // per block: gt lo, hi, eq lo, hi
   __shared__ __attribute__((aligned(16))) int red[4 * kTopkWaves];   // two halves, alternated by pass; scans
   __shared__ int found[2][3];   // per pass parity: digit, keys still wanted, keys in the digit's bin
-  // The keys at or above the sample's bound, then one word per thread that
-  // takes its other keys' writes (so the list is written without branches).
-  __shared__ uint32_t cand[kTopkCandCap + kTopkThreads];
+  // The scores at or above the sample's bound with their positions, then one
+  // entry per lane that takes the other slots' writes.
+  __shared__ uint2 cand[kTopkCandCap + 64];
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int n = lengths[r];
@@ -2828,13 +2833,14 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
   const int take = n < k ? n : k;
   int32_t* o = out + r * int64_t(k);
   const int groups = (n + kTopkThreads * kTopkGroup - 1) / (kTopkThreads * kTopkGroup);
+  // The scores' bits, later (on the passes over every key) their keys.
   uint32_t key[kTopkPerThread];
   if (take > 0) {
-    // Loads of all groups that reach into the row first, then the keys, so
-    // that every load is in flight at once.  A slot before position 0 (only in
-    // the last group) has a byte offset that wraps to 2^32 - 4|p| in 32 bits,
-    // past the buffer's range of 4n <= 2^18 bytes: it returns 0 with no
-    // branch, and the slot gets key 0.
+    // Every load of the groups that reach into the row is issued at once.  A
+    // slot before position 0 (only in the last group) has a byte offset that
+    // wraps to 2^32 - 4|p| in 32 bits, past the buffer's range of
+    // 4n <= 2^18 bytes: it returns 0 with no branch, and the slot then gets a
+    // NaN, which no float comparison below selects.
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(scores + r * ld, uint32_t(n) * 4u);
     const uint32_t off0 = uint32_t(n - 1 - tid) * 4u;
 #pragma unroll
@@ -2849,18 +2855,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
     }
 #pragma unroll
     for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g) {
-      if (g < groups) {
+      if (g == groups - 1) {
 #pragma unroll
         for (int i = 0; i < kTopkGroup; ++i) {
           const int j = kTopkGroup * g + i;
-          key[j] = topk_key(__builtin_bit_cast(float, key[j]));
-        }
-        if (g == groups - 1) {
-#pragma unroll
-          for (int i = 0; i < kTopkGroup; ++i) {
-            const int j = kTopkGroup * g + i;
-            key[j] = n - 1 - (kTopkThreads * j + tid) >= 0 ? key[j] : 0u;
-          }
+          key[j] = n - 1 - (kTopkThreads * j + tid) >= 0 ? key[j] : 0x7FC00000u;
         }
       }
     }
@@ -2912,20 +2911,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
       left = found[par][1];
       bin_n = found[par][2];
     };
-    uint32_t T;
-    int need;                                        // keys equal to T to take, largest positions first
     // Candidates.  The sampled keys give a lower bound P on T: the low edge of
     // the first-digit bin that holds the sample's rs-th largest key, with rs
     // about 1.5 times the sample's share of `take` (plus 8).  If at least
     // `take` and at most kTopkCandCap keys are >= P, those keys are the row's
     // largest and hold every key >= T, so the take-th largest of them is T and
-    // the number above T is the same: the three passes run over them alone,
-    // from a list in LDS.  Otherwise (a sample unlike the row, many equal
-    // keys) the passes run over every key.  P decides only how much is
-    // counted, never T or `need`.
-    uint32_t P = 0u;
-    int total = 0, cand_at = 0;                      // keys >= P; this thread's first place in the list
+    // the number above T is the same: the three passes count them alone, from
+    // a list in LDS, and the output is read off the list.  Otherwise (a
+    // sample unlike the row, many equal keys) the passes run over every key.
+    // P decides only how much is counted, never T or `need`.
+    float Pf = 0.0f;                                 // the score whose key is P
+    int total = 0;                                   // keys >= P
     bool use_list = false;
+    // Per 64-position block e = slot * waves + wave: its keys >= P, then
+    // (after a scan) the list index of its first one.
+    uint32_t* const blk = masks;
     {
       int m = 0;                                     // sampled slots inside the row
 #pragma unroll
@@ -2936,63 +2936,142 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
       const int rs = int(3 * int64_t(take) * m / (2 * int64_t(n))) + 8;
       if (m >= kTopkMinSample && 4 * rs <= m) {
         // This wave's sampled slot; slots in groups past the row are not
-        // loaded, and the last group's slots past the row hold key 0.
+        // loaded, and sampled slots past the row are not counted.
         const int wv = __builtin_amdgcn_readfirstlane(wave);
-        uint32_t sk = 0u;
+        uint32_t sv = 0u;
 #pragma unroll
         for (int w = 0; w < kTopkWaves; ++w)
-          if (w == wv && kTopkSampleStride * w < kTopkGroup * groups) sk = key[kTopkSampleStride * w];
-        if (sk != 0u) atomicAdd(&hist[sk >> 21], 1u);
+          if (w == wv && kTopkSampleStride * w < kTopkGroup * groups) sv = key[kTopkSampleStride * w];
+        if (n - 1 - (kTopkThreads * kTopkSampleStride * wv + tid) >= 0)
+          atomicAdd(&hist[topk_key(__builtin_bit_cast(float, sv)) >> 21], 1u);
         __syncthreads();
         int ds, unused_left, unused_n;
         scan_find(std::integral_constant<int, 1>{}, 0, rs, ds, unused_left, unused_n);
         // Digit 0 holds NaN and the slots past the row: no bound below it.
         if (ds > 0) {
-          P = uint32_t(ds) << 21;
-          int cnt = 0;
+          // key >= P as a float comparison against the score whose key is P;
+          // below the keys of numbers (P <= key(-inf)) every number passes.
+          // A bound above key(+inf) reads as a NaN and passes nothing.
+          const uint32_t P = uint32_t(ds) << 21;
+          Pf = P <= 0x007FFFFFu ? -__builtin_inff()
+                                : __builtin_bit_cast(float, P >= 0x80000000u ? P ^ 0x80000000u : ~P);
+          // Lane j of the wave gathers slot j's count, eight slots at a time.
+          uint32_t bc = 0u;
+          static_for<0, kTopkPerThread / 8>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            if (h / 2 < groups) {
+              uint32_t c[8];
 #pragma unroll
-          for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g)
-            if (g < groups)
-#pragma unroll
-              for (int i = 0; i < kTopkGroup; ++i) cnt += key[kTopkGroup * g + i] >= P ? 1 : 0;
-          cand_at = block_scan1_topk(cnt, red, total) - cnt;
+              for (int q = 0; q < 8; ++q)
+                c[q] = uint32_t(__builtin_popcountll(__builtin_amdgcn_ballot_w64(__builtin_bit_cast(float, key[8 * h + q]) >= Pf)));
+              bc = write_lanes8<8 * h>(bc, c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[7]);
+            }
+          });
+          blk[lane * kTopkWaves + wave] = bc;
+          __syncthreads();
+          const int c = int(blk[tid]);               // block tid (kTopkBlocks == kTopkThreads)
+          const int first = block_scan1_topk(c, red, total) - c;
+          blk[tid] = uint32_t(first);
           use_list = total >= take && total <= kTopkCandCap;
+          __syncthreads();
         }
       }
     }
     if (use_list) {
+      // Every key >= P with its position into the list, in block order and
+      // by lane within a block, i.e. by descending position.  Other slots
+      // write to a word of their lane past the list (no branches).
+      const int firsts = int(blk[lane * kTopkWaves + wave]);   // lane j: block (slot j, this wave)
+      int top_pos = n - 1 - tid;                               // slot 0's position
+      float Pw = Pf;
+      // Opaque copies (no instruction): the comparisons are made afresh here,
+      // straight into the mask the lane counts read, rather than carried over
+      // from the counting loop, and a slot's position stays one subtraction.
+      asm volatile("" : "+v"(top_pos), "+v"(Pw));
 #pragma unroll
       for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g)
         if (g < groups)
 #pragma unroll
           for (int i = 0; i < kTopkGroup; ++i) {
-            const uint32_t kv = key[kTopkGroup * g + i];
-            const bool c = kv >= P;
-            cand[c ? cand_at : kTopkCandCap + tid] = kv;
-            cand_at += c ? 1 : 0;
+            const int j = kTopkGroup * g + i;
+            const bool c = __builtin_bit_cast(float, key[j]) >= Pw;
+            const uint64_t b = __builtin_amdgcn_ballot_w64(c);
+            // the block's first index plus the candidates in lanes below
+            const uint32_t at = __builtin_amdgcn_mbcnt_hi(
+                uint32_t(b >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(b), uint32_t(__builtin_amdgcn_readlane(firsts, j))));
+            cand[c ? at : uint32_t(kTopkCandCap + lane)] = make_uint2(key[j], uint32_t(top_pos - kTopkThreads * j));
           }
       __syncthreads();
       int d0, d1, d2, rem, c0, n1, n2;
-      for (int i = tid; i < total; i += kTopkThreads) atomicAdd(&hcopy[cand[i] >> 21], 1u);
+      for (int i = tid; i < total; i += kTopkThreads) {   // the listed scores become keys here
+        const uint32_t kv = topk_key(__builtin_bit_cast(float, cand[i].x));
+        cand[i].x = kv;
+        atomicAdd(&hcopy[kv >> 21], 1u);
+      }
       __syncthreads();
       scan_find(std::integral_constant<int, kTopkCopies>{}, 1, take, d0, rem, c0);
       uint32_t prefix = uint32_t(d0);
       for (int i = tid; i < total; i += kTopkThreads) {
-        const uint32_t kv = cand[i];
+        const uint32_t kv = cand[i].x;
         if ((kv >> 21) == prefix) atomicAdd(&hist[(kv >> 10) & 2047u], 1u);
       }
       __syncthreads();
       scan_find(std::integral_constant<int, 1>{}, 0, rem, d1, rem, n1);
       prefix = (prefix << 11) | uint32_t(d1);
       for (int i = tid; i < total; i += kTopkThreads) {
-        const uint32_t kv = cand[i];
+        const uint32_t kv = cand[i].x;
         if ((kv >> 10) == prefix) atomicAdd(&hist[kv & 1023u], 1u);
       }
       __syncthreads();
       scan_find(std::integral_constant<int, 1>{}, 1, rem, d2, rem, n2);
-      T = (prefix << 10) | uint32_t(d2);
-      need = rem;
+      const uint32_t T = (prefix << 10) | uint32_t(d2);
+      const int need = rem;                          // keys equal to T to take, largest positions first
+      // Output off the list: thread t reads a run of consecutive entries;
+      // one scan of the runs' counts of keys > T and == T gives each run how
+      // many of either come before it.  An entry's offset is the number of
+      // selected entries before it: (keys > T before it) + min(need, ties
+      // before it); of the ties, the first `need` are taken.
+      const int per = (total + kTopkThreads - 1) / kTopkThreads;
+      const int i0 = tid * per, i1 = i0 + per < total ? i0 + per : total;
+      int ng = 0, nq = 0;
+      for (int i = i0; i < i1; ++i) {
+        const uint32_t kv = cand[i].x;
+        ng += kv > T ? 1 : 0;
+        nq += kv == T ? 1 : 0;
+      }
+      int ig, iq, tg, tq;
+      block_scan2_topk(ng, nq, red + 2 * kTopkWaves, ig, iq, tg, tq);
+      int gb = ig - ng, qb = iq - nq;
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(o, uint32_t(k) * 4u);
+      for (int i = i0; i < i1; ++i) {
+        const uint2 e = cand[i];
+        if (e.x > T) {
+          __builtin_amdgcn_raw_buffer_store_b32(e.y, ro, uint32_t(gb + (qb < need ? qb : need)) * 4u, 0, 0);
+          ++gb;
+        } else if (e.x == T) {
+          if (qb < need) __builtin_amdgcn_raw_buffer_store_b32(e.y, ro, uint32_t(gb + qb) * 4u, 0, 0);
+          ++qb;
+        }
+      }
     } else {
+      // Every score to its key; slots past the row get key 0.
+#pragma unroll
+      for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g) {
+        if (g < groups) {
+#pragma unroll
+          for (int i = 0; i < kTopkGroup; ++i) {
+            const int j = kTopkGroup * g + i;
+            key[j] = topk_key(__builtin_bit_cast(float, key[j]));
+          }
+          if (g == groups - 1) {
+#pragma unroll
+            for (int i = 0; i < kTopkGroup; ++i) {
+              const int j = kTopkGroup * g + i;
+              key[j] = n - 1 - (kTopkThreads * j + tid) >= 0 ? key[j] : 0u;
+            }
+          }
+        }
+      }
       int d0, rem, c0;
       // Pass 0 over every key: top 11 bits.
 #pragma unroll
@@ -3080,92 +3159,92 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
           prefix = (prefix << (pass == 2 ? 10 : 11)) | uint32_t(d);
         }
       }
-      T = prefix;
-      need = rem;
-    }
-    // Ballots per slot, gathered 16 slots to a register (lane 4s+q holds word
-    // q of slot s of the group) and stored with one write per group.
+      const uint32_t T = prefix;
+      const int need = rem;                            // keys equal to T to take, largest positions first
+      // Ballots per slot, gathered 16 slots to a register (lane 4s+q holds word
+      // q of slot s of the group) and stored with one write per group.
 #pragma unroll
-    for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g) {
-      if (g < groups) {
-        uint32_t acc = 0;
-        static_for<0, kTopkGroup / 2>([&](auto ic) {
-          constexpr int i = 2 * decltype(ic)::value;
-          const uint32_t ka = key[kTopkGroup * g + i], kb = key[kTopkGroup * g + i + 1];
-          const uint64_t ga = __ballot(ka > T), ea = __ballot(ka == T);
-          const uint64_t gb = __ballot(kb > T), eb = __ballot(kb == T);
-          acc = write_lanes8<4 * i>(acc, uint32_t(ga), uint32_t(ga >> 32), uint32_t(ea), uint32_t(ea >> 32),
-                                    uint32_t(gb), uint32_t(gb >> 32), uint32_t(eb), uint32_t(eb >> 32));
-        });
-        masks[((kTopkGroup * g + (lane >> 2)) * kTopkWaves + wave) * 4 + (lane & 3)] = acc;
+      for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g) {
+        if (g < groups) {
+          uint32_t acc = 0;
+          static_for<0, kTopkGroup / 2>([&](auto ic) {
+            constexpr int i = 2 * decltype(ic)::value;
+            const uint32_t ka = key[kTopkGroup * g + i], kb = key[kTopkGroup * g + i + 1];
+            const uint64_t ga = __builtin_amdgcn_ballot_w64(ka > T), ea = __builtin_amdgcn_ballot_w64(ka == T);
+            const uint64_t gb = __builtin_amdgcn_ballot_w64(kb > T), eb = __builtin_amdgcn_ballot_w64(kb == T);
+            acc = write_lanes8<4 * i>(acc, uint32_t(ga), uint32_t(ga >> 32), uint32_t(ea), uint32_t(ea >> 32),
+                                      uint32_t(gb), uint32_t(gb >> 32), uint32_t(eb), uint32_t(eb >> 32));
+          });
+          masks[((kTopkGroup * g + (lane >> 2)) * kTopkWaves + wave) * 4 + (lane & 3)] = acc;
+        }
       }
-    }
-    __syncthreads();
-    // Blocks e = slot * waves + wave (64 positions each, descending) in order;
-    // thread t scans blocks 2t and 2t+1.  Blocks past the row's groups count 0.
-    const int used = groups * kTopkGroup * kTopkWaves;
-    int pg[2], pq[2];
+      __syncthreads();
+      // Blocks e = slot * waves + wave (64 positions each, descending) in order;
+      // thread t scans blocks 2t and 2t+1.  Blocks past the row's groups count 0.
+      const int used = groups * kTopkGroup * kTopkWaves;
+      int pg[2], pq[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int e = 2 * tid + u;
-      pg[u] = pq[u] = 0;
-      if (e < used) {
-        const uint4 m = *reinterpret_cast<const uint4*>(&masks[4 * e]);
-        pg[u] = __builtin_popcount(m.x) + __builtin_popcount(m.y);
-        pq[u] = __builtin_popcount(m.z) + __builtin_popcount(m.w);
+      for (int u = 0; u < 2; ++u) {
+        const int e = 2 * tid + u;
+        pg[u] = pq[u] = 0;
+        if (e < used) {
+          const uint4 m = *reinterpret_cast<const uint4*>(&masks[4 * e]);
+          pg[u] = __builtin_popcount(m.x) + __builtin_popcount(m.y);
+          pq[u] = __builtin_popcount(m.z) + __builtin_popcount(m.w);
+        }
       }
-    }
-    int ig, iq, tg, tq;
-    block_scan2_topk(pg[0] + pg[1], pq[0] + pq[1], red + 2 * kTopkWaves, ig, iq, tg, tq);
-    const int gb = ig - pg[0] - pg[1], qb = iq - pq[0] - pq[1];
-    // Per block: keys > T and keys == T in the blocks before it.
-    int2* const before = reinterpret_cast<int2*>(hist);
-    before[2 * tid] = make_int2(gb, qb);
-    before[2 * tid + 1] = make_int2(gb + pg[0], qb + pq[0]);
-    __syncthreads();
-    // Output: a selected position's offset is the number of selected positions
-    // above it, = (keys > T above it) + min(need, ties above it).  Quarter
-    // u = 4e + c holds positions 16c .. 16c+15 of block e; thread t writes the
-    // quarters t, t + 1024, ...  The stores go through a buffer over the row's
-    // k outputs, so even an offset out of range could not write outside them.
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(o, uint32_t(k) * 4u);
-    uint4 mu[kTopkPerThread / 16];
-    int2 bu[kTopkPerThread / 16];
+      int ig, iq, tg, tq;
+      block_scan2_topk(pg[0] + pg[1], pq[0] + pq[1], red + 2 * kTopkWaves, ig, iq, tg, tq);
+      const int gb = ig - pg[0] - pg[1], qb = iq - pq[0] - pq[1];
+      // Per block: keys > T and keys == T in the blocks before it.
+      int2* const before = reinterpret_cast<int2*>(hist);
+      before[2 * tid] = make_int2(gb, qb);
+      before[2 * tid + 1] = make_int2(gb + pg[0], qb + pq[0]);
+      __syncthreads();
+      // Output: a selected position's offset is the number of selected positions
+      // above it, = (keys > T above it) + min(need, ties above it).  Quarter
+      // u = 4e + c holds positions 16c .. 16c+15 of block e; thread t writes the
+      // quarters t, t + 1024, ...  The stores go through a buffer over the row's
+      // k outputs, so even an offset out of range could not write outside them.
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(o, uint32_t(k) * 4u);
+      uint4 mu[kTopkPerThread / 16];
+      int2 bu[kTopkPerThread / 16];
 #pragma unroll
-    for (int i = 0; i < kTopkPerThread / 16; ++i) {   // every read first, then the writes
-      const int e = (tid + kTopkThreads * i) >> 2;
-      mu[i] = *reinterpret_cast<const uint4*>(&masks[4 * e]);
-      bu[i] = before[e];
-    }
-#pragma unroll
-    for (int i = 0; i < kTopkPerThread / 16; ++i) {
-      const int u = tid + kTopkThreads * i;
-      if (u >= 4 * used) break;
-      const int e = u >> 2, c = u & 3;
-      const uint4 m = mu[i];
-      const uint64_t gm = uint64_t(m.x) | (uint64_t(m.y) << 32), em = uint64_t(m.z) | (uint64_t(m.w) << 32);
-      const uint64_t below = (uint64_t(1) << (16 * c)) - 1;
-      uint32_t gq = uint32_t(gm >> (16 * c)) & 0xFFFFu, eq = uint32_t(em >> (16 * c)) & 0xFFFFu;
-      if ((gq | eq) == 0u) continue;
-      const int2 b = bu[i];
-      const int at_g = b.x + __popcll(gm & below), at_q = b.y + __popcll(em & below);
-      // The quarter's selected positions go to consecutive offsets from the
-      // number selected above it; of its ties, the first need - at_q.
-      const int allow = need - at_q;
-      uint32_t keep = 0u;
-      if (allow > 0) {                               // then keep has more than `drop` bits set
-        keep = eq;
-        for (int drop = __builtin_popcount(eq) - allow; drop > 0; --drop)
-          keep &= ~(0x80000000u >> __builtin_clz(keep));
+      for (int i = 0; i < kTopkPerThread / 16; ++i) {   // every read first, then the writes
+        const int e = (tid + kTopkThreads * i) >> 2;
+        mu[i] = *reinterpret_cast<const uint4*>(&masks[4 * e]);
+        bu[i] = before[e];
       }
-      uint32_t sel = gq | keep;
-      int at = at_g + (at_q < need ? at_q : need);
-      const int top = n - 1 - ((e / kTopkWaves) * kTopkThreads + (e % kTopkWaves) * 64 + 16 * c);
-      while (sel) {
-        const int bit = __builtin_ctz(sel);
-        sel &= sel - 1;
-        __builtin_amdgcn_raw_buffer_store_b32(top - bit, ro, uint32_t(at) * 4u, 0, 0);
-        ++at;
+#pragma unroll
+      for (int i = 0; i < kTopkPerThread / 16; ++i) {
+        const int u = tid + kTopkThreads * i;
+        if (u >= 4 * used) break;
+        const int e = u >> 2, c = u & 3;
+        const uint4 m = mu[i];
+        const uint64_t gm = uint64_t(m.x) | (uint64_t(m.y) << 32), em = uint64_t(m.z) | (uint64_t(m.w) << 32);
+        const uint64_t below = (uint64_t(1) << (16 * c)) - 1;
+        uint32_t gq = uint32_t(gm >> (16 * c)) & 0xFFFFu, eq = uint32_t(em >> (16 * c)) & 0xFFFFu;
+        if ((gq | eq) == 0u) continue;
+        const int2 b = bu[i];
+        const int at_g = b.x + __popcll(gm & below), at_q = b.y + __popcll(em & below);
+        // The quarter's selected positions go to consecutive offsets from the
+        // number selected above it; of its ties, the first need - at_q.
+        const int allow = need - at_q;
+        uint32_t keep = 0u;
+        if (allow > 0) {                               // then keep has more than `drop` bits set
+          keep = eq;
+          for (int drop = __builtin_popcount(eq) - allow; drop > 0; --drop)
+            keep &= ~(0x80000000u >> __builtin_clz(keep));
+        }
+        uint32_t sel = gq | keep;
+        int at = at_g + (at_q < need ? at_q : need);
+        const int top = n - 1 - ((e / kTopkWaves) * kTopkThreads + (e % kTopkWaves) * 64 + 16 * c);
+        while (sel) {
+          const int bit = __builtin_ctz(sel);
+          sel &= sel - 1;
+          __builtin_amdgcn_raw_buffer_store_b32(top - bit, ro, uint32_t(at) * 4u, 0, 0);
+          ++at;
+        }
       }
     }
   }

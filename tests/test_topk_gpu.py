@@ -185,8 +185,9 @@ def _takes_list_path(row: np.ndarray, n: int, k: int) -> bool:
 def test_topk_sampled_bound_both_paths(gpu_lib):
     """Rows built so that the sample's bound is right, too high (fewer than k
     keys reach it), too low (more keys than the list holds), and at the list's
-    capacity exactly (all ties at T) and one past it: every row must match the
-    oracle whichever path it takes."""
+    capacity exactly (all ties at T) and one past it, plus list-path rows with
+    T among denormals and zeros, below zero, and at -inf among NaN: every row
+    must match the oracle whichever path it takes."""
     rng = np.random.default_rng(7500)
     ld, k = 65536, 2048
     sp = _sampled_positions(ld)
@@ -203,6 +204,22 @@ def test_topk_sampled_bound_both_paths(gpu_lib):
         r[rng.choice(others, size=extra, replace=False)] = 1.0
         rows.append(r); want.append(w)
     r = rng.standard_normal(ld).astype(np.float32); r[::7] = np.nan                 # NaN among the keys
+    rows.append(r); want.append(True)
+    # The list path compares score bits as floats against the bound and T:
+    # T among denormals and signed zeros, ...
+    r = np.full(ld, -1.0, np.float32)
+    tiny = np.array([1, 2, 3, 100, 0x1000, 0x1FFFFF], np.uint32).view(np.float32)   # one first-digit bin
+    at = np.union1d(sp, rng.choice(ld, size=3000, replace=False))
+    r[at] = rng.choice(np.concatenate([tiny, np.float32([0.0, -0.0])]), size=at.size)
+    big = np.array([0x400000, 0x7FFFFF], np.uint32).view(np.float32)                 # larger denormals
+    r[rng.choice(np.setdiff1d(np.arange(ld), sp), size=40, replace=False)] = rng.choice(big, size=40)
+    rows.append(r); want.append(True)
+    r = -np.exp(rng.standard_normal(ld)).astype(np.float32)                       # ... every score negative, ...
+    rows.append(r); want.append(True)
+    r = np.full(ld, np.nan, np.float32)                                             # ... and T = -inf among NaN
+    at = np.union1d(sp, rng.choice(ld, size=4500, replace=False))
+    r[at] = -np.inf
+    r[rng.choice(np.setdiff1d(np.arange(ld), sp), size=1000, replace=False)] = rng.standard_normal(1000)
     rows.append(r); want.append(True)
     scores = np.stack(rows)
     lengths = np.full(len(rows), ld, np.int32)
