@@ -221,6 +221,11 @@ def test_topk_sampled_bound_both_paths(gpu_lib):
     r[at] = -np.inf
     r[rng.choice(np.setdiff1d(np.arange(ld), sp), size=1000, replace=False)] = rng.standard_normal(1000)
     rows.append(r); want.append(True)
+    for extra, w in ((k - sp.size, True), (k - 1 - sp.size, False)):               # exactly k at the bound / k - 1
+        r = np.full(ld, -5.0, np.float32)
+        r[sp] = 5.0
+        r[rng.choice(np.setdiff1d(np.arange(ld), sp), size=extra, replace=False)] = 5.0
+        rows.append(r); want.append(w)
     scores = np.stack(rows)
     lengths = np.full(len(rows), ld, np.int32)
     for i, (row, w) in enumerate(zip(rows, want)):
@@ -241,3 +246,15 @@ def test_topk_sample_size_edges(gpu_lib, k):
     if k <= 512:
         assert not paths[0] and paths[1] and all(paths[1:]), paths
     _check(gpu_lib, scores, lens, k, f"sample size edges k={k}")
+
+
+@pytest.mark.parametrize("k", [8191, 8192, 9000])
+def test_topk_k_at_and_past_the_list(gpu_lib, k):
+    """Full-length rows with k at the list's capacity (8192) and past it: the
+    list path can take a row only if exactly k keys reach the bound, so these
+    rows mostly count every key; lengths mixed."""
+    rng = np.random.default_rng(7700 + k)
+    ld, R = 65536, 8
+    scores = wl.indexer_scores(rng, R, ld, "bf16")
+    lengths = np.array([ld, ld - 1, 40000, 20000, k, k - 1, k + 1, 12544], np.int32)
+    _check(gpu_lib, scores, lengths, k, f"k={k} near the list size")
