@@ -2689,8 +2689,9 @@ hipError_t launch_moe_route(const float* logits, int64_t T, int n_experts, int t
 // On long rows a sample of 1024 keys first bounds T from below.  When few
 // enough keys reach the bound, they are listed in LDS with their positions, in
 // descending position order (per-block counts from wave ballots, one scan,
-// then each lane's rank in its wave's ballot): the passes count the list, and
-// the output is read off it, each thread taking a run of entries.  Otherwise
+// then each lane's rank in its wave's ballot): the passes count the list (the
+// last one only when the keys of T's first bin have low bits set), and the
+// output is read off it, each thread taking a run of entries.  Otherwise
 // the passes count every key, and the wave ballots of "key > T" and
 // "key == T" per slot give a bitmap of the row by descending position; one
 // scan over their popcounts gives each 64-position block its output offset
@@ -2826,6 +2827,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
   // The scores at or above the sample's bound with their positions, then one
   // entry per lane that takes the other slots' writes.
   __shared__ uint2 cand[kTopkCandCap + 64];
+  __shared__ uint32_t low_bits;   // list path: OR of the low 10 key bits in the threshold's first bin
   const int64_t r = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int n = lengths[r];
@@ -2981,6 +2983,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
       // Every key >= P with its position into the list, in block order and
       // by lane within a block, i.e. by descending position.  Other slots
       // write to a word of their lane past the list (no branches).
+      if (tid == 0) low_bits = 0u;
       const int firsts = int(blk[lane * kTopkWaves + wave]);   // lane j: block (slot j, this wave)
       int top_pos = n - 1 - tid;                               // slot 0's position
       float Pw = Pf;
@@ -3011,19 +3014,32 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
       __syncthreads();
       scan_find(std::integral_constant<int, kTopkCopies>{}, 1, take, d0, rem, c0);
       uint32_t prefix = uint32_t(d0);
+      uint32_t low = 0u;
       for (int i = tid; i < total; i += kTopkThreads) {
         const uint32_t kv = cand[i].x;
-        if ((kv >> 21) == prefix) atomicAdd(&hist[(kv >> 10) & 2047u], 1u);
+        if ((kv >> 21) == prefix) {
+          atomicAdd(&hist[(kv >> 10) & 2047u], 1u);
+          low |= kv;
+        }
       }
+      if (low & 1023u) atomicOr(&low_bits, 1u);
       __syncthreads();
       scan_find(std::integral_constant<int, 1>{}, 0, rem, d1, rem, n1);
       prefix = (prefix << 11) | uint32_t(d1);
-      for (int i = tid; i < total; i += kTopkThreads) {
-        const uint32_t kv = cand[i].x;
-        if ((kv >> 10) == prefix) atomicAdd(&hist[kv & 1023u], 1u);
+      // When every key of the first bin ends in ten zero bits (scores of bf16
+      // or fp16 values, say), the keys with T's 22-bit prefix all equal
+      // prefix << 10: that is T, and `rem` of them are wanted.  Otherwise the
+      // last pass finds the low bits.
+      if (low_bits != 0u) {
+        for (int i = tid; i < total; i += kTopkThreads) {
+          const uint32_t kv = cand[i].x;
+          if ((kv >> 10) == prefix) atomicAdd(&hist[kv & 1023u], 1u);
+        }
+        __syncthreads();
+        scan_find(std::integral_constant<int, 1>{}, 1, rem, d2, rem, n2);
+      } else {
+        d2 = 0;
       }
-      __syncthreads();
-      scan_find(std::integral_constant<int, 1>{}, 1, rem, d2, rem, n2);
       const uint32_t T = (prefix << 10) | uint32_t(d2);
       const int need = rem;                          // keys equal to T to take, largest positions first
       // Output off the list: thread t reads a run of consecutive entries;

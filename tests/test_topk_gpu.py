@@ -221,6 +221,17 @@ def test_topk_sampled_bound_both_paths(gpu_lib):
     r[at] = -np.inf
     r[rng.choice(np.setdiff1d(np.arange(ld), sp), size=1000, replace=False)] = rng.standard_normal(1000)
     rows.append(r); want.append(True)
+    # bf16-valued scores (every key ends in 16 zero bits, so the last pass can
+    # be skipped) with float32 values, whose low bits are set, well above the
+    # threshold (the skip still holds) or inside the threshold's first-digit
+    # bin, [1.75, 2) here (the last pass must run).
+    base = wl.indexer_scores(rng, 2, ld, "bf16")
+    r = base[0].copy()
+    r[rng.choice(ld, size=50, replace=False)] = np.float32(10.0) + rng.random(50, dtype=np.float32) * np.float32(1e-3)
+    rows.append(r); want.append(True)
+    r = base[1].copy()
+    r[rng.choice(ld, size=300, replace=False)] = (np.float32(1.75) + rng.random(300, dtype=np.float32) * np.float32(0.25))
+    rows.append(r); want.append(True)
     for extra, w in ((k - sp.size, True), (k - 1 - sp.size, False)):               # exactly k at the bound / k - 1
         r = np.full(ld, -5.0, np.float32)
         r[sp] = 5.0
