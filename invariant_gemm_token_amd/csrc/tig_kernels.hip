@@ -1018,12 +1018,14 @@ __device__ __forceinline__ float pair_tree_32(float (&e)[32]) {
 }
 
 // The two 32-lane halves of a wave exchange one float: lo = the value of lane
-// l & 31, hi = that of lane (l & 31) + 32, on every lane.
+// l & 31, hi = that of lane (l & 31) + 32, on every lane.  One lane swap
+// (the upper half of the first copy with the lower half of the second): no
+// lane index and no LDS permute.
 __device__ __forceinline__ void halves(float x, float& lo, float& hi) {
-  const float o = __shfl_xor(x, 32);
-  const bool upper = (threadIdx.x & 32) != 0;
-  lo = upper ? o : x;
-  hi = upper ? x : o;
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  lo = __builtin_bit_cast(float, unsigned(sw[0]));
+  hi = __builtin_bit_cast(float, unsigned(sw[1]));
 }
 
 // Wave-private transpose area: 32 rows x 64 floats, 16-byte chunk index XOR
