@@ -2722,6 +2722,7 @@ constexpr int kTopkMinSample = 256;
 // Keys at or above the sample's bound that the three passes can take from a
 // list in LDS.
 constexpr int kTopkCandCap = 8192;
+static_assert(kTopkBlocks == kTopkThreads, "thread t scans the count of block t");
 
 // f(integral_constant<I>), f(integral_constant<I+1>), ..., below N.
 template <int I, int N, class F>
@@ -2982,9 +2983,10 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
       }
     }
     if (use_list) {
-      // Every key >= P with its position into the list, in block order and
-      // by lane within a block, i.e. by descending position.  Other slots
-      // write to a word of their lane past the list (no branches).
+      // Every score at or above the bound, with its position, into the list,
+      // in block order and by lane within a block, i.e. by descending
+      // position.  Other slots write to an entry of their lane past the list
+      // (no branches).
       if (tid == 0) low_bits = 0u;
       const int firsts = int(blk[lane * kTopkWaves + wave]);   // lane j: block (slot j, this wave)
       int top_pos = n - 1 - tid;                               // slot 0's position
