@@ -2848,6 +2848,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
     // NaN, which no float comparison below selects.
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(scores + r * ld, uint32_t(n) * 4u);
     const uint32_t off0 = uint32_t(n - 1 - tid) * 4u;
+    // This wave's sampled slot (see below) has a load of its own, issued
+    // first, so that the sample can be counted while the rest lands.
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t sv =
+        __builtin_amdgcn_raw_buffer_load_b32(rs, off0 - uint32_t(kTopkThreads * 4 * kTopkSampleStride * wv), 0, 0);
 #pragma unroll
     for (int g = 0; g < kTopkPerThread / kTopkGroup; ++g) {
       if (g < groups) {
@@ -2940,13 +2945,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
       }
       const int rs = int(3 * int64_t(take) * m / (2 * int64_t(n))) + 8;
       if (m >= kTopkMinSample && 4 * rs <= m) {
-        // This wave's sampled slot; slots in groups past the row are not
-        // loaded, and sampled slots past the row are not counted.
-        const int wv = __builtin_amdgcn_readfirstlane(wave);
-        uint32_t sv = 0u;
-#pragma unroll
-        for (int w = 0; w < kTopkWaves; ++w)
-          if (w == wv && kTopkSampleStride * w < kTopkGroup * groups) sv = key[kTopkSampleStride * w];
+        // This wave's sampled slot, sv; sampled slots past the row are not
+        // counted.
         if (n - 1 - (kTopkThreads * kTopkSampleStride * wv + tid) >= 0)
           atomicAdd(&hist[topk_key(__builtin_bit_cast(float, sv)) >> 21], 1u);
         __syncthreads();
