@@ -2886,10 +2886,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
     // the top reaches `want`: thread t owns bins 4t..4t+3 and clears them as it
     // reads them; `above` counts the bins of the threads after it, i.e. the
     // larger digits.  Ends with a barrier; `par` alternates the scan's area.
-    auto scan_find = [&](auto ncop, int par, int want, int& digit, int& left, int& bin_n) {
+    // Bins below first_bin are known to be empty (and clear): their owners
+    // skip them.
+    auto scan_find = [&](auto ncop, int par, int want, int& digit, int& left, int& bin_n, int first_bin = 0) {
       constexpr int NCOP = decltype(ncop)::value;
       int h[4] = {0, 0, 0, 0};
-      if (tid < 2048 / 4) {                          // the 2048 bins' owners; the other threads add 0
+      if (tid < 2048 / 4 && 4 * tid + 3 >= first_bin) {   // the 2048 bins' owners; the others add 0
 #pragma unroll
         for (int c = 0; c < NCOP; ++c) {
           uint4* const w = reinterpret_cast<uint4*>(&hist[c * kTopkHistStride + 4 * tid]);
@@ -2931,6 +2933,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
     // sample unlike the row, many equal keys) the passes run over every key.
     // P decides only how much is counted, never T or `need`.
     float Pf = 0.0f;                                 // the score whose key is P
+    int ds = 0;                                      // P's first digit
     int total = 0;                                   // keys >= P
     bool use_list = false;
     // Per 64-position block e = slot * waves + wave: its keys >= P, then
@@ -2950,7 +2953,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
         if (n - 1 - (kTopkThreads * kTopkSampleStride * wv + tid) >= 0)
           atomicAdd(&hist[topk_key(__builtin_bit_cast(float, sv)) >> 21], 1u);
         __syncthreads();
-        int ds, unused_left, unused_n;
+        int unused_left, unused_n;
         scan_find(std::integral_constant<int, 1>{}, 0, rs, ds, unused_left, unused_n);
         // Digit 0 holds NaN and the slots past the row: no bound below it.
         if (ds > 0) {
@@ -3016,7 +3019,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_positions_kernel(const floa
         atomicAdd(&hcopy[kv >> 21], 1u);
       }
       __syncthreads();
-      scan_find(std::integral_constant<int, kTopkCopies>{}, 1, take, d0, rem, c0);
+      // every listed key's first digit is >= P's
+      scan_find(std::integral_constant<int, kTopkCopies>{}, 1, take, d0, rem, c0, ds);
       uint32_t prefix = uint32_t(d0);
       uint32_t low = 0u;
       for (int i = tid; i < total; i += kTopkThreads) {
