@@ -38,6 +38,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int BM = kBlockM, BN = kBlockN, BK = kBlockK;   // BM: the MoE kernel's tile
@@ -645,32 +646,39 @@ __device__ __forceinline__ void StoreEpi<EPI, MI>::operator()(const AccT<MI>& ac
   const int tid = opaque_tid();
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = int64_t(mt) * Geo<MI>::BM, n0 = int64_t(nt) * BN;
-  if constexpr (EPI == kEpiBF16) {
-    // Column pairs in one 4-byte store: the lanes of an even / odd pair hold
-    // columns c, c + 1 of the same rows, so a lane swap gives the even lane
-    // row r's pair and the odd lane row r + 1's (half the store instructions).
-    // Needs N and ldc even and C 4-byte aligned (the same for every lane).
-    if (((N | ldc) & 1) == 0 && (reinterpret_cast<uintptr_t>(C) & 3) == 0) {
-      const bool odd = (lane & 1) != 0;
+  // Column pairs in one store (4 bytes of bf16, 8 of FP32): the lanes of an
+  // even / odd pair hold columns c, c + 1 of the same rows, so a lane swap
+  // gives the even lane row r's pair and the odd lane row r + 1's (half the
+  // store instructions).  Needs N and ldc even and C aligned to the pair
+  // (the same for every lane).
+  if (((N | ldc) & 1) == 0 && (reinterpret_cast<uintptr_t>(C) & (EPI == kEpiF32 ? 7 : 3)) == 0) {
+    const bool odd = (lane & 1) != 0;
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int64_t pc = (n0 + acc_col(wn, j, lane)) & ~int64_t(1);   // the pair's first column
+      for (int j = 0; j < 2; ++j) {
+        const int64_t pc = (n0 + acc_col(wn, j, lane)) & ~int64_t(1);   // the pair's first column
 #pragma unroll
-          for (int v = 0; v < 16; v += 2) {
-            const float a = acc.c[i][j][v], b = acc.c[i][j][v + 1];
-            const float got = __builtin_bit_cast(
-                float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, odd ? a : b), 0xB1, 0xf, 0xf, false));
-            const float lo = odd ? got : a, hi = odd ? b : got;
-            const int64_t row = m0 + acc_row<MI>(wm, i, v + (odd ? 1 : 0), lane);
-            if (pc < N && row < M)
+        for (int v = 0; v < 16; v += 2) {
+          const float a = acc.c[i][j][v], b = acc.c[i][j][v + 1];
+          const float got = __builtin_bit_cast(
+              float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, odd ? a : b), 0xB1, 0xf, 0xf, false));
+          const float lo = odd ? got : a, hi = odd ? b : got;
+          const int64_t row = m0 + acc_row<MI>(wm, i, v + (odd ? 1 : 0), lane);
+          if (pc < N && row < M) {
+            if constexpr (EPI == kEpiF32) {
+              f32x2 pr;
+              pr[0] = lo;
+              pr[1] = hi;
+              __builtin_nontemporal_store(pr, reinterpret_cast<f32x2*>(&static_cast<float*>(C)[row * ldc + pc]));
+            } else {
               __builtin_nontemporal_store(uint32_t(f32_to_bf16_rne(lo)) | (uint32_t(f32_to_bf16_rne(hi)) << 16),
                                           reinterpret_cast<uint32_t*>(&static_cast<uint16_t*>(C)[row * ldc + pc]));
+            }
           }
         }
-      return;
-    }
+      }
+    return;
   }
 #pragma unroll
   for (int i = 0; i < MI; ++i)
