@@ -1616,25 +1616,12 @@ struct MoeStoreEpi {
   static constexpr bool kSplitTop = false;
   MoeOperands op;
   __device__ __forceinline__ void spill(const AccT<MI>&) const {}
-  __device__ __forceinline__ void operator()(const AccT<MI>& acc, int item, int nt, char*) const {
-    const int tid = opaque_tid();
-    const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  __device__ __forceinline__ void operator()(const AccT<MI>& acc, int item, int nt, char* region) const {
     const CONST_AS int32_t* it = (const CONST_AS int32_t*)op.items + 4 * item;
     const int rows = it[2] - it[1] * Geo<MI>::BM;
     float* C = op.Y + (int64_t(it[3]) + int64_t(it[1]) * Geo<MI>::BM) * op.N;
-    const int64_t n0 = int64_t(nt) * BN;
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t col = n0 + acc_col(wn, j, lane);
-        if (col >= op.N) continue;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = acc_row<MI>(wm, i, v, lane);
-          if (row < rows) __builtin_nontemporal_store(acc.c[i][j][v], &C[int64_t(row) * op.N + col]);   // as StoreEpi
-        }
-      }
+    const StoreEpi<kEpiF32, MI> st{C, op.N, rows, op.N};
+    st(acc, 0, nt, region);
   }
 };
 
