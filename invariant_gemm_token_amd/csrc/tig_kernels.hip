@@ -39,6 +39,7 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4v;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int BM = kBlockM, BN = kBlockN, BK = kBlockK;   // BM: the MoE kernel's tile
@@ -646,6 +647,52 @@ __device__ __forceinline__ void StoreEpi<EPI, MI>::operator()(const AccT<MI>& ac
   const int tid = opaque_tid();
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = int64_t(mt) * Geo<MI>::BM, n0 = int64_t(nt) * BN;
+  // FP32 with N and ldc multiples of 4 and C 16-byte aligned: the lanes of a
+  // quad hold columns c .. c + 3 of the same four rows (registers 4u .. 4u+3),
+  // and two lane-swap levels (lanes 1 apart, then 2 apart) transpose that 4 x 4
+  // block, so that lane q writes row q's four columns in one 16-byte store.
+  if constexpr (EPI == kEpiF32) {
+    if (((N | ldc) & 3) == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0) {
+      const int q = lane & 3;
+      auto swp = [](float x, auto ctrl) {
+        return __builtin_bit_cast(
+            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), decltype(ctrl)::value, 0xf, 0xf, false));
+      };
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int64_t qc = (n0 + acc_col(wn, j, lane)) & ~int64_t(3);   // the quad's first column
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float a0 = acc.c[i][j][4 * u], a1 = acc.c[i][j][4 * u + 1];
+            const float a2 = acc.c[i][j][4 * u + 2], a3 = acc.c[i][j][4 * u + 3];
+            // Lanes 1 apart: the even lane keeps rows 0 and 2 (its columns c, c + 1),
+            // the odd lane rows 1 and 3.
+            const bool o1 = (q & 1) != 0;
+            const float g0 = swp(o1 ? a0 : a1, std::integral_constant<int, 0xB1>{});
+            const float g1 = swp(o1 ? a2 : a3, std::integral_constant<int, 0xB1>{});
+            // pair (row r, columns 2p, 2p + 1) held: lo/hi of two rows
+            const float p0l = o1 ? g0 : a0, p0h = o1 ? a1 : g0;   // row o1 (0 or 1)
+            const float p1l = o1 ? g1 : a2, p1h = o1 ? a3 : g1;   // row 2 + o1
+            // Lanes 2 apart: lanes 0, 1 keep their first row's pair and take the
+            // partner's; lanes 2, 3 keep the second row's pair.
+            const bool o2 = (q & 2) != 0;
+            const float s0 = swp(o2 ? p0l : p1l, std::integral_constant<int, 0x4E>{});
+            const float s1 = swp(o2 ? p0h : p1h, std::integral_constant<int, 0x4E>{});
+            f32x4v out;
+            out[0] = o2 ? s0 : p0l;
+            out[1] = o2 ? s1 : p0h;
+            out[2] = o2 ? p1l : s0;
+            out[3] = o2 ? p1h : s1;
+            const int64_t row = m0 + acc_row<MI>(wm, i, 4 * u + q, lane & ~3);
+            if (qc < N && row < M)
+              __builtin_nontemporal_store(out, reinterpret_cast<f32x4v*>(&static_cast<float*>(C)[row * ldc + qc]));
+          }
+        }
+      return;
+    }
+  }
   // Column pairs in one store (4 bytes of bf16, 8 of FP32): the lanes of an
   // even / odd pair hold columns c, c + 1 of the same rows, so a lane swap
   // gives the even lane row r's pair and the odd lane row r + 1's (half the
