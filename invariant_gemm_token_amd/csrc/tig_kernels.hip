@@ -40,6 +40,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) float f32x4v;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int BM = kBlockM, BN = kBlockN, BK = kBlockK;   // BM: the MoE kernel's tile
@@ -647,12 +648,13 @@ __device__ __forceinline__ void StoreEpi<EPI, MI>::operator()(const AccT<MI>& ac
   const int tid = opaque_tid();
   const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const int64_t m0 = int64_t(mt) * Geo<MI>::BM, n0 = int64_t(nt) * BN;
-  // FP32 with N and ldc multiples of 4 and C 16-byte aligned: the lanes of a
-  // quad hold columns c .. c + 3 of the same four rows (registers 4u .. 4u+3),
-  // and two lane-swap levels (lanes 1 apart, then 2 apart) transpose that 4 x 4
-  // block, so that lane q writes row q's four columns in one 16-byte store.
-  if constexpr (EPI == kEpiF32) {
-    if (((N | ldc) & 3) == 0 && (reinterpret_cast<uintptr_t>(C) & 15) == 0) {
+  // N and ldc multiples of 4, C aligned to four values: the lanes of a quad
+  // hold columns c .. c + 3 of the same four rows (registers 4u .. 4u+3), and
+  // two lane-swap levels (lanes 1 apart, then 2 apart) transpose that 4 x 4
+  // block, so that lane q writes row q's four columns in one store (16 bytes
+  // of FP32, 8 of bf16).
+  {
+    if (((N | ldc) & 3) == 0 && (reinterpret_cast<uintptr_t>(C) & (EPI == kEpiF32 ? 15 : 7)) == 0) {
       const int q = lane & 3;
       auto swp = [](float x, auto ctrl) {
         return __builtin_bit_cast(
@@ -686,8 +688,16 @@ __device__ __forceinline__ void StoreEpi<EPI, MI>::operator()(const AccT<MI>& ac
             out[2] = o2 ? p1l : s0;
             out[3] = o2 ? p1h : s1;
             const int64_t row = m0 + acc_row<MI>(wm, i, 4 * u + q, lane & ~3);
-            if (qc < N && row < M)
-              __builtin_nontemporal_store(out, reinterpret_cast<f32x4v*>(&static_cast<float*>(C)[row * ldc + qc]));
+            if (qc < N && row < M) {
+              if constexpr (EPI == kEpiF32) {
+                __builtin_nontemporal_store(out, reinterpret_cast<f32x4v*>(&static_cast<float*>(C)[row * ldc + qc]));
+              } else {
+                u32x2 pk;
+                pk[0] = uint32_t(f32_to_bf16_rne(out[0])) | (uint32_t(f32_to_bf16_rne(out[1])) << 16);
+                pk[1] = uint32_t(f32_to_bf16_rne(out[2])) | (uint32_t(f32_to_bf16_rne(out[3])) << 16);
+                __builtin_nontemporal_store(pk, reinterpret_cast<u32x2*>(&static_cast<uint16_t*>(C)[row * ldc + qc]));
+              }
+            }
           }
         }
       return;
