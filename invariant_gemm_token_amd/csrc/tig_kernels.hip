@@ -653,55 +653,53 @@ __device__ __forceinline__ void StoreEpi<EPI, MI>::operator()(const AccT<MI>& ac
   // two lane-swap levels (lanes 1 apart, then 2 apart) transpose that 4 x 4
   // block, so that lane q writes row q's four columns in one store (16 bytes
   // of FP32, 8 of bf16).
-  {
-    if (((N | ldc) & 3) == 0 && (reinterpret_cast<uintptr_t>(C) & (EPI == kEpiF32 ? 15 : 7)) == 0) {
-      const int q = lane & 3;
-      auto swp = [](float x, auto ctrl) {
-        return __builtin_bit_cast(
-            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), decltype(ctrl)::value, 0xf, 0xf, false));
-      };
+  if (((N | ldc) & 3) == 0 && (reinterpret_cast<uintptr_t>(C) & (EPI == kEpiF32 ? 15 : 7)) == 0) {
+    const int q = lane & 3;
+    auto swp = [](float x, auto ctrl) {
+      return __builtin_bit_cast(
+          float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), decltype(ctrl)::value, 0xf, 0xf, false));
+    };
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int64_t qc = (n0 + acc_col(wn, j, lane)) & ~int64_t(3);   // the quad's first column
+      for (int j = 0; j < 2; ++j) {
+        const int64_t qc = (n0 + acc_col(wn, j, lane)) & ~int64_t(3);   // the quad's first column
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float a0 = acc.c[i][j][4 * u], a1 = acc.c[i][j][4 * u + 1];
-            const float a2 = acc.c[i][j][4 * u + 2], a3 = acc.c[i][j][4 * u + 3];
-            // Lanes 1 apart: the even lane keeps rows 0 and 2 (its columns c, c + 1),
-            // the odd lane rows 1 and 3.
-            const bool o1 = (q & 1) != 0;
-            const float g0 = swp(o1 ? a0 : a1, std::integral_constant<int, 0xB1>{});
-            const float g1 = swp(o1 ? a2 : a3, std::integral_constant<int, 0xB1>{});
-            // pair (row r, columns 2p, 2p + 1) held: lo/hi of two rows
-            const float p0l = o1 ? g0 : a0, p0h = o1 ? a1 : g0;   // row o1 (0 or 1)
-            const float p1l = o1 ? g1 : a2, p1h = o1 ? a3 : g1;   // row 2 + o1
-            // Lanes 2 apart: lanes 0, 1 keep their first row's pair and take the
-            // partner's; lanes 2, 3 keep the second row's pair.
-            const bool o2 = (q & 2) != 0;
-            const float s0 = swp(o2 ? p0l : p1l, std::integral_constant<int, 0x4E>{});
-            const float s1 = swp(o2 ? p0h : p1h, std::integral_constant<int, 0x4E>{});
-            f32x4v out;
-            out[0] = o2 ? s0 : p0l;
-            out[1] = o2 ? s1 : p0h;
-            out[2] = o2 ? p1l : s0;
-            out[3] = o2 ? p1h : s1;
-            const int64_t row = m0 + acc_row<MI>(wm, i, 4 * u + q, lane & ~3);
-            if (qc < N && row < M) {
-              if constexpr (EPI == kEpiF32) {
-                __builtin_nontemporal_store(out, reinterpret_cast<f32x4v*>(&static_cast<float*>(C)[row * ldc + qc]));
-              } else {
-                u32x2 pk;
-                pk[0] = uint32_t(f32_to_bf16_rne(out[0])) | (uint32_t(f32_to_bf16_rne(out[1])) << 16);
-                pk[1] = uint32_t(f32_to_bf16_rne(out[2])) | (uint32_t(f32_to_bf16_rne(out[3])) << 16);
-                __builtin_nontemporal_store(pk, reinterpret_cast<u32x2*>(&static_cast<uint16_t*>(C)[row * ldc + qc]));
-              }
+        for (int u = 0; u < 4; ++u) {
+          const float a0 = acc.c[i][j][4 * u], a1 = acc.c[i][j][4 * u + 1];
+          const float a2 = acc.c[i][j][4 * u + 2], a3 = acc.c[i][j][4 * u + 3];
+          // Lanes 1 apart: the even lane keeps rows 0 and 2 (its columns c, c + 1),
+          // the odd lane rows 1 and 3.
+          const bool o1 = (q & 1) != 0;
+          const float g0 = swp(o1 ? a0 : a1, std::integral_constant<int, 0xB1>{});
+          const float g1 = swp(o1 ? a2 : a3, std::integral_constant<int, 0xB1>{});
+          // pair (row r, columns 2p, 2p + 1) held: lo/hi of two rows
+          const float p0l = o1 ? g0 : a0, p0h = o1 ? a1 : g0;   // row o1 (0 or 1)
+          const float p1l = o1 ? g1 : a2, p1h = o1 ? a3 : g1;   // row 2 + o1
+          // Lanes 2 apart: lanes 0, 1 keep their first row's pair and take the
+          // partner's; lanes 2, 3 keep the second row's pair.
+          const bool o2 = (q & 2) != 0;
+          const float s0 = swp(o2 ? p0l : p1l, std::integral_constant<int, 0x4E>{});
+          const float s1 = swp(o2 ? p0h : p1h, std::integral_constant<int, 0x4E>{});
+          f32x4v out;
+          out[0] = o2 ? s0 : p0l;
+          out[1] = o2 ? s1 : p0h;
+          out[2] = o2 ? p1l : s0;
+          out[3] = o2 ? p1h : s1;
+          const int64_t row = m0 + acc_row<MI>(wm, i, 4 * u + q, lane & ~3);
+          if (qc < N && row < M) {
+            if constexpr (EPI == kEpiF32) {
+              __builtin_nontemporal_store(out, reinterpret_cast<f32x4v*>(&static_cast<float*>(C)[row * ldc + qc]));
+            } else {
+              u32x2 pk;
+              pk[0] = uint32_t(f32_to_bf16_rne(out[0])) | (uint32_t(f32_to_bf16_rne(out[1])) << 16);
+              pk[1] = uint32_t(f32_to_bf16_rne(out[2])) | (uint32_t(f32_to_bf16_rne(out[3])) << 16);
+              __builtin_nontemporal_store(pk, reinterpret_cast<u32x2*>(&static_cast<uint16_t*>(C)[row * ldc + qc]));
             }
           }
         }
-      return;
-    }
+      }
+    return;
   }
   // Column pairs in one store (4 bytes of bf16, 8 of FP32): the lanes of an
   // even / odd pair hold columns c, c + 1 of the same rows, so a lane swap
